@@ -1,0 +1,258 @@
+"""Python binding of libcpthd.so: argument marshalling only.
+
+The functions named ``cpthd_*`` map one to one onto the C entry points of
+include/cpthd.h and take torch tensors (device memory) in place of pointers;
+every step of the computation runs in the library's HIP kernels.  torch is
+used for device memory and the current stream only.
+
+Above them sit small conveniences (``partition_indices``, ``reorder_kv``,
+``AttnPlan``, ``attention``) and ``CPAttention``, an autograd function that
+captures the load-balancing strategy and the plan in forward so that backward
+sees the same token layout (TransformerEngine PR #3221, "What changed":
+backward reuses the strategy captured in forward).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import torch
+
+from . import _lib
+
+DUAL_CHUNK_SWAP = 0
+NO_LOAD_BALANCE = 1
+
+_DEV_BITS = {1: "cu_seqlens_padded not non-decreasing or not starting at 0",
+             2: "cu_seqlens_padded[B] != T",
+             4: "DualChunkSwap: a padded document length is not divisible by 2*cp_size",
+             8: "cu_seqlens not non-decreasing, or an actual length exceeds its padded length",
+             16: "workspace does not hold a plan for these arguments"}
+
+
+def _p(t):
+    """Device pointer of a tensor (None -> NULL).  Rejects CPU / non-contiguous tensors."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _s(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _ev(events):
+    if events is None:
+        return None, 0
+    return events.array_ptr(), events.n
+
+
+def describe_dev_status(bits: int) -> str:
+    return "; ".join(msg for b, msg in _DEV_BITS.items() if bits & b) or "ok"
+
+
+# ----------------------------------------------------------------------------
+# one-to-one wrappers of the C ABI
+# ----------------------------------------------------------------------------
+def cpthd_partition_indices(cu_seqlens_padded, num_docs, total_tokens, cp_size, rank, strategy, out_indices,
+                            dev_status=None, stream=None):
+    return _lib.call("cpthd_partition_indices", _p(cu_seqlens_padded), num_docs, total_tokens, cp_size, rank,
+                     strategy, _p(out_indices), _p(dev_status), _s(stream))
+
+
+def cpthd_reorder_kv(k_gathered, v_gathered, k_out, v_out, row_bytes, cu_seqlens_padded, num_docs, total_tokens,
+                     capacity_tokens, cp_size, strategy, dev_status=None, stream=None):
+    return _lib.call("cpthd_reorder_kv", _p(k_gathered), _p(v_gathered), _p(k_out), _p(v_out), row_bytes,
+                     _p(cu_seqlens_padded), num_docs, total_tokens, capacity_tokens, cp_size, strategy,
+                     _p(dev_status), _s(stream))
+
+
+def cpthd_attn_workspace_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs):
+    return int(_lib.load().cpthd_attn_workspace_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads,
+                                                      head_dim, max_docs))
+
+
+def cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank,
+                    strategy, num_q_heads, num_kv_heads, head_dim, workspace, dev_status=None, stream=None):
+    return _lib.call("cpthd_attn_plan", _p(cu_seqlens), _p(cu_seqlens_padded), num_docs, total_tokens,
+                     capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, _p(workspace),
+                     workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream))
+
+
+def cpthd_attn_fwd(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
+                   num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
+                   workspace, dev_status=None, stream=None, events=None):
+    ev, nev = _ev(events)
+    return _lib.call("cpthd_attn_fwd", _p(q_local), _p(k), _p(v), total_tokens, capacity_tokens, num_docs, cp_size,
+                     rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                     window_right, _p(o_local), _p(lse_local), _p(workspace),
+                     workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream), ev, nev)
+
+
+def cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
+                   rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                   window_right, dq_local, dk, dv, workspace, dev_status=None, stream=None, events=None):
+    ev, nev = _ev(events)
+    return _lib.call("cpthd_attn_bwd", _p(q_local), _p(k), _p(v), _p(o_local), _p(do_local), _p(lse_local),
+                     total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads,
+                     head_dim, softmax_scale, causal, window_left, window_right, _p(dq_local), _p(dk), _p(dv),
+                     _p(workspace), workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream),
+                     ev, nev)
+
+
+# ----------------------------------------------------------------------------
+# HIP events for the optional per-kernel timing argument
+# ----------------------------------------------------------------------------
+class HipEvents:
+    """n raw hipEvent_t handles, created through the HIP runtime torch already loaded."""
+
+    def __init__(self, n: int):
+        torch.cuda.init()
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self.n = n
+        self._arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            rc = self._hip.hipEventCreate(ctypes.byref(self._arr, i * ctypes.sizeof(ctypes.c_void_p)))
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreate failed ({rc})")
+
+    def array_ptr(self):
+        return ctypes.cast(self._arr, ctypes.c_void_p)
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._arr[i]),
+                                           ctypes.c_void_p(self._arr[j]))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def close(self):
+        for i in range(self.n):
+            if self._arr[i]:
+                self._hip.hipEventDestroy(ctypes.c_void_p(self._arr[i]))
+                self._arr[i] = None
+
+
+# ----------------------------------------------------------------------------
+# conveniences
+# ----------------------------------------------------------------------------
+def check_dev_status(dev_status) -> None:
+    bits = int(dev_status.item())
+    if bits:
+        raise ValueError(f"device-detected metadata error (bits {bits}): {describe_dev_status(bits)}")
+
+
+def partition_indices(cu_seqlens_padded, total_tokens, cp_size, rank, strategy, out=None, dev_status=None):
+    """int32 [T/cp_size] physical token indices of ``rank`` (device tensor)."""
+    num_docs = cu_seqlens_padded.numel() - 1
+    if out is None:
+        out = torch.empty(total_tokens // cp_size, dtype=torch.int32, device=cu_seqlens_padded.device)
+    cpthd_partition_indices(cu_seqlens_padded, num_docs, total_tokens, cp_size, rank, strategy, out, dev_status)
+    return out
+
+
+def reorder_kv(k_gathered, v_gathered, cu_seqlens_padded, total_tokens, cp_size, strategy, k_out=None, v_out=None,
+               dev_status=None):
+    """Physical-order K and V from the rank-major all-gathered buffers."""
+    if k_out is None:
+        k_out = torch.empty_like(k_gathered)
+    if v_out is None:
+        v_out = torch.empty_like(v_gathered)
+    row_bytes = k_gathered[0].numel() * k_gathered.element_size()
+    cpthd_reorder_kv(k_gathered, v_gathered, k_out, v_out, row_bytes, cu_seqlens_padded,
+                     cu_seqlens_padded.numel() - 1, total_tokens, k_gathered.shape[0], cp_size, strategy, dev_status)
+    return k_out, v_out
+
+
+class AttnPlan:
+    """Workspace holding one rank's attention plan; sized once for a capacity, rebuilt per micro-batch."""
+
+    def __init__(self, capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, device="cuda"):
+        self.capacity = capacity_tokens
+        self.cp_size = cp_size
+        self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
+        self.max_docs = max_docs
+        nbytes = cpthd_attn_workspace_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs)
+        if nbytes == 0:
+            raise ValueError("unsupported attention configuration")
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        self.built = None
+
+    def build(self, cu_seqlens, cu_seqlens_padded, total_tokens, rank, strategy, dev_status=None):
+        num_docs = cu_seqlens_padded.numel() - 1
+        if num_docs > self.max_docs:
+            raise ValueError("more documents than the workspace was sized for")
+        cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, self.capacity, self.cp_size, rank,
+                        strategy, self.Hq, self.Hkv, self.D, self.workspace, dev_status)
+        self.built = dict(total_tokens=total_tokens, num_docs=num_docs, rank=rank, strategy=strategy)
+        return self
+
+    def _args(self):
+        if self.built is None:
+            raise RuntimeError("plan not built")
+        b = self.built
+        return (b["total_tokens"], self.capacity, b["num_docs"], self.cp_size, b["rank"], b["strategy"],
+                self.Hq, self.Hkv, self.D)
+
+
+def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, lse_local=None, dev_status=None,
+             events=None):
+    S = plan.built["total_tokens"] // plan.cp_size
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(plan.D)
+    if o_local is None:
+        o_local = torch.empty((S, plan.Hq, plan.D), dtype=torch.bfloat16, device=q_local.device)
+    if lse_local is None:
+        lse_local = torch.empty((S, plan.Hq), dtype=torch.float32, device=q_local.device)
+    cpthd_attn_fwd(q_local, k, v, *plan._args(), softmax_scale, 1, -1, 0, o_local, lse_local, plan.workspace,
+                   dev_status, events=events)
+    return o_local, lse_local
+
+
+def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softmax_scale=None, dq_local=None,
+             dk=None, dv=None, dev_status=None, events=None):
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(plan.D)
+    if dq_local is None:
+        dq_local = torch.empty(q_local.shape, dtype=torch.float32, device=q_local.device)
+    if dk is None:
+        dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+    if dv is None:
+        dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, *plan._args(), softmax_scale, 1, -1, 0, dq_local,
+                   dk, dv, plan.workspace, dev_status, events=events)
+    return dq_local, dk, dv
+
+
+class CPAttention(torch.autograd.Function):
+    """Causal THD attention of one CP rank; backward reuses the plan (and strategy) captured in forward."""
+
+    @staticmethod
+    def forward(ctx, q_local, k, v, plan: AttnPlan, softmax_scale):
+        o, lse = attn_fwd(q_local, k, v, plan, softmax_scale)
+        ctx.plan = plan
+        ctx.layout = dict(plan.built)
+        ctx.scale = softmax_scale
+        ctx.save_for_backward(q_local, k, v, o, lse)
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q_local, k, v, o, lse = ctx.saved_tensors
+        if ctx.plan.built != ctx.layout:
+            raise RuntimeError("the plan was rebuilt for another layout between forward and backward")
+        dq, dk, dv = attn_bwd(q_local, k, v, o, do.contiguous(), lse, ctx.plan, ctx.scale)
+        return dq.to(q_local.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+
+
+def attention(q_local, k, v, plan: AttnPlan, softmax_scale=None):
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(plan.D)
+    return CPAttention.apply(q_local, k, v, plan, softmax_scale)

@@ -1,0 +1,290 @@
+// Strategy-specific attention metadata of one CP rank (gfx950).
+//
+// TransformerEngine PR #3221: the sequence diagram's "gather K/V and build
+// strategy-specific metadata" step; "Why": DualChunkSwap gives a rank two
+// attention steps per document (chunks r and 2*cp_size-1-r), NO_LOAD_BALANCE
+// one step over its contiguous chunk; commit messages: "simplify packed
+// metadata to one chunk and one attention step per rank".
+//
+// Here the two steps become *segments*: maximal runs of the rank's local rows
+// that are consecutive physical tokens of one document.  A query tile is up to
+// 128/G tokens of one segment (times the G q heads of a kv head); its causal key
+// range is [document start, last actual token of the tile].  A key tile is up
+// to 128 keys of one document's slot; the rank's rows that see it are the
+// suffixes (physical token >= first key) of the document's segments.  Both
+// lists are sorted by work, longest first, so the hardware dispatcher's
+// in-order work-group launch acts as a longest-processing-time queue.
+//
+// One work-group of 1024 threads builds the whole plan: it validates the cu
+// arrays, scans per-document tile counts in chunks of 1024 documents, emits
+// the tiles in parallel, and counting-sorts them by cost.
+#include "cpthd_device.h"
+#include "cpthd_host.h"
+
+namespace cpthd {
+
+constexpr int kPlanThreads = 1024;
+
+__device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Exclusive prefix sum over the work-group; also returns the total.
+__device__ inline int block_exclusive_scan(int v, int* s_wave, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) s_wave[w] = x;
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    int wv = threadIdx.x < kPlanThreads / 64 ? s_wave[threadIdx.x] : 0;
+    int z = wv;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      int y = __shfl_up(z, o, 64);
+      if (lane >= o) z += y;
+    }
+    if (threadIdx.x < kPlanThreads / 64) s_wave[16 + threadIdx.x] = z - wv;
+    if (threadIdx.x == kPlanThreads / 64 - 1) s_wave[32] = z;
+  }
+  __syncthreads();
+  const int res = x - v + s_wave[16 + w];
+  total = s_wave[32];
+  __syncthreads();
+  return res;
+}
+
+__device__ inline DocSeg doc_segments(const int32_t* cu_a, const int32_t* cu_p, int i, int S, int cp, int rank,
+                                      int strategy) {
+  DocSeg d;
+  const int ds = cu_p[i], L = cu_p[i + 1] - ds;
+  d.ds = ds;
+  d.ve = ds + (cu_a[i + 1] - cu_a[i]);
+  if (strategy == kDCS) {
+    const int c = L / (2 * cp);
+    d.la = ds / cp;
+    d.pa = ds + rank * c;
+    d.na = c;
+    d.lb = d.la + c;
+    d.pb = ds + (2 * cp - 1 - rank) * c;
+    d.nb = c;
+  } else {
+    const int lo = max(ds, rank * S), hi = min(ds + L, rank * S + S);
+    d.na = max(0, hi - lo);
+    d.pa = lo;
+    d.la = lo - rank * S;
+    d.lb = d.la + d.na;
+    d.pb = lo;
+    d.nb = 0;
+  }
+  return d;
+}
+
+// Query chunks of kQChunk rows the rank iterates for keys from k0 on.
+__device__ inline int kv_tile_cost(const DocSeg& d, int k0, int G) {
+  int cost = 0;
+  int lo = max(d.pa, k0), hi = min(d.pa + d.na, d.ve);
+  if (hi > lo) cost += cdiv((hi - lo) * G, kQChunk);
+  lo = max(d.pb, k0);
+  hi = min(d.pb + d.nb, d.ve);
+  if (hi > lo) cost += cdiv((hi - lo) * G, kQChunk);
+  return cost;
+}
+
+template <typename Tile>
+__device__ void sort_by_cost_desc(const Tile* tmp, Tile* out, int n, int* s_hist, int* s_wave) {
+  for (int b = threadIdx.x; b < kCostBins; b += kPlanThreads) s_hist[b] = 0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += kPlanThreads) atomicAdd(&s_hist[min(tmp[t].cost, kCostBins - 1)], 1);
+  __syncthreads();
+  // position of bin b = number of tiles in bins above b
+  const int hi = kCostBins - 1 - 2 * threadIdx.x;
+  const int v0 = s_hist[hi], v1 = s_hist[hi - 1];
+  int total;
+  const int excl = block_exclusive_scan(v0 + v1, s_wave, total);
+  s_hist[hi] = excl;
+  s_hist[hi - 1] = excl + v0;
+  __syncthreads();
+  for (int t = threadIdx.x; t < n; t += kPlanThreads) {
+    const Tile e = tmp[t];
+    const int pos = atomicAdd(&s_hist[min(e.cost, kCostBins - 1)], 1);
+    out[pos] = e;
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu_a,
+                                                            const int32_t* __restrict__ cu_p, int B, int T, int cp,
+                                                            int rank, int strategy, int Hq, int Hkv, int D,
+                                                            char* __restrict__ ws, PlanLayout lay, int32_t* status) {
+  __shared__ int s_bits;
+  __shared__ int s_wave[40];
+  __shared__ int s_qoff[kPlanThreads], s_kvoff[kPlanThreads];
+  __shared__ int s_hist[kCostBins];
+
+  PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws);
+  QTile* qt = reinterpret_cast<QTile*>(ws + lay.qtiles);
+  QTile* qtmp = reinterpret_cast<QTile*>(ws + lay.qtiles_tmp);
+  KVTile* kvt = reinterpret_cast<KVTile*>(ws + lay.kvtiles);
+  KVTile* kvtmp = reinterpret_cast<KVTile*>(ws + lay.kvtiles_tmp);
+  DocSeg* docs = reinterpret_cast<DocSeg*>(ws + lay.docs);
+
+  const int tid = threadIdx.x;
+  const int S = T / cp, G = Hq / Hkv, bm = tokens_per_qtile(G);
+  if (tid == 0) {
+    s_bits = 0;
+    hdr->valid = 0;
+  }
+  __syncthreads();
+
+  // 1. validate the metadata
+  int bits = 0;
+  for (int i = tid; i < B; i += kPlanThreads) {
+    const int p0 = cu_p[i], p1 = cu_p[i + 1], a0 = cu_a[i], a1 = cu_a[i + 1];
+    if (p1 < p0) bits |= kDevCuOrder;
+    if (a1 < a0 || a1 - a0 > p1 - p0) bits |= kDevActual;
+    if (strategy == kDCS && ((p1 - p0) % (2 * cp)) != 0) bits |= kDevDcsDivisible;
+  }
+  if (tid == 0) {
+    if (cu_p[0] != 0) bits |= kDevCuOrder;
+    if (cu_a[0] != 0) bits |= kDevActual;
+    if (cu_p[B] != T) bits |= kDevCuTotal;
+  }
+  if (bits) atomicOr(&s_bits, bits);
+  __syncthreads();
+  if (s_bits) {
+    if (tid == 0) {
+      if (status) atomicOr(status, s_bits);
+      hdr->n_qtiles = 0;
+      hdr->n_kvtiles = 0;
+    }
+    return;
+  }
+
+  // 2. documents in chunks of 1024: segments, tile counts, scan, emission
+  int carry_q = 0, carry_kv = 0;
+  for (int base = 0; base < B; base += kPlanThreads) {
+    const int i = base + tid;
+    const int cnt = min(kPlanThreads, B - base);
+    int nq = 0, nkv = 0;
+    if (i < B) {
+      const DocSeg d = doc_segments(cu_a, cu_p, i, S, cp, rank, strategy);
+      docs[i] = d;
+      nq = cdiv(d.na, bm) + cdiv(d.nb, bm);
+      nkv = cdiv(cu_p[i + 1] - d.ds, kKeysPerWG);
+    }
+    int tq, tkv;
+    const int oq = block_exclusive_scan(nq, s_wave, tq);
+    const int okv = block_exclusive_scan(nkv, s_wave, tkv);
+    s_qoff[tid] = oq;
+    s_kvoff[tid] = okv;
+    __threadfence_block();
+    __syncthreads();
+    for (int t = tid; t < tq; t += kPlanThreads) {
+      int lo = 0, hi = cnt - 1;   // last document whose first tile is <= t
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_qoff[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const DocSeg d = docs[base + lo];
+      int k = t - s_qoff[lo];
+      const int nA = cdiv(d.na, bm);
+      QTile e;
+      if (k < nA) {
+        e.lrow0 = d.la + k * bm;
+        e.p0 = d.pa + k * bm;
+        e.ntok = min(bm, d.na - k * bm);
+      } else {
+        k -= nA;
+        e.lrow0 = d.lb + k * bm;
+        e.p0 = d.pb + k * bm;
+        e.ntok = min(bm, d.nb - k * bm);
+      }
+      e.ds = d.ds;
+      e.ve = d.ve;
+      e.kv_end = e.p0 < d.ve ? min(e.p0 + e.ntok, d.ve) : d.ds;
+      e.cost = cdiv(e.kv_end - d.ds, kKvStep);
+      e.doc = base + lo;
+      qtmp[carry_q + t] = e;
+    }
+    for (int t = tid; t < tkv; t += kPlanThreads) {
+      int lo = 0, hi = cnt - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_kvoff[mid] <= t) lo = mid; else hi = mid - 1;
+      }
+      const DocSeg d = docs[base + lo];
+      const int k = t - s_kvoff[lo];
+      const int L = cu_p[base + lo + 1] - d.ds;
+      KVTile e;
+      e.k0 = d.ds + k * kKeysPerWG;
+      e.nkeys = min(kKeysPerWG, L - k * kKeysPerWG);
+      e.doc = base + lo;
+      e.cost = kv_tile_cost(d, e.k0, G);
+      kvtmp[carry_kv + t] = e;
+    }
+    carry_q += tq;
+    carry_kv += tkv;
+    __threadfence_block();
+    __syncthreads();
+  }
+
+  // 3. longest first
+  sort_by_cost_desc(qtmp, qt, carry_q, s_hist, s_wave);
+  sort_by_cost_desc(kvtmp, kvt, carry_kv, s_hist, s_wave);
+
+  // 4. header last
+  if (tid == 0) {
+    hdr->magic = kPlanMagic;
+    hdr->version = kPlanVersion;
+    hdr->T = T;
+    hdr->S = S;
+    hdr->cp = cp;
+    hdr->rank = rank;
+    hdr->strategy = strategy;
+    hdr->Hq = Hq;
+    hdr->Hkv = Hkv;
+    hdr->D = D;
+    hdr->G = G;
+    hdr->num_docs = B;
+    hdr->bm_tok = bm;
+    hdr->n_qtiles = carry_q;
+    hdr->n_kvtiles = carry_kv;
+    hdr->max_qtiles = (int)lay.max_qtiles;
+    hdr->max_kvtiles = (int)lay.max_kvtiles;
+    hdr->max_docs = (int)lay.max_docs;
+    __threadfence();
+    hdr->valid = 1;
+  }
+}
+
+}  // namespace cpthd
+
+using namespace cpthd;
+
+extern "C" size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp_size, int32_t num_q_heads,
+                                             int32_t num_kv_heads, int32_t head_dim, int32_t max_docs) {
+  if (cp_size < 1 || max_docs < 1) return 0;
+  if (check_tokens(capacity_tokens, capacity_tokens, cp_size, max_docs)) return 0;
+  if (check_heads(num_q_heads, num_kv_heads, head_dim)) return 0;
+  return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, max_docs).total;
+}
+
+extern "C" int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t num_docs,
+                               int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,
+                               int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
+  if (!cu_seqlens || !cu_seqlens_padded) return CPTHD_ERR_NULL;
+  if (cp_size < 1 || rank < 0 || rank >= cp_size) return CPTHD_ERR_RANK;
+  if (int e = check_strategy(strategy)) return e;
+  if (int e = check_tokens(total_tokens, capacity_tokens, cp_size, num_docs)) return e;
+  if (int e = check_heads(num_q_heads, num_kv_heads, head_dim)) return e;
+  const PlanLayout lay = plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, num_docs);
+  if (!workspace || workspace_bytes < lay.total || reinterpret_cast<uintptr_t>(workspace) % 256)
+    return CPTHD_ERR_WORKSPACE;
+  return launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, nullptr, 0, 0, cu_seqlens, cu_seqlens_padded,
+                num_docs, (int)total_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
+                (char*)workspace, lay, dev_status);
+}

@@ -1,0 +1,137 @@
+// Device-side definitions shared by the cpthd kernels (gfx950 / CDNA4 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cpthd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kDCS = 0;      // DualChunkSwap
+constexpr int kContig = 1;   // NO_LOAD_BALANCE
+
+// status bits (mirror the public header)
+constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual = 8, kDevPlan = 16;
+
+// ---------------------------------------------------------------------------
+// tiling constants shared by the plan and the attention kernels
+// ---------------------------------------------------------------------------
+constexpr int kRowsPerWG = 128;   // query rows (token x head pairs) per fwd / dq work-group
+constexpr int kKeysPerWG = 128;   // keys per dk/dv work-group
+constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
+constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
+constexpr int kCostBins = 2048;   // counting-sort bins for longest-first ordering
+constexpr int kPlanMagic = 0x43505444;  // "CPTD"
+constexpr int kPlanVersion = 1;
+
+// Query tile: `ntok` consecutive local rows of one segment (a run of the rank's
+// rows inside one document), all q heads of one kv group.  Keys [ds, kv_end).
+struct QTile {
+  int32_t lrow0;   // first local row
+  int32_t ntok;    // rows (tokens) in the tile
+  int32_t p0;      // physical token of the first row
+  int32_t ds;      // document start (physical)
+  int32_t kv_end;  // one past the last key any actual row of the tile sees
+  int32_t ve;      // end of the document's actual tokens
+  int32_t cost;
+  int32_t doc;
+};
+
+// Key tile of one document: keys [k0, k0 + nkeys) (inside the document's slot).
+struct KVTile {
+  int32_t k0;
+  int32_t nkeys;
+  int32_t doc;
+  int32_t cost;
+};
+
+// The rank's rows of one document: up to two segments (DualChunkSwap chunks
+// r and 2cp-1-r; contiguous: one), each `n` local rows from local row `l`
+// at physical token `p`.
+struct DocSeg {
+  int32_t ds, ve, la, pa, na, lb, pb, nb;
+};
+
+struct PlanHeader {
+  int32_t magic, version, valid;
+  int32_t T, S, cp, rank, strategy, Hq, Hkv, D, G, num_docs;
+  int32_t bm_tok;               // tokens per query tile
+  int32_t n_qtiles, n_kvtiles;
+  int32_t max_qtiles, max_kvtiles, max_docs;
+  int32_t pad_[45];
+};
+static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
+
+// Workspace layout (byte offsets), identical on host and device.
+struct PlanLayout {
+  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, delta, total;
+  int64_t max_qtiles, max_kvtiles, max_docs;
+};
+
+__host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+__host__ __device__ inline int tokens_per_qtile(int G) { return kRowsPerWG / G; }
+
+__host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int Hq, int Hkv, int max_docs) {
+  PlanLayout L;
+  const int G = Hq / Hkv;
+  const int64_t S = capacity / cp;
+  const int bm = tokens_per_qtile(G);
+  L.max_docs = max_docs;
+  L.max_qtiles = (S + bm - 1) / bm + 2 * (int64_t)max_docs;
+  L.max_kvtiles = (capacity + kKeysPerWG - 1) / kKeysPerWG + (int64_t)max_docs;
+  size_t off = sizeof(PlanHeader);
+  L.qtiles = off;       off = align_up(off + L.max_qtiles * sizeof(QTile), 256);
+  L.qtiles_tmp = off;   off = align_up(off + L.max_qtiles * sizeof(QTile), 256);
+  L.kvtiles = off;      off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
+  L.kvtiles_tmp = off;  off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
+  L.docs = off;         off = align_up(off + (size_t)max_docs * sizeof(DocSeg), 256);
+  L.delta = off;        off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// small device helpers
+// ---------------------------------------------------------------------------
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite)
+__device__ inline uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+}
+
+__device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline bf16x8 as_bf16x8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+// Largest i in [0, n] with a[i] <= x, for a non-decreasing array a[0..n] with a[0] <= x.
+__device__ inline int upper_index(const int32_t* a, int n, int64_t x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if ((int64_t)a[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+}  // namespace cpthd

@@ -1,0 +1,186 @@
+// Partition indices and K/V restoration for one CP rank (gfx950).
+//
+// TransformerEngine PR #3221, "Why": DualChunkSwap cuts every document into
+// 2*cp_size equal chunks and rank r owns the mirrored pair (r, 2*cp_size-1-r);
+// NO_LOAD_BALANCE cuts the physical buffer into cp_size contiguous chunks.
+// Commit messages: rank-major (contiguous) ownership needs no K/V reorder;
+// review thread: the THD stream dependency follows K/V restoration.
+//
+// Both kernels are pure data movement (HBM bound).  Under DualChunkSwap the
+// rank's local rows of document i start at local row cu_padded[i] / cp_size
+// (every earlier document contributed L/cp_size rows), so an output position
+// finds its document with one binary search over cu_seqlens_padded, without a
+// prefix sum.
+#include "cpthd_device.h"
+#include "cpthd_host.h"
+
+namespace cpthd {
+
+// Checks on cu_seqlens_padded shared by partition and reorder.
+__device__ inline void validate_cu_padded(const int32_t* cu, int B, int64_t T, int cp, int strategy,
+                                          int32_t* status) {
+  if (status == nullptr) return;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int nthreads = gridDim.x * blockDim.x;
+  int bits = 0;
+  for (int i = gid; i < B; i += nthreads) {
+    const int a = cu[i], b = cu[i + 1];
+    if (b < a) bits |= kDevCuOrder;
+    if (strategy == kDCS && ((b - a) % (2 * cp)) != 0) bits |= kDevDcsDivisible;
+  }
+  if (gid == 0) {
+    if (cu[0] != 0) bits |= kDevCuOrder;
+    if ((int64_t)cu[B] != T) bits |= kDevCuTotal;
+  }
+  if (bits) atomicOr(status, bits);
+}
+
+// One thread writes 4 consecutive outputs j = 4*gid .. 4*gid+3 of [0, S).
+__global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restrict__ cu, int B, int T, int cp,
+                                                        int rank, int strategy, int32_t* __restrict__ out,
+                                                        int32_t* status) {
+  validate_cu_padded(cu, B, T, cp, strategy, status);
+  const int S = T / cp;
+  const int64_t j0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
+  if (j0 >= S) return;
+  int32_t res[4];
+  if (strategy == kContig) {
+    for (int u = 0; u < 4; ++u) res[u] = rank * S + (int)j0 + u;
+  } else {
+    // document of output j: cu[i] <= j*cp < cu[i+1]
+    int i = upper_index(cu, B - 1, j0 * cp);
+    for (int u = 0; u < 4; ++u) {
+      const int64_t j = j0 + u;
+      while (i < B - 1 && (int64_t)cu[i + 1] <= j * cp) ++i;
+      const int start = cu[i];
+      const int c = (cu[i + 1] - start) / (2 * cp);
+      const int jj = (int)(j - start / cp);
+      int p = jj < c ? start + rank * c + jj : start + (2 * cp - 1 - rank) * c + (jj - c);
+      res[u] = min(max(p, 0), T - 1);   // stays in range even for a rejected layout
+    }
+  }
+  if (j0 + 3 < S && (S & 3) == 0) {
+    *reinterpret_cast<int4*>(out + j0) = make_int4(res[0], res[1], res[2], res[3]);
+  } else {
+    for (int u = 0; u < 4 && j0 + u < S; ++u) out[j0 + u] = res[u];
+  }
+}
+
+// Restoration: each wave copies whole token rows.  Row p of the output (physical
+// order) comes from gathered row s*S + (local index of p on its owner s).
+constexpr int kReorderRowsPerWave = 4;
+
+__device__ inline int64_t gathered_row_of(const int32_t* cu, int B, int S, int cp, int strategy, int p) {
+  if (strategy == kContig) return p;
+  const int i = upper_index(cu, B - 1, p);       // document holding physical row p
+  const int start = cu[i];
+  const int L = cu[i + 1] - start;
+  const int c = L / (2 * cp);
+  if (c <= 0) return p;                           // only for a rejected layout
+  const int pos = p - start;
+  const int chunk = min(pos / c, 2 * cp - 1);
+  const int off = pos - chunk * c;
+  const int owner = chunk < cp ? chunk : 2 * cp - 1 - chunk;
+  const int local = start / cp + (chunk < cp ? off : c + off);
+  return (int64_t)owner * S + local;
+}
+
+__global__ __launch_bounds__(256) void reorder_kernel(const char* __restrict__ kg, const char* __restrict__ vg,
+                                                      char* __restrict__ ko, char* __restrict__ vo,
+                                                      int64_t row_bytes, const int32_t* __restrict__ cu, int B,
+                                                      int T, int cp, int strategy, int32_t* status) {
+  if (blockIdx.y == 0) validate_cu_padded(cu, B, T, cp, strategy, status);
+  const char* src = blockIdx.y == 0 ? kg : vg;
+  char* dst = blockIdx.y == 0 ? ko : vo;
+  const int S = T / cp;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * kReorderRowsPerWave;
+  const int64_t n16 = row_bytes / 16;
+  int64_t g[kReorderRowsPerWave];
+  for (int rr = 0; rr < kReorderRowsPerWave; ++rr) {
+    const int64_t p = min(row0 + rr, (int64_t)T - 1);
+    const int64_t gr = gathered_row_of(cu, B, S, cp, strategy, (int)p);
+    g[rr] = __builtin_amdgcn_readfirstlane((int)min(max(gr, (int64_t)0), (int64_t)T - 1));
+  }
+  const int nrows = (int)min((int64_t)kReorderRowsPerWave, (int64_t)T - row0);
+  if (nrows <= 0) return;
+  for (int64_t e = lane; e < n16; e += 64) {
+    u32x4 val[kReorderRowsPerWave];
+#pragma unroll
+    for (int rr = 0; rr < kReorderRowsPerWave; ++rr)
+      if (rr < nrows) val[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + g[rr] * row_bytes) + e);
+#pragma unroll
+    for (int rr = 0; rr < kReorderRowsPerWave; ++rr)
+      if (rr < nrows) __builtin_nontemporal_store(val[rr], reinterpret_cast<u32x4*>(dst + (row0 + rr) * row_bytes) + e);
+  }
+}
+
+}  // namespace cpthd
+
+using namespace cpthd;
+
+extern "C" int cpthd_partition_indices(const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                                       int32_t cp_size, int32_t rank, int32_t strategy, int32_t* out_indices,
+                                       int32_t* dev_status, hipStream_t stream) {
+  if (!cu_seqlens_padded || !out_indices) return CPTHD_ERR_NULL;
+  if (cp_size < 1 || rank < 0 || rank >= cp_size) return CPTHD_ERR_RANK;
+  if (int e = check_strategy(strategy)) return e;
+  if (int e = check_tokens(total_tokens, total_tokens, cp_size, num_docs)) return e;
+  const int64_t S = total_tokens / cp_size;
+  const int64_t threads = (S + 3) / 4;
+  dim3 grid((unsigned)((threads + 255) / 256));
+  return launch(partition_kernel, grid, dim3(256), 0, stream, nullptr, 0, 0, cu_seqlens_padded, num_docs,
+                (int)total_tokens, cp_size, rank, strategy, out_indices, dev_status);
+}
+
+extern "C" int cpthd_reorder_kv(const void* k_gathered, const void* v_gathered, void* k_out, void* v_out,
+                                int64_t row_bytes, const int32_t* cu_seqlens_padded, int32_t num_docs,
+                                int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t strategy,
+                                int32_t* dev_status, hipStream_t stream) {
+  if (!k_gathered || !v_gathered || !k_out || !v_out || !cu_seqlens_padded) return CPTHD_ERR_NULL;
+  if (cp_size < 1) return CPTHD_ERR_RANK;
+  if (int e = check_strategy(strategy)) return e;
+  if (int e = check_tokens(total_tokens, capacity_tokens, cp_size, num_docs)) return e;
+  if (row_bytes <= 0 || row_bytes % 16) return CPTHD_ERR_ALIGN;
+  for (const void* p : {k_gathered, v_gathered, (const void*)k_out, (const void*)v_out})
+    if (reinterpret_cast<uintptr_t>(p) % 16) return CPTHD_ERR_ALIGN;
+  const int64_t bytes = total_tokens * row_bytes;
+  auto overlap = [bytes](const void* a, const void* b) {
+    const char* x = (const char*)a;
+    const char* y = (const char*)b;
+    return x < y + bytes && y < x + bytes;
+  };
+  if (strategy == CPTHD_NO_LOAD_BALANCE) {
+    if (k_out == k_gathered && v_out == v_gathered) return CPTHD_OK;   // already in physical order
+    if ((k_out != k_gathered && overlap(k_out, k_gathered)) || (v_out != v_gathered && overlap(v_out, v_gathered)))
+      return CPTHD_ERR_ALIAS;
+  } else {
+    for (const void* o : {(const void*)k_out, (const void*)v_out})
+      for (const void* i : {k_gathered, v_gathered})
+        if (overlap(o, i)) return CPTHD_ERR_ALIAS;
+  }
+  if (overlap(k_out, v_out)) return CPTHD_ERR_ALIAS;
+  const int64_t rows_per_wg = 4 * kReorderRowsPerWave;
+  dim3 grid((unsigned)((total_tokens + rows_per_wg - 1) / rows_per_wg), 2);
+  // a NO_LOAD_BALANCE copy where only one of K/V moves copies both; same bytes result
+  return launch(reorder_kernel, grid, dim3(256), 0, stream, nullptr, 0, 0, (const char*)k_gathered,
+                (const char*)v_gathered, (char*)k_out, (char*)v_out, row_bytes, cu_seqlens_padded, num_docs,
+                (int)total_tokens, cp_size, strategy, dev_status);
+}
+
+extern "C" const char* cpthd_status_string(int status) {
+  switch (status) {
+    case CPTHD_OK: return "ok";
+    case CPTHD_ERR_NULL: return "a required pointer is NULL";
+    case CPTHD_ERR_RANK: return "cp_size < 1 or rank outside [0, cp_size)";
+    case CPTHD_ERR_STRATEGY: return "unknown load-balancing strategy";
+    case CPTHD_ERR_TOKENS: return "bad token count (T <= 0, T > capacity, T % cp_size != 0, or num_docs < 1)";
+    case CPTHD_ERR_HEADS: return "unsupported heads (Hq % Hkv != 0, Hq/Hkv > 64, or head_dim not in {16,32,64,128})";
+    case CPTHD_ERR_MASK: return "only causal attention with window (-1, 0) is supported";
+    case CPTHD_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case CPTHD_ERR_LAUNCH: return "HIP kernel launch failed";
+    case CPTHD_ERR_ALIGN: return "row size not a multiple of 16 bytes or pointer not 16-byte aligned";
+    case CPTHD_ERR_ALIAS: return "output buffer overlaps an input buffer";
+    default: return "unknown status";
+  }
+}

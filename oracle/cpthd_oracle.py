@@ -168,11 +168,12 @@ def _doc_rows(idx, cu_padded, cu_actual, docs):
         yield d, rows, lpos[rows], cu_p[d], cu_a[d + 1] - cu_a[d]
 
 
-def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None):
+def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None, kv_heads=None):
     """Forward for one rank: returns (O [S,Hq,D], LSE [S,Hq], computed [S]) in float64.
 
     ``docs`` restricts the work to those documents (rows of other documents are
     NaN and ``computed`` is False there); None means every document.
+    ``kv_heads`` restricts it to the q heads of those kv heads (others NaN).
     """
     q_local = np.asarray(q_local, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -186,16 +187,19 @@ def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None):
     lse = np.full((S, Hq), np.nan)
     computed = np.zeros(S, dtype=bool)
     doc_of = token_map(cu_padded, cu_actual)[0][np.asarray(idx, dtype=np.int64)]
+    hsel = np.array([kv_heads is None or h // G in kv_heads for h in range(Hq)])
     for d in docs:
         sel = doc_of == d
         computed |= sel
-        o[sel] = 0.0           # pads: O = 0, LSE = -inf (overwritten for actual rows below)
-        lse[sel] = -np.inf
+        o[np.ix_(sel, hsel)] = 0.0      # pads: O = 0, LSE = -inf (overwritten for actual rows below)
+        lse[np.ix_(sel, hsel)] = -np.inf
     for d, rows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
         if rows.size == 0:
             continue
         kpos = np.arange(a)
         for h in range(Hq):
+            if kv_heads is not None and h // G not in kv_heads:
+                continue
             kd = k[start:start + a, h // G]
             vd = v[start:start + a, h // G]
             for b0 in range(0, rows.size, _ROW_BLOCK):
@@ -211,12 +215,13 @@ def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None):
     return o, lse, computed
 
 
-def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=None):
+def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=None, kv_heads=None):
     """Backward for one rank: returns (dQ [S,Hq,D], dK [T,Hkv,D], dV [T,Hkv,D]) in float64.
 
     dK/dV are the gradients contributed by this rank's query rows only (rows of
     keys no query of the rank sees are 0).  With ``docs`` given, dQ rows and
-    dK/dV rows outside those documents are NaN.
+    dK/dV rows outside those documents are NaN; ``kv_heads`` restricts the
+    work to those kv heads and their q heads in the same way.
     """
     q_local = np.asarray(q_local, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -232,16 +237,20 @@ def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=Non
     dk = np.full((T, Hkv, D), np.nan)
     dv = np.full((T, Hkv, D), np.nan)
     doc_of = token_map(cu_padded, cu_actual)[0][np.asarray(idx, dtype=np.int64)]
+    hsel = np.array([kv_heads is None or h // G in kv_heads for h in range(Hq)])
+    gsel = np.array([kv_heads is None or g in kv_heads for g in range(Hkv)])
     for d in docs:
-        dq[doc_of == d] = 0.0
-        dk[cu_p[d]:cu_p[d + 1]] = 0.0
-        dv[cu_p[d]:cu_p[d + 1]] = 0.0
+        dq[np.ix_(doc_of == d, hsel)] = 0.0
+        dk[cu_p[d]:cu_p[d + 1], gsel] = 0.0
+        dv[cu_p[d]:cu_p[d + 1], gsel] = 0.0
     for d, rows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
         if rows.size == 0:
             continue
         kpos = np.arange(a)
         for h in range(Hq):
             g = h // G
+            if kv_heads is not None and g not in kv_heads:
+                continue
             kd = k[start:start + a, g]
             vd = v[start:start + a, g]
             for b0 in range(0, rows.size, _ROW_BLOCK):

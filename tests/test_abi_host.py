@@ -1,0 +1,145 @@
+"""The C-ABI library loads, exports every declared symbol, and rejects bad arguments
+on the host before launching anything (no GPU needed: no call here reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from context_causal_thd_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpthd.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cpthd_\w+)\s*\(", text)))
+
+
+def _defines():
+    out = {}
+    for name, val in re.findall(r"#define\s+(CPTHD_\w+)\s+\(?(-?\d+)\)?", open(HEADER).read()):
+        out[name] = int(val)
+    return out
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures must cover the header exactly"
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    d = _defines()
+    for name, code in d.items():
+        if name.startswith("CPTHD_ERR_") or name == "CPTHD_OK":
+            s = lib.cpthd_status_string(code).decode()
+            assert s and s != "unknown status", name
+    assert lib.cpthd_status_string(12345) == b"unknown status"
+
+
+FAKE = 0x10000   # never dereferenced: every call below fails validation first
+
+
+def test_partition_host_errors(lib):
+    d = _defines()
+    f = lib.cpthd_partition_indices
+    assert f(None, 3, 28, 2, 0, 0, FAKE, None, None) == d["CPTHD_ERR_NULL"]
+    assert f(FAKE, 3, 28, 2, 0, 0, None, None, None) == d["CPTHD_ERR_NULL"]
+    assert f(FAKE, 3, 28, 0, 0, 0, FAKE, None, None) == d["CPTHD_ERR_RANK"]
+    assert f(FAKE, 3, 28, 2, 2, 0, FAKE, None, None) == d["CPTHD_ERR_RANK"]
+    assert f(FAKE, 3, 28, 2, -1, 0, FAKE, None, None) == d["CPTHD_ERR_RANK"]
+    assert f(FAKE, 3, 28, 2, 0, 7, FAKE, None, None) == d["CPTHD_ERR_STRATEGY"]
+    assert f(FAKE, 3, 27, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
+    assert f(FAKE, 3, 0, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
+    assert f(FAKE, 0, 28, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
+    assert f(FAKE, 3, 1 << 33, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
+
+
+def test_reorder_host_errors(lib):
+    d = _defines()
+    f = lib.cpthd_reorder_kv
+    A, B, C, E = 0x100000, 0x200000, 0x300000, 0x400000
+    assert f(None, B, C, E, 64, FAKE, 3, 28, 28, 2, 0, None, None) == d["CPTHD_ERR_NULL"]
+    assert f(A, B, C, E, 64, FAKE, 3, 28, 28, 0, 0, None, None) == d["CPTHD_ERR_RANK"]
+    assert f(A, B, C, E, 64, FAKE, 3, 28, 28, 2, 3, None, None) == d["CPTHD_ERR_STRATEGY"]
+    assert f(A, B, C, E, 64, FAKE, 3, 28, 20, 2, 0, None, None) == d["CPTHD_ERR_TOKENS"]
+    assert f(A, B, C, E, 60, FAKE, 3, 28, 28, 2, 0, None, None) == d["CPTHD_ERR_ALIGN"]
+    assert f(A + 8, B, C, E, 64, FAKE, 3, 28, 28, 2, 0, None, None) == d["CPTHD_ERR_ALIGN"]
+    assert f(A, B, A + 64, E, 64, FAKE, 3, 28, 28, 2, 0, None, None) == d["CPTHD_ERR_ALIAS"]   # DCS out overlaps in
+    assert f(A, B, A, B, 64, FAKE, 3, 28, 28, 2, 0, None, None) == d["CPTHD_ERR_ALIAS"]
+    assert f(A, B, A, B, 64, FAKE, 3, 28, 28, 2, 1, None, None) == 0    # contiguous in place: nothing to do
+
+
+def test_workspace_bytes(lib):
+    f = lib.cpthd_attn_workspace_bytes
+    n = f(65536, 4, 32, 8, 128, 200)
+    assert n > 16384 * 32 * 4            # holds at least delta [S, Hq] fp32
+    assert f(65536, 4, 32, 8, 128, 400) > n
+    assert f(65536, 4, 32, 7, 128, 200) == 0    # Hq % Hkv
+    assert f(65536, 4, 32, 8, 96, 200) == 0     # head_dim
+    assert f(65536, 4, 128, 1, 128, 200) == 0   # G > 64
+    assert f(65535, 4, 32, 8, 128, 200) == 0    # capacity % cp
+    assert f(65536, 0, 32, 8, 128, 200) == 0
+    assert f(65536, 4, 32, 8, 128, 0) == 0
+
+
+def test_attention_host_errors(lib):
+    d = _defines()
+    ws_bytes = lib.cpthd_attn_workspace_bytes(64, 2, 4, 2, 16, 4)
+    plan, fwd, bwd = lib.cpthd_attn_plan, lib.cpthd_attn_fwd, lib.cpthd_attn_bwd
+    P = 0x100000  # 256-aligned fake pointer
+    ok = dict(T=64, cap=64, B=4, cp=2, r=0, s=0, hq=4, hkv=2, D=16)
+
+    def call_plan(**kw):
+        a = dict(ok, **kw)
+        return plan(P, P, a["B"], a["T"], a["cap"], a["cp"], a["r"], a["s"], a["hq"], a["hkv"], a["D"],
+                    kw.get("ws", P), kw.get("wsb", ws_bytes), None, None)
+
+    assert plan(None, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, P, ws_bytes, None, None) == d["CPTHD_ERR_NULL"]
+    assert call_plan(r=2) == d["CPTHD_ERR_RANK"]
+    assert call_plan(s=2) == d["CPTHD_ERR_STRATEGY"]
+    assert call_plan(T=66) == d["CPTHD_ERR_TOKENS"]
+    assert call_plan(T=128) == d["CPTHD_ERR_TOKENS"]        # above capacity
+    assert call_plan(hkv=3) == d["CPTHD_ERR_HEADS"]
+    assert call_plan(D=48) == d["CPTHD_ERR_HEADS"]
+    assert call_plan(ws=None) == d["CPTHD_ERR_WORKSPACE"]
+    assert call_plan(wsb=ws_bytes - 1) == d["CPTHD_ERR_WORKSPACE"]
+    assert call_plan(ws=P + 16) == d["CPTHD_ERR_WORKSPACE"]
+
+    def call_fwd(**kw):
+        a = dict(ok, **kw)
+        return fwd(P, P, P, a["T"], a["cap"], a["B"], a["cp"], a["r"], a["s"], a["hq"], a["hkv"], a["D"], 0.25,
+                   kw.get("causal", 1), kw.get("wl", -1), kw.get("wr", 0), P, P, P, ws_bytes, None, None, None, 0)
+
+    assert call_fwd(causal=0) == d["CPTHD_ERR_MASK"]
+    assert call_fwd(wl=128) == d["CPTHD_ERR_MASK"]
+    assert call_fwd(wr=1) == d["CPTHD_ERR_MASK"]
+    assert call_fwd(cp=0) == d["CPTHD_ERR_RANK"]
+    assert call_fwd(B=0) == d["CPTHD_ERR_TOKENS"]
+    assert fwd(P, None, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, ws_bytes, None, None, None, 0) \
+        == d["CPTHD_ERR_NULL"]
+    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, None, P, ws_bytes, None, None,
+               None, 0) == d["CPTHD_ERR_NULL"]
+    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 1, P, P, P, P, ws_bytes, None, None,
+               None, 0) == d["CPTHD_ERR_MASK"]
+    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, P, 16, None, None,
+               None, 0) == d["CPTHD_ERR_WORKSPACE"]
+
+
+def test_product_path_has_no_oracle_or_cpu_fallback():
+    pkg = os.path.join(ROOT, "context_causal_thd_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
+                assert "numpy" not in text, f

@@ -1,0 +1,219 @@
+"""GPU parity: attention forward (O, LSE) and backward (dQ, dK, dV) against the fp64 oracle.
+
+Inputs are the seeded bf16 values (the oracle runs on exactly those values,
+upcast to float64).  Small layouts are compared in full; the full-size
+configurations are compared on sampled documents and kv heads, which the
+oracle computes exactly, plus properties that hold everywhere (finite values,
+exact zeros on pads and untouched rows, nothing written past the active rows).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import assert_attn_close, bf16_dev, i32_dev, log, status_dev, to_np64
+
+pytestmark = pytest.mark.gpu
+
+cpthd = pytest.importorskip("context_causal_thd_amd")
+
+
+class Share:
+    """One rank's share on the GPU: plan, forward and (optionally) backward."""
+
+    def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False):
+        self.wl, self.s, self.r = wl, strategy, rank
+        T, cp = wl.T, wl.cp
+        S = T // cp
+        cap = capacity or T
+        capS = cap // cp
+        self.idx = oracle.partition_indices(wl.cu_padded, cp, rank, strategy)
+        q = wl.q(self.idx)
+        k, v = wl.k(), wl.v()
+        self.q_np, self.k_np, self.v_np = q, k, v
+        fill = float("nan") if poison else 0.0
+
+        def buf(shape_tail, src, dtype=torch.bfloat16, rows=cap):
+            t = torch.full((rows,) + shape_tail, fill, dtype=dtype, device="cuda")
+            if src is not None:
+                t[:src.shape[0]] = bf16_dev(src) if dtype == torch.bfloat16 else src
+            return t
+
+        self.q = buf((wl.Hq, wl.D), q, rows=capS)
+        self.k = buf((wl.Hkv, wl.D), k)
+        self.v = buf((wl.Hkv, wl.D), v)
+        self.cu_a, self.cu_p = i32_dev(wl.cu_actual), i32_dev(wl.cu_padded)
+        self.plan = cpthd.AttnPlan(cap, cp, wl.Hq, wl.Hkv, wl.D, max_docs=max(wl.num_docs, 1))
+        self.st = status_dev()
+        self.plan.build(self.cu_a, self.cu_p, T, rank, strategy, self.st)
+        canary = 7.0
+        self.o = torch.full((capS, wl.Hq, wl.D), canary, dtype=torch.bfloat16, device="cuda")
+        self.lse = torch.full((capS, wl.Hq), canary, dtype=torch.float32, device="cuda")
+        cpthd.attn_fwd(self.q, self.k, self.v, self.plan, wl.softmax_scale, self.o, self.lse, self.st)
+        self.S, self.capS, self.cap = S, capS, cap
+        if backward:
+            do = wl.do(self.idx)
+            self.do_np = do
+            self.do = buf((wl.Hq, wl.D), do, rows=capS)
+            self.dq = torch.full((capS, wl.Hq, wl.D), canary, dtype=torch.float32, device="cuda")
+            self.dk = torch.full((cap, wl.Hkv, wl.D), canary, dtype=torch.float32, device="cuda")
+            self.dv = torch.full((cap, wl.Hkv, wl.D), canary, dtype=torch.float32, device="cuda")
+            cpthd.attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, self.plan, wl.softmax_scale,
+                           self.dq, self.dk, self.dv, self.st)
+        torch.cuda.synchronize()
+        assert int(self.st.item()) == 0, cpthd.api.describe_dev_status(int(self.st.item()))
+
+    def check_tails(self):
+        """Rows past the active prefix keep their canaries."""
+        S, T = self.S, self.wl.T
+        assert (self.o[S:].float() == 7.0).all() and (self.lse[S:] == 7.0).all()
+        if hasattr(self, "dq"):
+            assert (self.dq[S:] == 7.0).all() and (self.dk[T:] == 7.0).all() and (self.dv[T:] == 7.0).all()
+
+    def compare(self, docs=None, kv_heads=None, backward=True):
+        wl = self.wl
+        S, T = self.S, wl.T
+        o_ref, lse_ref, _ = oracle.attn_fwd(self.q_np, self.k_np, self.v_np, self.idx, wl.cu_padded, wl.cu_actual,
+                                            wl.softmax_scale, docs=docs, kv_heads=kv_heads)
+        o = to_np64(self.o[:S])
+        lse = to_np64(self.lse[:S])
+        assert np.isfinite(o).all(), "O must be finite everywhere"
+        _, _, valid_tok = oracle.token_map(wl.cu_padded, wl.cu_actual)
+        vq = valid_tok[self.idx]
+        assert np.isneginf(lse[~vq]).all() and (o[~vq] == 0).all(), "pad rows: O = 0, LSE = -inf"
+        assert np.isfinite(lse[vq]).all()
+        assert_attn_close("O", o, o_ref, vq[:, None, None])
+        assert_attn_close("LSE", lse, lse_ref, vq[:, None])
+        if not backward:
+            return
+        dq_ref, dk_ref, dv_ref = oracle.attn_bwd(self.q_np, self.k_np, self.v_np, self.do_np, self.idx,
+                                                 wl.cu_padded, wl.cu_actual, wl.softmax_scale, docs=docs,
+                                                 kv_heads=kv_heads)
+        dq = to_np64(self.dq[:S])
+        dk = to_np64(self.dk[:T])
+        dv = to_np64(self.dv[:T])
+        for name, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
+            assert np.isfinite(x).all(), f"{name} must be finite everywhere"
+        assert (dq[~vq] == 0).all() and (dk[~valid_tok] == 0).all() and (dv[~valid_tok] == 0).all()
+        assert_attn_close("dQ", dq, dq_ref, vq[:, None, None])
+        assert_attn_close("dK", dk, dk_ref, valid_tok[:, None, None])
+        assert_attn_close("dV", dv, dv_ref, valid_tok[:, None, None])
+
+
+def _small_cases():
+    cases = []
+    seed = 0
+    for D in (16, 32, 64, 128):
+        for Hq, Hkv in ((2, 2), (4, 1), (8, 2), (6, 2), (16, 2)):
+            for cp, s in ((1, 0), (2, 0), (3, 1), (4, 1), (2, 1), (4, 0)):
+                seed += 1
+                if (seed % 3) and D != 128:
+                    continue
+                wl = W.small_random(seed, cp, s, max_docs=5, max_len=360, Hq=Hq, Hkv=Hkv, D=D, bf16=True)
+                cases.append(wl)
+    return cases
+
+
+SMALL = _small_cases()
+
+
+def test_config1_all_shares():
+    wl = W.config1(bf16=True)
+    for s in wl.strategies:
+        for r in wl.ranks:
+            log(f"config1 s={s} r={r}")
+            sh = Share(wl, s, r)
+            sh.compare()
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"{w.name}-D{w.D}-h{w.Hq}x{w.Hkv}-cp{w.cp}-s{w.strategies[0]}")
+def test_small_full_parity(wl):
+    s = wl.strategies[0]
+    for r in range(wl.cp):
+        log(f"{wl.name} T={wl.T} docs={wl.num_docs} s={s} r={r}")
+        sh = Share(wl, s, r)
+        sh.compare()
+
+
+def test_config2_forward_both_strategies():
+    wl = W.config2()
+    for s in wl.strategies:
+        for r in wl.ranks:
+            log(f"config2 s={s} r={r}")
+            sh = Share(wl, s, r, backward=False)
+            sh.compare(backward=False)
+
+
+def _sample_docs(wl, idx, n=3):
+    """Largest document the rank touches, smallest, and the one holding the rank's first row."""
+    doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    touched = np.unique(doc[idx])
+    L = np.diff(wl.cu_padded.astype(np.int64))[touched]
+    pick = {int(touched[np.argmax(L)]), int(touched[np.argmin(L)]), int(doc[idx[0]])}
+    return sorted(pick)[:n]
+
+
+@pytest.mark.parametrize("s", [0, 1])
+@pytest.mark.parametrize("r", [0, 3])
+def test_config3_sampled(s, r):
+    wl = W.config3()
+    log(f"config3 s={s} r={r}")
+    sh = Share(wl, s, r)
+    docs = _sample_docs(wl, sh.idx)
+    log(f"  docs {docs}")
+    sh.compare(docs=docs, kv_heads=[0, 7])
+
+
+@pytest.mark.parametrize("r", [0, 7])
+def test_config4_sampled(r):
+    wl = W.config4()
+    log(f"config4 r={r}")
+    sh = Share(wl, 1, r)
+    doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    touched = np.unique(doc[sh.idx])
+    L = np.diff(wl.cu_padded.astype(np.int64))[touched]
+    docs = sorted({int(touched[np.argmin(L)]), int(doc[sh.idx[0]])})
+    log(f"  docs {docs}")
+    sh.compare(docs=docs, kv_heads=[5])
+
+
+def test_config5_capacity_microbatches():
+    """Fixed-capacity buffers, NaN-poisoned beyond the active T, canaries on output tails."""
+    for m in (0, 5, 11):
+        wl = W.config5(m)
+        for s in wl.strategies:
+            for r in (0, 3):
+                log(f"config5 mb={m} T={wl.T} s={s} r={r}")
+                sh = Share(wl, s, r, capacity=W.CONFIG5_CAPACITY, poison=True)
+                sh.check_tails()
+                docs = _sample_docs(wl, sh.idx, n=2)
+                sh.compare(docs=docs, kv_heads=[3])
+
+
+def test_plan_mismatch_sets_status_and_writes_nothing():
+    wl = W.config1(bf16=True)
+    sh = Share(wl, 0, 0)
+    st = status_dev()
+    o = torch.full_like(sh.o, 3.0)
+    lse = torch.full_like(sh.lse, 3.0)
+    # rank 1 against a plan built for rank 0
+    cpthd.cpthd_attn_fwd(sh.q, sh.k, sh.v, wl.T, wl.T, wl.num_docs, wl.cp, 1, 0, wl.Hq, wl.Hkv, wl.D,
+                         wl.softmax_scale, 1, -1, 0, o, lse, sh.plan.workspace, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 16
+    assert (o.float() == 3.0).all() and (lse == 3.0).all()
+
+
+def test_plan_rejects_bad_layouts():
+    wl = W.config1(bf16=True)
+    plan = cpthd.AttnPlan(64, 2, 2, 2, 16, max_docs=4)
+    st = status_dev()
+    cu_bad = i32_dev([0, 6, 20, 28])                          # 6 % 4 != 0 under DCS
+    plan.build(i32_dev(wl.cu_actual), cu_bad, 28, 0, 0, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 4
+    st = status_dev()
+    plan.build(i32_dev([0, 9, 17, 24]), i32_dev(wl.cu_padded), 28, 0, 0, st)   # actual 9 > padded 8
+    torch.cuda.synchronize()
+    assert int(st.item()) & 8

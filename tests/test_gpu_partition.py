@@ -1,0 +1,120 @@
+"""GPU parity: partition indices and K/V restoration are bit-exact against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import i32_dev, log, status_dev
+
+pytestmark = pytest.mark.gpu
+
+cpthd = pytest.importorskip("context_causal_thd_amd")
+
+
+def _layouts():
+    out = [("config1", W.config1()), ("config2", W.config2()), ("config3", W.config3()), ("config4", W.config4())]
+    out += [(f"config5.mb{m}", W.config5(m)) for m in range(W.CONFIG5_MICROBATCHES)]
+    for seed in range(12):
+        for cp in (1, 2, 3, 4, 8):
+            for s in (0, 1):
+                out.append((f"small{seed}.cp{cp}.s{s}", W.small_random(seed, cp, s, max_docs=7, max_len=200)))
+    return out
+
+
+LAYOUTS = _layouts()
+
+
+def _gpu_indices(cu_p, T, cp, r, s):
+    cu = i32_dev(cu_p)
+    out = torch.full((T // cp + 8,), -7, dtype=torch.int32, device="cuda")   # canary tail
+    st = status_dev()
+    cpthd.cpthd_partition_indices(cu, cu.numel() - 1, T, cp, r, s, out, st)
+    res = out.cpu().numpy()
+    assert (res[T // cp:] == -7).all(), "wrote past T/cp"
+    assert int(st.item()) == 0
+    return res[:T // cp]
+
+
+@pytest.mark.parametrize("name,wl", LAYOUTS, ids=[n for n, _ in LAYOUTS])
+def test_partition_bit_exact(name, wl):
+    log(f"partition {name}")
+    for s in (0, 1):
+        try:
+            oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
+        except ValueError:
+            continue
+        for r in range(wl.cp):
+            ref = oracle.partition_indices(wl.cu_padded, wl.cp, r, s)
+            got = _gpu_indices(wl.cu_padded, wl.T, wl.cp, r, s)
+            np.testing.assert_array_equal(got, ref)
+
+
+def test_partition_million_tokens_ten_thousand_docs():
+    cu_p, _ = W.config5b()
+    T = int(cu_p[-1])
+    for s in (0, 1):
+        for r in range(4):
+            log(f"partition 5b s={s} r={r}")
+            np.testing.assert_array_equal(_gpu_indices(cu_p, T, 4, r, s), oracle.partition_indices(cu_p, 4, r, s))
+
+
+def test_partition_device_status_bits():
+    cu = i32_dev([0, 6, 16])                     # 6 not divisible by 2*cp = 4
+    out = torch.empty(8, dtype=torch.int32, device="cuda")
+    st = status_dev()
+    cpthd.cpthd_partition_indices(cu, 2, 16, 2, 0, 0, out, st)
+    assert int(st.item()) & 4
+    st = status_dev()
+    cpthd.cpthd_partition_indices(cu, 2, 16, 2, 0, 1, out, st)   # contiguous accepts it
+    assert int(st.item()) == 0
+    st = status_dev()
+    cpthd.cpthd_partition_indices(i32_dev([0, 8, 4, 16]), 3, 16, 2, 0, 1, out, st)
+    assert int(st.item()) & 1
+    st = status_dev()
+    cpthd.cpthd_partition_indices(i32_dev([0, 8, 12]), 2, 16, 2, 0, 1, out, st)
+    assert int(st.item()) & 2
+    torch.cuda.synchronize()
+
+
+def _rand_rows(T, row_elems, seed):
+    rng = np.random.default_rng(seed)
+    bits = rng.integers(0, 1 << 16, size=(T, row_elems), dtype=np.uint16)   # any bit pattern, NaNs included
+    return torch.from_numpy(bits.view(np.int16)).to("cuda")
+
+
+REORDER = [(n, wl) for n, wl in LAYOUTS if not n.startswith("config4")][::2] + [("config3", W.config3())]
+
+
+@pytest.mark.parametrize("name,wl", REORDER, ids=[n for n, _ in REORDER])
+def test_reorder_bit_exact(name, wl):
+    log(f"reorder {name}")
+    row_elems = 1024 if wl.T >= 4096 else 8 * (1 + wl.T % 3)
+    cap = max(wl.T, wl.capacity) + 16
+    for s in (0, 1):
+        try:
+            oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
+        except ValueError:
+            continue
+        k_phys = _rand_rows(wl.T, row_elems, 1)
+        v_phys = _rand_rows(wl.T, row_elems, 2)
+        parts = [oracle.partition_indices(wl.cu_padded, wl.cp, r, s) for r in range(wl.cp)]
+        order = torch.from_numpy(oracle.all_gather(np.arange(wl.T), parts)).to("cuda")
+        kg = torch.full((cap, row_elems), 0x7FC0, dtype=torch.int16, device="cuda")
+        vg = torch.full((cap, row_elems), 0x7FC0, dtype=torch.int16, device="cuda")
+        kg[:wl.T] = k_phys[order]          # simulated all-gather (rank-major), oracle partition
+        vg[:wl.T] = v_phys[order]
+        ko = torch.full((cap, row_elems), 123, dtype=torch.int16, device="cuda")
+        vo = torch.full((cap, row_elems), 123, dtype=torch.int16, device="cuda")
+        st = status_dev()
+        cpthd.cpthd_reorder_kv(kg, vg, ko, vo, row_elems * 2, i32_dev(wl.cu_padded), wl.num_docs, wl.T, cap,
+                               wl.cp, s, st)
+        assert int(st.item()) == 0
+        assert torch.equal(ko[:wl.T], k_phys) and torch.equal(vo[:wl.T], v_phys)
+        assert (ko[wl.T:] == 123).all() and (vo[wl.T:] == 123).all(), "wrote past T"
+        if s == 1:   # in place: nothing to do and nothing changes
+            before = kg.clone()
+            cpthd.cpthd_reorder_kv(kg, vg, kg, vg, row_elems * 2, i32_dev(wl.cu_padded), wl.num_docs, wl.T, cap,
+                                   wl.cp, s, st)
+            assert torch.equal(kg, before)
+    torch.cuda.synchronize()

@@ -225,3 +225,20 @@ def test_docs_subset_matches_full():
         np.testing.assert_array_equal(sdq[comp], dq[comp])
         np.testing.assert_array_equal(sdk[lo:hi], dk[lo:hi])
         np.testing.assert_array_equal(sdv[lo:hi], dv[lo:hi])
+
+
+def test_kv_head_subset_matches_full():
+    wl = W.small_random(9, 2, 1, max_docs=4, max_len=24, Hq=4, Hkv=2, D=4)
+    idx, q, k, v, do = _inputs(wl, 0, 1)
+    o, lse, _ = oracle.attn_fwd(q, k, v, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale)
+    dq, dk, dv = oracle.attn_bwd(q, k, v, do, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale)
+    for g in range(2):
+        so, slse, _ = oracle.attn_fwd(q, k, v, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, kv_heads=[g])
+        sdq, sdk, sdv = oracle.attn_bwd(q, k, v, do, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, kv_heads=[g])
+        hs = slice(2 * g, 2 * g + 2)
+        np.testing.assert_array_equal(so[:, hs], o[:, hs])
+        np.testing.assert_array_equal(slse[:, hs], lse[:, hs])
+        np.testing.assert_array_equal(sdq[:, hs], dq[:, hs])
+        np.testing.assert_array_equal(sdk[:, g], dk[:, g])
+        np.testing.assert_array_equal(sdv[:, g], dv[:, g])
+        assert np.isnan(so[:, 2 * (1 - g)]).all() and np.isnan(sdk[:, 1 - g]).all()
