@@ -236,7 +236,7 @@ def config5b():
 
 
 def small_random(seed, cp, strategy, max_docs=5, max_len=32, Hq=2, Hkv=1, D=16, pads=True,
-                 bf16=False) -> Workload:
+                 bf16=False, qkv_scale=1.0, do_scale=1.0) -> Workload:
     """A tiny random layout valid for the given strategy (for brute-force checks)."""
     rng = np.random.default_rng([1000, seed])
     nd = int(rng.integers(1, max_docs + 1))
@@ -261,4 +261,4 @@ def small_random(seed, cp, strategy, max_docs=5, max_len=32, Hq=2, Hkv=1, D=16, 
         actual[-1] = 2 * cp if not pads else int(rng.integers(0, 2 * cp + 1))
         T = 2 * cp
     return Workload(f"small{seed}", [1000, seed], T, Hq, Hkv, D, _cu(padded), _cu(actual), cp,
-                    (strategy,), tuple(range(cp)), True, qkv_scale=1.0, do_scale=1.0, bf16=bf16)
+                    (strategy,), tuple(range(cp)), True, qkv_scale=qkv_scale, do_scale=do_scale, bf16=bf16)
