@@ -1,0 +1,266 @@
+"""Throughput of one CP rank's share of causal THD attention on one MI355X.
+
+A step is one pass of the whole hot path over the configured rank shares of
+the Llama-3-8B-shaped packed workload (T = 32768 bf16 tokens, 32 q / 8 kv
+heads, head dim 128, log-normal document lengths padded to multiples of 8,
+cp_size = 4, ranks 0 and 3, both strategies).  For every share:
+
+  partition indices -> (DualChunkSwap: K/V restoration from the rank-major
+  gathered buffer) -> attention plan -> forward (O, LSE) -> backward (dQ, dK, dV)
+
+Inputs are resident in HBM before the timed region.  The metric is useful
+causal attention FLOP/s: forward 4*D*Hq*N, backward 10*D*Hq*N, with N the
+number of (query, key) pairs the causal document mask allows for the share's
+actual query rows.  Prints one JSON line; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads as W  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+SHARES = [(0, 0), (0, 3), (1, 0), (1, 3)]   # (strategy, rank)
+STRAT_NAME = {0: "dcs", 1: "contiguous"}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def useful_pairs(idx, cu_p, cu_a):
+    """Allowed (query, key) pairs for the rank's query rows: sum over actual rows of (position + 1)."""
+    cu_p = cu_p.astype(np.int64)
+    cu_a = cu_a.astype(np.int64)
+    doc = np.searchsorted(cu_p, idx, side="right") - 1
+    pos = idx - cu_p[doc]
+    actual = cu_a[doc + 1] - cu_a[doc]
+    ok = pos < actual
+    return int(np.sum(pos[ok] + 1))
+
+
+def cpu_baseline(wl, budget_s=15.0):
+    """Time the CPU oracle (fwd + bwd) on a bounded sample: whole kv heads of the DualChunkSwap rank-0 share."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    idx = oracle.partition_indices(wl.cu_padded, wl.cp, 0, 0)
+    q, k, v, do = wl.q(idx), wl.k(), wl.v(), wl.do(idx)
+    pairs = useful_pairs(idx, wl.cu_padded, wl.cu_actual)
+    G = wl.Hq // wl.Hkv
+    t0 = time.perf_counter()
+    heads = 0
+    for g in range(wl.Hkv):
+        oracle.attn_fwd(q, k, v, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, kv_heads=[g])
+        oracle.attn_bwd(q, k, v, do, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, kv_heads=[g])
+        heads += 1
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    flops = 14.0 * wl.D * G * heads * pairs
+    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"fwd+bwd of {heads} of {wl.Hkv} kv heads ({heads * G} of {wl.Hq} q heads) of the "
+                      f"DualChunkSwap rank-0 share, all {wl.num_docs} documents ({pairs} causal pairs per head), "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU's rank share only; run it with --gpus 1 (the multi-GPU all-gather / "
+              "reduce-scatter path is not part of this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import context_causal_thd_amd as cpthd
+
+    dev = "cuda"
+    wl = W.config3()
+    T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
+    S = T // cp
+    log(f"workload: T={T} docs={wl.num_docs} Hq={Hq} Hkv={Hkv} D={D} cp={cp}")
+
+    def bf16(x):
+        return torch.from_numpy(W.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q_full, k_phys, v_phys, do_full = bf16(wl.q()), bf16(wl.k()), bf16(wl.v()), bf16(wl.do())
+    cu_a = torch.from_numpy(wl.cu_actual).to(dev)
+    cu_p = torch.from_numpy(wl.cu_padded).to(dev)
+    status = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    # per-share resident buffers (untimed set-up)
+    shares = []
+    for s, r in SHARES:
+        idx = cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status)
+        idx_l = idx.long()
+        sh = dict(s=s, r=r, idx=torch.empty_like(idx), q=q_full[idx_l].contiguous(), do=do_full[idx_l].contiguous())
+        if s == 0:   # simulated all-gather: rank-major concatenation of every rank's K/V rows
+            parts = [cpthd.partition_indices(cu_p, T, cp, rr, s, dev_status=status).long() for rr in range(cp)]
+            order = torch.cat(parts)
+            sh["kg"], sh["vg"] = k_phys[order].contiguous(), v_phys[order].contiguous()
+            sh["k"], sh["v"] = torch.empty_like(k_phys), torch.empty_like(v_phys)
+        else:        # rank-major contiguous ownership: the gathered buffer is already physical order
+            sh["kg"], sh["vg"] = k_phys, v_phys
+            sh["k"], sh["v"] = k_phys, v_phys
+        sh["plan"] = cpthd.AttnPlan(T, cp, Hq, Hkv, D, max_docs=wl.num_docs)
+        sh["o"] = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+        sh["lse"] = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+        sh["dq"] = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+        sh["dk"] = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+        sh["dv"] = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+        sh["pairs"] = useful_pairs(idx.cpu().numpy().astype(np.int64), wl.cu_padded, wl.cu_actual)
+        shares.append(sh)
+    del q_full, do_full
+    torch.cuda.synchronize()
+    cpthd.check_dev_status(status)
+
+    row_bytes = Hkv * D * 2
+    n_kernels = 6   # partition, reorder, plan, fwd, bwd-dq, bwd-dkdv
+
+    def make_events():
+        return ([[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)] for _ in shares],
+                [[cpthd.HipEvents(2), cpthd.HipEvents(4)] for _ in shares])
+
+    def step(evs):
+        for i, sh in enumerate(shares):
+            e, he = (evs[0][i], evs[1][i]) if evs else (None, None)
+            if e:
+                e[0][0].record()
+            cpthd.partition_indices(cu_p, T, cp, sh["r"], sh["s"], out=sh["idx"], dev_status=status)
+            if e:
+                e[0][1].record()
+                e[1][0].record()
+            if sh["s"] == 0:
+                cpthd.reorder_kv(sh["kg"], sh["vg"], cu_p, T, cp, 0, k_out=sh["k"], v_out=sh["v"],
+                                 dev_status=status)
+            if e:
+                e[1][1].record()
+                e[2][0].record()
+            sh["plan"].build(cu_a, cu_p, T, sh["r"], sh["s"], status)
+            if e:
+                e[2][1].record()
+            cpthd.attn_fwd(sh["q"], sh["k"], sh["v"], sh["plan"], wl.softmax_scale, sh["o"], sh["lse"], status,
+                           events=he[0] if he else None)
+            cpthd.attn_bwd(sh["q"], sh["k"], sh["v"], sh["o"], sh["do"], sh["lse"], sh["plan"], wl.softmax_scale,
+                           sh["dq"], sh["dk"], sh["dv"], status, events=he[1] if he else None)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    cpthd.check_dev_status(status)
+    log(f"warmup done ({args.warmup} steps)")
+
+    events = [make_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k_step in range(args.steps):
+        step(events[k_step])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    cpthd.check_dev_status(status)
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+    acc = np.zeros((len(shares), n_kernels))
+    for evs, hevs in events:
+        for i in range(len(shares)):
+            for j in range(3):
+                acc[i, j] += evs[i][j][0].elapsed_time(evs[i][j][1])
+            acc[i, 3] += hevs[i][0].elapsed_ms(0, 1)
+            acc[i, 4] += hevs[i][1].elapsed_ms(0, 1)
+            acc[i, 5] += hevs[i][1].elapsed_ms(2, 3)
+
+    # pure-GPU step time: the per-kernel event durations of one step
+    per_kernel_ms = acc / args.steps
+    gpu_step_ms = float(per_kernel_ms.sum())
+    wall_step_ms = elapsed * 1e3 / args.steps
+    pairs = np.array([sh["pairs"] for sh in shares], dtype=np.float64)
+    flops_fwd = 4.0 * D * Hq * pairs
+    flops_bwd = 10.0 * D * Hq * pairs
+    step_flops = float(np.sum(flops_fwd + flops_bwd))
+    value = step_flops / (wall_step_ms * 1e-3) / 1e12
+
+    names = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"]
+    kernel_ms = {n: float(per_kernel_ms[:, j].sum()) for j, n in enumerate(names)}
+    # algorithmic flops per kernel: fwd = 4DHqN; of the backward's 10DHqN, the key-tile pass computes the
+    # score and dP recompute plus dK and dV (8DHqN), the query-tile pass dQ (2DHqN; its recompute is extra)
+    algo = {"attn_fwd": flops_fwd, "attn_bwd_dkdv": 0.8 * flops_bwd, "attn_bwd_dq": 0.2 * flops_bwd}
+    dominant = max(algo, key=lambda n: kernel_ms[n])
+    j = names.index(dominant)
+    achieved = float(np.sum(algo[dominant]) / (kernel_ms[dominant] * 1e-3) / 1e12)
+    roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "avg_launch_us": float(per_kernel_ms[:, j].mean() * 1e3)}
+
+    dcs = [i for i, sh in enumerate(shares) if sh["s"] == 0]
+    part_bytes = 4.0 * S
+    reorder_bytes = 2.0 * 2.0 * T * row_bytes      # read + write of K and V
+    breakdown = {
+        "per_share": [
+            {"strategy": STRAT_NAME[sh["s"]], "rank": sh["r"], "causal_pairs_per_head": int(sh["pairs"]),
+             "fwd_tflops": float(flops_fwd[i] / (per_kernel_ms[i, 3] * 1e-3) / 1e12),
+             "bwd_tflops": float(flops_bwd[i] / ((per_kernel_ms[i, 4] + per_kernel_ms[i, 5]) * 1e-3) / 1e12),
+             "fwd_bwd_tflops": float((flops_fwd[i] + flops_bwd[i]) / (per_kernel_ms[i, 3:].sum() * 1e-3) / 1e12),
+             "ms": {n: float(per_kernel_ms[i, jj]) for jj, n in enumerate(names)}}
+            for i, sh in enumerate(shares)],
+        "kernel_ms_per_step": kernel_ms,
+        "attn_fwd_bwd_tflops": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12),
+        "attn_frac_of_bf16_peak": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS),
+        "partition_gbs": float(part_bytes / (per_kernel_ms[:, 0].mean() * 1e-3) / 1e9),
+        "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
+        "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
+        "gpu_kernel_ms_per_step": gpu_step_ms,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle) ...")
+        cpu = cpu_baseline(wl, args.cpu_budget)
+
+    out = {
+        "metric": "useful causal attn TFLOP/s per CP-rank share (fwd+bwd) + % bf16 MFMA peak",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall_step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "config3: T=32768 packed bf16 tokens, 32 q / 8 kv heads, head_dim 128, log-normal "
+                               "doc lengths (median 1024, sigma 1) clipped to [64,8192] padded to x8, cp_size=4; "
+                               "shares dcs r0, dcs r3, contiguous r0, contiguous r3; partition + reorder + plan + "
+                               "attention fwd + bwd per share",
+                   "T": T, "cp_size": cp, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
+                   "num_docs": wl.num_docs, "parallelism": "one CP rank share per call, 1 GPU"},
+        "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "breakdown": breakdown,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
