@@ -10,12 +10,17 @@
 // T physical rows; a reduce-scatter over the ranks would sum them.
 //
 // Two passes, no atomics, deterministic:
-//   1. query tiles (the forward's tiles): delta from O and dO, then
-//      S^T = K Q^T, P^T = exp2(S^T - LSE), dP^T = V dO^T, dS^T, dQ^T += K^T dS^T;
-//   2. key tiles (128 keys of one document, 32 per wave): for every query row of
-//      the rank that sees the tile, 64 rows per step,
-//      S = Q K^T, dP = dO V^T (key as the lane index), dS,
-//      dV += P^T dO, dK += dS^T Q with Q and dO staged transposed in LDS.
+//   1. query tiles (the forward's tiles, 64 rows per wave): delta from O and
+//      dO, then per 64-key step S^T = K Q^T, P^T = exp2(S^T - LSE),
+//      dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (the K^T
+//      operand comes from the natural K tile through the transpose LDS read);
+//   2. key tiles (128 keys of one document, 32 per wave): for every query row
+//      of the rank that sees the tile, 64 rows per step, S = Q K^T and
+//      dP = dO V^T with the key as the lane index, dS = P (dP - delta),
+//      dV += P^T dO and dK += dS^T Q (dO^T and Q^T operands through the
+//      transpose read of the natural tiles).
+// Both passes load the next step's rows into registers while computing the
+// current one and double-buffer their LDS tiles.
 #include "attn_common.h"
 #include "cpthd_host.h"
 
@@ -29,9 +34,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  __shared__ __align__(16) uint16_t Ks[kKvStep * (DP + 8)];
-  __shared__ __align__(16) uint16_t Kt[DP * (kKvStep + 8)];
-  __shared__ __align__(16) uint16_t Vs[kKvStep * (DP + 8)];
+  constexpr int KS = Lds<DP>::kNat;
+  __shared__ __align__(16) uint16_t Ks[2][kKvStep * KS];
+  __shared__ __align__(16) uint16_t Vs[2][kKvStep * KS];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   if (!plan_matches(hdr, prm)) {
@@ -50,91 +55,137 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
-  const int m = wave * 32 + l32;
-  const int tt = m / G, g = m - tt * G;
-  const bool row_in = m < bm * G && tt < t.ntok;
-  const int p_q = t.p0 + tt;
-  const bool valid = row_in && p_q < t.ve;
-  const int64_t qrow = (int64_t)(t.lrow0 + tt) * Hq + kvh * G + g;
 
-  bf16x8 qf[DP / 16], df[DP / 16];
-  float dpart = 0.f;
+  bool row_in[2], valid[2];
+  int p_q[2];
+  int64_t qrow[2];
+  float dlt[2], lse2[2];
+  bf16x8 qf[2][DP / 16], df[2][DP / 16];
 #pragma unroll
-  for (int s = 0; s < DP / 16; ++s) {
-    u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
-    const int d = 16 * s + 8 * h;
-    if (valid && d < D) {
-      qv = *reinterpret_cast<const u32x4*>(q + qrow * D + d);
-      dv4 = *reinterpret_cast<const u32x4*>(dout + qrow * D + d);
-      ov = *reinterpret_cast<const u32x4*>(o + qrow * D + d);
+  for (int qb = 0; qb < 2; ++qb) {
+    const int m = wave * kRowsPerWave + 32 * qb + l32;
+    const int tt = m / G, g = m - tt * G;
+    row_in[qb] = m < bm * G && tt < t.ntok;
+    p_q[qb] = t.p0 + tt;
+    valid[qb] = row_in[qb] && p_q[qb] < t.ve;
+    qrow[qb] = (int64_t)(t.lrow0 + tt) * Hq + kvh * G + g;
+    float dpart = 0.f;
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) {
+      u32x4 qv = {0u, 0u, 0u, 0u}, dv4 = {0u, 0u, 0u, 0u}, ov = {0u, 0u, 0u, 0u};
+      const int d = 16 * s + 8 * h;
+      if (valid[qb] && d < D) {
+        qv = *reinterpret_cast<const u32x4*>(q + qrow[qb] * D + d);
+        dv4 = *reinterpret_cast<const u32x4*>(dout + qrow[qb] * D + d);
+        ov = *reinterpret_cast<const u32x4*>(o + qrow[qb] * D + d);
+      }
+      qf[qb][s] = as_bf16x8(qv);
+      df[qb][s] = as_bf16x8(dv4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = dv4[i], b = ov[i];
+        dpart += __uint_as_float(a << 16) * __uint_as_float(b << 16) +
+                 __uint_as_float(a & 0xFFFF0000u) * __uint_as_float(b & 0xFFFF0000u);
+      }
     }
-    qf[s] = as_bf16x8(qv);
-    df[s] = as_bf16x8(dv4);
-    const uint16_t* a = reinterpret_cast<const uint16_t*>(&dv4);
-    const uint16_t* b = reinterpret_cast<const uint16_t*>(&ov);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dpart += __uint_as_float((uint32_t)a[i] << 16) * __uint_as_float((uint32_t)b[i] << 16);
+    dlt[qb] = dpart + xor32(dpart);
+    if (row_in[qb] && h == 0) delta[qrow[qb]] = valid[qb] ? dlt[qb] : 0.f;
+    lse2[qb] = valid[qb] ? lse[qrow[qb]] * 1.4426950408889634f : INFINITY;
   }
-  const float dlt = dpart + xor32(dpart);
-  if (row_in && h == 0) delta[qrow] = valid ? dlt : 0.f;
-  const float lse2 = valid ? lse[qrow] * 1.4426950408889634f : INFINITY;
 
-  f32x16 acc[DP / 32];
+  f32x16 acc[2][DP / 32];
 #pragma unroll
-  for (int db = 0; db < DP / 32; ++db) acc[db] = f32x16{};
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db) acc[qb][db] = f32x16{};
 
-  const float sl2 = prm.scale_log2;
-  for (int kb = t.ds; kb < t.kv_end; kb += kKvStep) {
-    __syncthreads();
-    const int kend = t.kv_end;
+  const int kend = t.kv_end;
+  TileRegs<DP, kKvStep> kr, vr;
+  auto fetch = [&](int kb) {
     auto key_row = [&](int r) -> int64_t {
       const int kabs = kb + r;
       return kabs < kend ? (int64_t)kabs * Hkv + kvh : -1;
     };
-    stage_rows<DP, kKvStep, true, true>(k, D, key_row, Ks, Kt);
-    stage_rows<DP, kKvStep, true, false>(v, D, key_row, Vs, nullptr);
-    __syncthreads();
+    kr.load(k, D, key_row);
+    vr.load(v, D, key_row);
+  };
+  const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
+  if (nsteps > 0) {
+    fetch(t.ds);
+    kr.store(Ks[0], KS);
+    vr.store(Vs[0], KS);
+  }
+  __syncthreads();
 
+  const float sl2 = prm.scale_log2;
+  for (int it = 0; it < nsteps; ++it) {
+    const int kb = t.ds + it * kKvStep;
+    const int buf = it & 1;
+    if (it + 1 < nsteps) fetch(kb + kKvStep);
+    const uint16_t* Kt = Ks[buf];
+    const uint16_t* Vt = Vs[buf];
     const bool need_mask = kb + kKvStep - 1 > t.p0;
-    bf16x8 dsb[4];
+
+    bf16x8 dsb[2][4];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
-        sc = mfma32(lds_a_nat<DP>(Ks, 32 * b + l32, s, h), qf[s], sc);
-        dp = mfma32(lds_a_nat<DP>(Vs, 32 * b + l32, s, h), df[s], dp);
+        const bf16x8 ka = lds_row8(Kt, KS, 32 * b + l32, 16 * s, h);
+        const bf16x8 va = lds_row8(Vt, KS, 32 * b + l32, 16 * s, h);
+        sc[0] = mfma32(ka, qf[0][s], sc[0]);
+        sc[1] = mfma32(ka, qf[1][s], sc[1]);
+        dp[0] = mfma32(va, df[0][s], dp[0]);
+        dp[1] = mfma32(va, df[1][s], dp[1]);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pv = exp2_fast(sc[r] * sl2 - lse2);
-        if (need_mask) {
-          const int key = kb + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (key > p_q) pv = 0.f;
+      for (int qb = 0; qb < 2; ++qb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float pv = exp2_fast(fmaf(sc[qb][r], sl2, -lse2[qb]));
+          if (need_mask) {
+            const int key = kb + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (key > p_q[qb]) pv = 0.f;
+          }
+          sc[qb][r] = pv * (dp[qb][r] - dlt[qb]);
         }
-        sc[r] = pv * (dp[r] - dlt);
+        dsb[qb][2 * b] = acc_to_bf16(sc[qb], 0);
+        dsb[qb][2 * b + 1] = acc_to_bf16(sc[qb], 8);
       }
-      dsb[2 * b] = acc_to_bf16(sc, 0);
-      dsb[2 * b + 1] = acc_to_bf16(sc, 8);
     }
 #pragma unroll
     for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc[db] = mfma32(lds_a_trn<kKvStep>(Kt, 32 * db + l32, ks, h), dsb[ks], acc[db]);
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = lds_tr8(Kt, KS, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
+        acc[0][db] = mfma32(a, dsb[0][ks], acc[0][db]);
+        acc[1][db] = mfma32(a, dsb[1][ks], acc[1][db]);
+      }
+
+    if (it + 1 < nsteps) {
+      kr.store(Ks[buf ^ 1], KS);
+      vr.store(Vs[buf ^ 1], KS);
+    }
+    __syncthreads();
   }
 
-  if (!row_in) return;
-  const float sc = valid ? prm.scale : 0.f;
 #pragma unroll
-  for (int db = 0; db < DP / 32; ++db)
+  for (int qb = 0; qb < 2; ++qb) {
+    if (!row_in[qb]) continue;
+    const float sc = valid[qb] ? prm.scale : 0.f;
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const int d0 = 32 * db + 8 * gi + 4 * h;
-      if (d0 < D) {
-        f32x4 w = {acc[db][4 * gi] * sc, acc[db][4 * gi + 1] * sc, acc[db][4 * gi + 2] * sc, acc[db][4 * gi + 3] * sc};
-        *reinterpret_cast<f32x4*>(dq + qrow * D + d0) = w;
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const int d0 = 32 * db + 8 * gi + 4 * h;
+        if (d0 < D) {
+          const f32x4 w = {acc[qb][db][4 * gi] * sc, acc[qb][db][4 * gi + 1] * sc, acc[qb][db][4 * gi + 2] * sc,
+                           acc[qb][db][4 * gi + 3] * sc};
+          *reinterpret_cast<f32x4*>(dq + qrow[qb] * D + d0) = w;
+        }
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -145,12 +196,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ dk,
     float* __restrict__ dv, const char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  __shared__ __align__(16) uint16_t Qs[kQChunk * (DP + 8)];
-  __shared__ __align__(16) uint16_t Qt[DP * (kQChunk + 8)];
-  __shared__ __align__(16) uint16_t Ds[kQChunk * (DP + 8)];
-  __shared__ __align__(16) uint16_t Dt[DP * (kQChunk + 8)];
-  __shared__ float s_lse2[kQChunk], s_delta[kQChunk];
-  __shared__ int s_pq[kQChunk];
+  constexpr int QS = Lds<DP>::kNat;
+  __shared__ __align__(16) uint16_t Qs[2][kQChunk * QS];
+  __shared__ __align__(16) uint16_t Ds[2][kQChunk * QS];
+  __shared__ float s_lse2[2][kQChunk], s_delta[2][kQChunk];
+  __shared__ int s_pq[2][kQChunk];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   if (!plan_matches(hdr, prm)) {
@@ -193,58 +243,101 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     dva[db] = f32x16{};
   }
 
+  // the rank's rows of the document that see the tile: suffixes (token >= k0)
+  // of the document's segments, cut into steps of tpc tokens
+  const int tpc = kQChunk / G;
+  int plo[2], phi[2], sl[2], sp[2], nch[2];
+#pragma unroll
+  for (int si = 0; si < 2; ++si) {
+    sp[si] = si == 0 ? ds.pa : ds.pb;
+    const int sn = si == 0 ? ds.na : ds.nb;
+    sl[si] = si == 0 ? ds.la : ds.lb;
+    plo[si] = max(sp[si], kt.k0);
+    phi[si] = min(sp[si] + sn, ds.ve);
+    nch[si] = (phi[si] > plo[si] && sl[si] >= 0 && sl[si] + (phi[si] - sp[si]) <= S)
+                  ? (phi[si] - plo[si] + tpc - 1) / tpc : 0;
+  }
+  const int nchunks = nch[0] + nch[1];
+  auto chunk_c0 = [&](int i, int& si) {
+    si = i < nch[0] ? 0 : 1;
+    return plo[si] + (i - (si ? nch[0] : 0)) * tpc;
+  };
+
+  TileRegs<DP, kQChunk> qr, dr;
+  float pf_lse = INFINITY, pf_delta = 0.f;
+  int pf_pq = -1;
+  auto fetch = [&](int i) {
+    int si;
+    const int c0 = chunk_c0(i, si);
+    const int ntok = min(tpc, phi[si] - c0);
+    const int l0 = sl[si] + (c0 - sp[si]);
+    auto qrow_of = [&](int r) -> int64_t {
+      const int t2 = r / G;
+      return (r < tpc * G && t2 < ntok) ? (int64_t)(l0 + t2) * Hq + kvh * G + (r - t2 * G) : -1;
+    };
+    qr.load(q, D, qrow_of);
+    dr.load(dout, D, qrow_of);
+    if (tid < kQChunk) {
+      const int64_t qrw = qrow_of(tid);
+      pf_lse = qrw >= 0 ? lse[qrw] * 1.4426950408889634f : INFINITY;
+      pf_delta = qrw >= 0 ? delta[qrw] : 0.f;
+      pf_pq = qrw >= 0 ? c0 + tid / G : -1;
+    }
+  };
+  auto stage = [&](int buf) {
+    qr.store(Qs[buf], QS);
+    dr.store(Ds[buf], QS);
+    if (tid < kQChunk) {
+      s_lse2[buf][tid] = pf_lse;
+      s_delta[buf][tid] = pf_delta;
+      s_pq[buf][tid] = pf_pq;
+    }
+  };
+  if (nchunks > 0) {
+    fetch(0);
+    stage(0);
+  }
+  __syncthreads();
+
   const float sl2 = prm.scale_log2;
-  const int tpc = kQChunk / G;   // tokens per step
   const int kmax = kt.k0 + kt.nkeys - 1;
-  for (int segi = 0; segi < 2; ++segi) {
-    const int sp = segi == 0 ? ds.pa : ds.pb, sn = segi == 0 ? ds.na : ds.nb, sl = segi == 0 ? ds.la : ds.lb;
-    const int plo = max(sp, kt.k0), phi = min(sp + sn, ds.ve);
-    if (phi <= plo || sl < 0 || sl + (phi - sp) > S) continue;
-    for (int c0 = plo; c0 < phi; c0 += tpc) {
-      const int ntok = min(tpc, phi - c0);
-      const int l0 = sl + (c0 - sp);
-      __syncthreads();
-      auto qrow_of = [&](int r) -> int64_t {
-        const int t2 = r / G;
-        return (r < tpc * G && t2 < ntok) ? (int64_t)(l0 + t2) * Hq + kvh * G + (r - t2 * G) : -1;
-      };
-      stage_rows<DP, kQChunk, true, true>(q, D, qrow_of, Qs, Qt);
-      stage_rows<DP, kQChunk, true, true>(dout, D, qrow_of, Ds, Dt);
-      if (tid < kQChunk) {
-        const int64_t qr = qrow_of(tid);
-        s_lse2[tid] = qr >= 0 ? lse[qr] * 1.4426950408889634f : INFINITY;
-        s_delta[tid] = qr >= 0 ? delta[qr] : 0.f;
-        s_pq[tid] = qr >= 0 ? c0 + tid / G : -1;
+  for (int i = 0; i < nchunks; ++i) {
+    const int buf = i & 1;
+    int si;
+    const int c0 = chunk_c0(i, si);
+    if (i + 1 < nchunks) fetch(i + 1);
+    const bool need_mask = kmax > c0;   // some key of the tile lies after the step's first row
+    const uint16_t* Qt = Qs[buf];
+    const uint16_t* Dt = Ds[buf];
+#pragma unroll
+    for (int qb = 0; qb < kQChunk / 32; ++qb) {
+      f32x16 sc = f32x16{}, dp = f32x16{};
+#pragma unroll
+      for (int s = 0; s < DP / 16; ++s) {
+        sc = mfma32(lds_row8(Qt, QS, 32 * qb + l32, 16 * s, h), kf[s], sc);
+        dp = mfma32(lds_row8(Dt, QS, 32 * qb + l32, 16 * s, h), vf[s], dp);
       }
-      __syncthreads();
-      const bool need_mask = kmax > c0;   // some key of the tile lies after the chunk's first row
 #pragma unroll
-      for (int qb = 0; qb < kQChunk / 32; ++qb) {
-        f32x16 sc = f32x16{}, dp = f32x16{};
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
+        float pv = exp2_fast(fmaf(sc[r], sl2, -s_lse2[buf][qi]));
+        if (need_mask && key > s_pq[buf][qi]) pv = 0.f;
+        sc[r] = pv;
+        dp[r] = pv * (dp[r] - s_delta[buf][qi]);
+      }
+      const bf16x8 p0 = acc_to_bf16(sc, 0), p1 = acc_to_bf16(sc, 8);
+      const bf16x8 s0 = acc_to_bf16(dp, 0), s1 = acc_to_bf16(dp, 8);
 #pragma unroll
-        for (int s = 0; s < DP / 16; ++s) {
-          sc = mfma32(lds_a_nat<DP>(Qs, 32 * qb + l32, s, h), kf[s], sc);
-          dp = mfma32(lds_a_nat<DP>(Ds, 32 * qb + l32, s, h), vf[s], dp);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int qi = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-          float pv = exp2_fast(sc[r] * sl2 - s_lse2[qi]);
-          if (need_mask && key > s_pq[qi]) pv = 0.f;
-          sc[r] = pv;
-          dp[r] = pv * (dp[r] - s_delta[qi]);
-        }
-        const bf16x8 p0 = acc_to_bf16(sc, 0), p1 = acc_to_bf16(sc, 8);
-        const bf16x8 s0 = acc_to_bf16(dp, 0), s1 = acc_to_bf16(dp, 8);
-#pragma unroll
-        for (int db = 0; db < DP / 32; ++db) {
-          dva[db] = mfma32(p0, lds_a_trn<kQChunk>(Dt, 32 * db + l32, 2 * qb, h), dva[db]);
-          dva[db] = mfma32(p1, lds_a_trn<kQChunk>(Dt, 32 * db + l32, 2 * qb + 1, h), dva[db]);
-          dka[db] = mfma32(s0, lds_a_trn<kQChunk>(Qt, 32 * db + l32, 2 * qb, h), dka[db]);
-          dka[db] = mfma32(s1, lds_a_trn<kQChunk>(Qt, 32 * db + l32, 2 * qb + 1, h), dka[db]);
-        }
+      for (int db = 0; db < DP / 32; ++db) {
+        const int r0 = 32 * qb + 4 * h;
+        dva[db] = mfma32(p0, lds_tr8(Dt, QS, r0, r0 + 8, 32 * db), dva[db]);
+        dva[db] = mfma32(p1, lds_tr8(Dt, QS, r0 + 16, r0 + 24, 32 * db), dva[db]);
+        dka[db] = mfma32(s0, lds_tr8(Qt, QS, r0, r0 + 8, 32 * db), dka[db]);
+        dka[db] = mfma32(s1, lds_tr8(Qt, QS, r0 + 16, r0 + 24, 32 * db), dka[db]);
       }
     }
+    if (i + 1 < nchunks) stage(buf ^ 1);
+    __syncthreads();
   }
 
   // dV[key][d] = C[i = key][j = d]: lane holds d = 32*db + l32 for 16 keys of its wave

@@ -33,43 +33,68 @@ __device__ inline bool load_qtile(const char* ws, const PlanLayout& lay, int idx
   return true;
 }
 
-// Stage `nrows` rows (starting at global row index row(r) of `src`, D valid
-// bf16 per row, zero beyond D or beyond nvalid) into LDS, natural layout
-// nat[r][DP + 8] and / or transposed trn[d][NR + 8].
-template <int DP, int NR, bool NAT, bool TRN, typename RowFn>
-__device__ inline void stage_rows(const uint16_t* __restrict__ src, int D, RowFn row_of, uint16_t* nat,
-                                  uint16_t* trn) {
-  constexpr int CH = DP / 8;
-  for (int c = threadIdx.x; c < NR * CH; c += blockDim.x) {
-    const int r = c / CH, ch = c - r * CH;
-    const int64_t g = row_of(r);
-    u32x4 val = {0u, 0u, 0u, 0u};
-    if (g >= 0 && ch * 8 < D) val = *reinterpret_cast<const u32x4*>(src + g * D + ch * 8);
-    if (NAT) *reinterpret_cast<u32x4*>(nat + r * (DP + 8) + ch * 8) = val;
-    if (TRN) {
-      const uint16_t* e = reinterpret_cast<const uint16_t*>(&val);
+// LDS row strides (in bf16 elements) of natural [row][DP] tiles.  kNat keeps
+// 16 consecutive rows of a 16-byte-per-lane read on distinct banks; kTr puts
+// the 4 rows that one transpose read touches on disjoint 16-bank spans.
+template <int DP> struct Lds {
+  static constexpr int kNat = DP + 8;
+  static constexpr int kTr = DP + (DP == 32 ? 0 : 32);
+};
+
+// Per-thread register staging of an [NR rows x DP] bf16 tile: NPF 16-byte
+// chunks per thread, chunk c = tid + 256*u -> row c / (DP/8), column 8*(c % (DP/8)).
+template <int DP, int NR>
+struct TileRegs {
+  static constexpr int CH = DP / 8;
+  static constexpr int NPF = (NR * CH + 255) / 256;
+  u32x4 v[NPF];
+
+  // row_of(r) -> global row index (element offset / D) or -1 for a zero row
+  template <typename RowFn>
+  __device__ inline void load(const uint16_t* __restrict__ src, int D, RowFn row_of) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) trn[(ch * 8 + i) * (NR + 8) + r] = e[i];
+    for (int u = 0; u < NPF; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int r = c / CH, ch = c - r * CH;
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (r < NR) {
+        const int64_t g = row_of(r);
+        if (g >= 0 && ch * 8 < D) x = *reinterpret_cast<const u32x4*>(src + g * D + ch * 8);
+      }
+      v[u] = x;
     }
   }
+  __device__ inline void store(uint16_t* lds, int stride) const {
+#pragma unroll
+    for (int u = 0; u < NPF; ++u) {
+      const int c = threadIdx.x + 256 * u;
+      const int r = c / CH, ch = c - r * CH;
+      if (r < NR) *reinterpret_cast<u32x4*>(lds + r * stride + ch * 8) = v[u];
+    }
+  }
+};
+
+// Operand with the contraction index along a tile's rows' contiguous dimension:
+// lane l gets X[row][k0 + 8*(l/32) .. +7] (one 16-byte LDS read).
+__device__ inline bf16x8 lds_row8(const uint16_t* tile, int stride, int row, int k0, int half) {
+  return *reinterpret_cast<const bf16x8*>(tile + row * stride + k0 + 8 * half);
 }
 
-// A operand (32 rows x 16 k) from a natural LDS tile: row 32*blk + l%32, k = 16*s + 8*(l/32).
-template <int DP>
-__device__ inline bf16x8 lds_a_nat(const uint16_t* nat, int row, int s, int half) {
-  return *reinterpret_cast<const bf16x8*>(nat + row * (DP + 8) + 16 * s + 8 * half);
-}
-
-// A operand from a transposed LDS tile trn[d][NR+8] whose contraction index
-// follows the accumulator permutation: k-step `ks` of 16 covers entries
-// 16*ks + {4h..4h+3, 8+4h..8+4h+3} (h = l/32).
-template <int NR>
-__device__ inline bf16x8 lds_a_trn(const uint16_t* trn, int drow, int ks, int half) {
-  const uint16_t* p = trn + drow * (NR + 8) + 16 * ks + 4 * half;
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(p);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(p + 8);
-  u32x4 v = {lo.x, lo.y, hi.x, hi.y};
-  return as_bf16x8(v);
+// Operand whose lane index runs along a tile's contiguous (column) dimension,
+// read from a natural [row][col] LDS tile with two gfx950 transpose reads
+// (ds_read_b64_tr_b16): lane l gets X[r0 + s][c0 + l%32] in slots s = 0..3 and
+// X[r1 + s][c0 + l%32] in slots 4..7.  Within each 16-lane group the hardware
+// hands output lane j, slot s, element j%4 of the 8 bytes addressed by lane
+// 4s + j/4, so lane i addresses row r + i/4, columns c + 4*(i%4) .. +3.
+__device__ inline bf16x8 lds_tr8(const uint16_t* tile, int stride, int r0, int r1, int c0) {
+  const int l = threadIdx.x & 63, sub = l & 15;
+  const int col = c0 + 16 * ((l >> 4) & 1) + 4 * (sub & 3);
+  typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (r0 + (sub >> 2)) * stride + col));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (r1 + (sub >> 2)) * stride + col));
+  typedef short i16x8 __attribute__((ext_vector_type(8)));
+  const i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Eight accumulator entries r0..r0+7 of a 32x32 result as a bf16 operand.

@@ -14,6 +14,7 @@ typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDCS = 0;      // DualChunkSwap
 constexpr int kContig = 1;   // NO_LOAD_BALANCE
@@ -24,7 +25,8 @@ constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual
 // ---------------------------------------------------------------------------
 // tiling constants shared by the plan and the attention kernels
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWG = 128;   // query rows (token x head pairs) per fwd / dq work-group
+constexpr int kRowsPerWave = 64;  // query rows per wave in the fwd / dq kernels (two 32-row MFMA blocks)
+constexpr int kRowsPerWG = 256;   // query rows (token x head pairs) per fwd / dq work-group (4 waves)
 constexpr int kKeysPerWG = 128;   // keys per dk/dv work-group
 constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
 constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
@@ -114,8 +116,12 @@ __device__ inline uint16_t f2bf(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// Two fp32 -> packed bf16 pair (v_cvt_pk_bf16_f32: round to nearest even).
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
 }
 
 __device__ inline f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
