@@ -47,8 +47,18 @@ def build(verbose: bool = False) -> str:
                 print(out)
     tmp = LIB + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-mcode-object-version=5", "-shared", "-fPIC", *objs, "-o", tmp])
+    _check_defined(tmp)
     os.replace(tmp, LIB)
     return LIB
+
+
+def _check_defined(path):
+    """Every kernel host stub the library references must be defined (clang's host pass can
+    drop a kernel template silently instead of reporting an error)."""
+    r = subprocess.run(["nm", "-D", path], stdout=subprocess.PIPE, text=True)
+    missing = [l.split()[-1] for l in r.stdout.splitlines() if " U " in l and "cpthd" in l]
+    if missing:
+        raise RuntimeError("kernel stubs missing from the library: " + ", ".join(missing))
 
 
 if __name__ == "__main__":

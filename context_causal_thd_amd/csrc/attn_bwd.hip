@@ -26,17 +26,28 @@
 
 namespace cpthd {
 
+#ifndef CPTHD_DQ_ROW_BLOCKS
+#define CPTHD_DQ_ROW_BLOCKS 1
+#endif
+constexpr int kDqRowBlocks = CPTHD_DQ_ROW_BLOCKS;   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
+#ifndef CPTHD_DKDV_QUERY_HALVES
+#define CPTHD_DKDV_QUERY_HALVES 1
+#endif
+constexpr int kDkdvQueryHalves = CPTHD_DKDV_QUERY_HALVES;   // 1: 4 waves; 2: 8 waves splitting each step's rows
+
 // ---------------------------------------------------------------------------
 // pass 1: delta and dQ over the query tiles
 // ---------------------------------------------------------------------------
-template <int DP>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
+template <int DP, int QB>
+__global__ __launch_bounds__(64 * (8 / QB), 1) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  constexpr int KS = Lds<DP>::kNat;
-  __shared__ __align__(16) uint16_t Ks[2][kKvStep * KS];
-  __shared__ __align__(16) uint16_t Vs[2][kKvStep * KS];
+  constexpr int NW = 8 / QB;       // waves; QB 32-row blocks each, 256 rows in all
+  using KT = LdsTile<DP, true>;    // K: read by rows (S^T operand) and transposed (K^T operand of dQ^T)
+  using VT = LdsTile<DP, false>;   // V: read by rows (dP^T operand)
+  __shared__ __align__(16) uint16_t K0[KT::ELEMS], K1[KT::ELEMS];
+  __shared__ __align__(16) uint16_t V0[VT::ELEMS], V1[VT::ELEMS];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   if (!plan_matches(hdr, prm)) {
@@ -51,19 +62,37 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     return;
   }
   float* delta = reinterpret_cast<float*>(ws + lay.delta);
+  float* lse2w = reinterpret_cast<float*>(ws + lay.lse2);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
 
-  bool row_in[2], valid[2];
-  int p_q[2];
-  int64_t qrow[2];
-  float dlt[2], lse2[2];
-  bf16x8 qf[2][DP / 16], df[2][DP / 16];
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+  const int kend = t.kv_end;
+  const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
+  TileLoader<DP, true, NW> kld;
+  TileLoader<DP, false, NW> vld;
+  {
+    auto rowoff = [&](int r) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
+    kld.init(wave, lane, D, rowoff);
+    vld.init(wave, lane, D, rowoff);
+  }
+  if (nsteps > 0) {
+    kld.issue(krs, K0, 0, wave);
+    vld.issue(vrs, V0, 0, wave);
+  }
+
+  bool row_in[QB], valid[QB];
+  int p_q[QB];
+  int64_t qrow[QB];
+  float dlt[QB], lse2[QB];
+  bf16x8 qf[QB][DP / 16], df[QB][DP / 16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int m = wave * kRowsPerWave + 32 * qb + l32;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int m = wave * 32 * QB + 32 * qb + l32;
     const int tt = m / G, g = m - tt * G;
     row_in[qb] = m < bm * G && tt < t.ntok;
     p_q[qb] = t.p0 + tt;
@@ -89,65 +118,56 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
       }
     }
     dlt[qb] = dpart + xor32(dpart);
-    if (row_in[qb] && h == 0) delta[qrow[qb]] = valid[qb] ? dlt[qb] : 0.f;
     lse2[qb] = valid[qb] ? lse[qrow[qb]] * 1.4426950408889634f : INFINITY;
+    if (row_in[qb] && h == 0) {
+      delta[qrow[qb]] = valid[qb] ? dlt[qb] : 0.f;
+      lse2w[qrow[qb]] = valid[qb] ? lse2[qb] : 0.f;
+    }
   }
 
-  f32x16 acc[2][DP / 32];
+  f32x16 acc[QB][DP / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DP / 32; ++db) acc[qb][db] = f32x16{};
 
-  const int kend = t.kv_end;
-  TileRegs<DP, kKvStep> kr, vr;
-  auto fetch = [&](int kb) {
-    auto key_row = [&](int r) -> int64_t {
-      const int kabs = kb + r;
-      return kabs < kend ? (int64_t)kabs * Hkv + kvh : -1;
-    };
-    kr.load(k, D, key_row);
-    vr.load(v, D, key_row);
-  };
-  const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
-  if (nsteps > 0) {
-    fetch(t.ds);
-    kr.store(Ks[0], KS);
-    vr.store(Vs[0], KS);
-  }
-  __syncthreads();
+  lds_loads_barrier();
 
   const float sl2 = prm.scale_log2;
-  for (int it = 0; it < nsteps; ++it) {
+  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
     const int kb = t.ds + it * kKvStep;
-    const int buf = it & 1;
-    if (it + 1 < nsteps) fetch(kb + kKvStep);
-    const uint16_t* Kt = Ks[buf];
-    const uint16_t* Vt = Vs[buf];
+    if (it + 1 < nsteps) {
+      const uint32_t soff = (uint32_t)(it + 1) * kKvStep * row_bytes;
+      kld.issue(krs, Kn, soff, wave);
+      vld.issue(vrs, Vn, soff, wave);
+    }
     const bool need_mask = kb + kKvStep - 1 > t.p0;
-
-    bf16x8 dsb[2][4];
+    bf16x8 dsb[QB][4];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      f32x16 sc[2] = {f32x16{}, f32x16{}}, dp[2] = {f32x16{}, f32x16{}};
+      f32x16 sc[QB], dp[QB];
 #pragma unroll
-      for (int s = 0; s < DP / 16; ++s) {
-        const bf16x8 ka = lds_row8(Kt, KS, 32 * b + l32, 16 * s, h);
-        const bf16x8 va = lds_row8(Vt, KS, 32 * b + l32, 16 * s, h);
-        sc[0] = mfma32(ka, qf[0][s], sc[0]);
-        sc[1] = mfma32(ka, qf[1][s], sc[1]);
-        dp[0] = mfma32(va, df[0][s], dp[0]);
-        dp[1] = mfma32(va, df[1][s], dp[1]);
+      for (int qb = 0; qb < QB; ++qb) {
+        sc[qb] = f32x16{};
+        dp[qb] = f32x16{};
       }
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int s = 0; s < DP / 16; ++s) {
+        const bf16x8 ka = lds_row8<DP, true>(Kt, 32 * b + l32, 16 * s, h);
+        const bf16x8 va = lds_row8<DP, false>(Vt, 32 * b + l32, 16 * s, h);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          sc[qb] = mfma32(ka, qf[qb][s], sc[qb]);
+          dp[qb] = mfma32(va, df[qb][s], dp[qb]);
+        }
+      }
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const int lim = p_q[qb] - kb - 32 * b - 4 * h;   // key offset 8(r/4) + r%4 allowed iff <= lim
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           float pv = exp2_fast(fmaf(sc[qb][r], sl2, -lse2[qb]));
-          if (need_mask) {
-            const int key = kb + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > p_q[qb]) pv = 0.f;
-          }
+          if (need_mask && 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
           sc[qb][r] = pv * (dp[qb][r] - dlt[qb]);
         }
         dsb[qb][2 * b] = acc_to_bf16(sc[qb], 0);
@@ -158,20 +178,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
     for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = lds_tr8(Kt, KS, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
-        acc[0][db] = mfma32(a, dsb[0][ks], acc[0][db]);
-        acc[1][db] = mfma32(a, dsb[1][ks], acc[1][db]);
+        const bf16x8 a = lds_tr8<DP, true>(Kt, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, dsb[qb][ks], acc[qb][db]);
       }
-
-    if (it + 1 < nsteps) {
-      kr.store(Ks[buf ^ 1], KS);
-      vr.store(Vs[buf ^ 1], KS);
-    }
-    __syncthreads();
+    lds_loads_barrier();
+  };
+  for (int it = 0; it < nsteps; it += 2) {
+    step(it, K0, V0, K1, V1);
+    if (it + 1 < nsteps) step(it + 1, K1, V1, K0, V0);
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     if (!row_in[qb]) continue;
     const float sc = valid[qb] ? prm.scale : 0.f;
 #pragma unroll
@@ -191,16 +210,32 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(
 // ---------------------------------------------------------------------------
 // pass 2: dK and dV over the key tiles
 // ---------------------------------------------------------------------------
-template <int DP>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
+// Direct loads of one step's Q and dO rows (local rows from `base` / Hq, ntok
+// tokens) and of their LSE*log2(e) and delta values into the given buffers.
+template <int DP, int NW>
+__device__ inline void issue_q_chunk(const TileLoader<DP, true, NW>& qld, const uint16_t* q, const uint16_t* dout,
+                                     const float* lse2w, const float* delta, int64_t base, int ntok,
+                                     uint32_t tok_bytes, int Hq, int D, uint32_t ld_off, int wave, uint16_t* Qn,
+                                     uint16_t* On, float* Ln, float* En) {
+  const uint32_t nrec = (uint32_t)ntok * tok_bytes;
+  qld.issue(make_rsrc(q + base * D, nrec), Qn, 0, wave);
+  qld.issue(make_rsrc(dout + base * D, nrec), On, 0, wave);
+  if (wave == 0) lds_load_dword(make_rsrc(lse2w + base, (uint32_t)ntok * Hq * 4), Ln, ld_off);
+  if (wave == 1) lds_load_dword(make_rsrc(delta + base, (uint32_t)ntok * Hq * 4), En, ld_off);
+}
+
+template <int DP, int NQH>
+__global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ dk,
     float* __restrict__ dv, const char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  constexpr int QS = Lds<DP>::kNat;
-  __shared__ __align__(16) uint16_t Qs[2][kQChunk * QS];
-  __shared__ __align__(16) uint16_t Ds[2][kQChunk * QS];
-  __shared__ float s_lse2[2][kQChunk], s_delta[2][kQChunk];
-  __shared__ int s_pq[2][kQChunk];
+  // 4 * NQH waves: wave w owns keys k0 + 32*(w%4) .. +31 and, with NQH = 2, only
+  // query block w/4 of every 64-row step (the two halves' dK/dV are summed at the end)
+  constexpr int NW = 4 * NQH;
+  using QT = LdsTile<DP, true>;   // Q and dO: read by rows (S, dP operands) and transposed (dK, dV operands)
+  __shared__ __align__(16) uint16_t Q0[QT::ELEMS], Q1[QT::ELEMS];
+  __shared__ __align__(16) uint16_t O0[QT::ELEMS], O1[QT::ELEMS];
+  __shared__ __align__(16) float L0[kQChunk], L1[kQChunk], E0[kQChunk], E1[kQChunk];   // LSE*log2(e), delta
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   if (!plan_matches(hdr, prm)) {
@@ -217,12 +252,53 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
   }
   const DocSeg ds = reinterpret_cast<const DocSeg*>(ws + lay.docs)[kt.doc];
   const float* delta = reinterpret_cast<const float*>(ws + lay.delta);
+  const float* lse2w = reinterpret_cast<const float*>(ws + lay.lse2);
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv, S = prm.S;
-  const int key = kt.k0 + wave * 32 + l32;          // this lane's key (B operand column)
-  const bool key_in = wave * 32 + l32 < kt.nkeys;
+  const int kw = wave & 3, qh = wave >> 2;
+  const int key = kt.k0 + kw * 32 + l32;            // this lane's key (B operand column)
+  const bool key_in = kw * 32 + l32 < kt.nkeys;
   const int64_t krow = (int64_t)key * Hkv + kvh;
+
+  // the rank's rows of the document that see the tile: suffixes (token >= k0)
+  // of the document's segments, cut into steps of tpc tokens
+  const int tpc = kQChunk / G;
+  int plo[2], phi[2], sl[2], sp[2], nch[2];
+#pragma unroll
+  for (int si = 0; si < 2; ++si) {
+    sp[si] = si == 0 ? ds.pa : ds.pb;
+    const int sn = si == 0 ? ds.na : ds.nb;
+    sl[si] = si == 0 ? ds.la : ds.lb;
+    plo[si] = max(sp[si], kt.k0);
+    phi[si] = min(sp[si] + sn, ds.ve);
+    nch[si] = (phi[si] > plo[si] && sl[si] >= 0 && sl[si] + (phi[si] - sp[si]) <= S)
+                  ? (phi[si] - plo[si] + tpc - 1) / tpc : 0;
+  }
+  const int nchunks = nch[0] + nch[1];
+  // chunk i: first token c0 and first local row l0
+  auto chunk_at = [&](int i, int& c0, int& l0, int& ntok) {
+    const int si = i < nch[0] ? 0 : 1;
+    c0 = plo[si] + (i - (si ? nch[0] : 0)) * tpc;
+    l0 = sl[si] + (c0 - sp[si]);
+    ntok = min(tpc, phi[si] - c0);
+  };
+
+  // Q / dO rows of a chunk: tile row r = token r/G, head r%G; LSE / delta: one float per row
+  const uint32_t tok_bytes = (uint32_t)Hq * D * 2;
+  TileLoader<DP, true, NW> qld;
+  qld.init(wave, lane, D, [&](int r) -> int64_t {
+    const int t2 = r / G;
+    return r < tpc * G ? (int64_t)t2 * tok_bytes + (int64_t)(kvh * G + r - t2 * G) * D * 2 : -1;
+  });
+  const uint32_t ld_off = lane < tpc * G ? (uint32_t)((lane / G) * Hq + kvh * G + lane % G) * 4u : 0x80000000u;
+  auto issue = [&](int i, uint16_t* Qn, uint16_t* On, float* Ln, float* En) {
+    int c0, l0, ntok;
+    chunk_at(i, c0, l0, ntok);
+    issue_q_chunk<DP, NW>(qld, q, dout, lse2w, delta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn, On, Ln,
+                      En);
+  };
+  if (nchunks > 0) issue(0, Q0, O0, L0, E0);
 
   bf16x8 kf[DP / 16], vf[DP / 16];
 #pragma unroll
@@ -242,102 +318,93 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     dka[db] = f32x16{};
     dva[db] = f32x16{};
   }
-
-  // the rank's rows of the document that see the tile: suffixes (token >= k0)
-  // of the document's segments, cut into steps of tpc tokens
-  const int tpc = kQChunk / G;
-  int plo[2], phi[2], sl[2], sp[2], nch[2];
-#pragma unroll
-  for (int si = 0; si < 2; ++si) {
-    sp[si] = si == 0 ? ds.pa : ds.pb;
-    const int sn = si == 0 ? ds.na : ds.nb;
-    sl[si] = si == 0 ? ds.la : ds.lb;
-    plo[si] = max(sp[si], kt.k0);
-    phi[si] = min(sp[si] + sn, ds.ve);
-    nch[si] = (phi[si] > plo[si] && sl[si] >= 0 && sl[si] + (phi[si] - sp[si]) <= S)
-                  ? (phi[si] - plo[si] + tpc - 1) / tpc : 0;
-  }
-  const int nchunks = nch[0] + nch[1];
-  auto chunk_c0 = [&](int i, int& si) {
-    si = i < nch[0] ? 0 : 1;
-    return plo[si] + (i - (si ? nch[0] : 0)) * tpc;
-  };
-
-  TileRegs<DP, kQChunk> qr, dr;
-  float pf_lse = INFINITY, pf_delta = 0.f;
-  int pf_pq = -1;
-  auto fetch = [&](int i) {
-    int si;
-    const int c0 = chunk_c0(i, si);
-    const int ntok = min(tpc, phi[si] - c0);
-    const int l0 = sl[si] + (c0 - sp[si]);
-    auto qrow_of = [&](int r) -> int64_t {
-      const int t2 = r / G;
-      return (r < tpc * G && t2 < ntok) ? (int64_t)(l0 + t2) * Hq + kvh * G + (r - t2 * G) : -1;
-    };
-    qr.load(q, D, qrow_of);
-    dr.load(dout, D, qrow_of);
-    if (tid < kQChunk) {
-      const int64_t qrw = qrow_of(tid);
-      pf_lse = qrw >= 0 ? lse[qrw] * 1.4426950408889634f : INFINITY;
-      pf_delta = qrw >= 0 ? delta[qrw] : 0.f;
-      pf_pq = qrw >= 0 ? c0 + tid / G : -1;
-    }
-  };
-  auto stage = [&](int buf) {
-    qr.store(Qs[buf], QS);
-    dr.store(Ds[buf], QS);
-    if (tid < kQChunk) {
-      s_lse2[buf][tid] = pf_lse;
-      s_delta[buf][tid] = pf_delta;
-      s_pq[buf][tid] = pf_pq;
-    }
-  };
-  if (nchunks > 0) {
-    fetch(0);
-    stage(0);
-  }
-  __syncthreads();
+  lds_loads_barrier();
 
   const float sl2 = prm.scale_log2;
   const int kmax = kt.k0 + kt.nkeys - 1;
-  for (int i = 0; i < nchunks; ++i) {
-    const int buf = i & 1;
-    int si;
-    const int c0 = chunk_c0(i, si);
-    if (i + 1 < nchunks) fetch(i + 1);
-    const bool need_mask = kmax > c0;   // some key of the tile lies after the step's first row
-    const uint16_t* Qt = Qs[buf];
-    const uint16_t* Dt = Ds[buf];
-#pragma unroll
-    for (int qb = 0; qb < kQChunk / 32; ++qb) {
+  auto step = [&](int i, const uint16_t* Qt, const uint16_t* Dt, const float* Lt, const float* Et, uint16_t* Qn,
+                  uint16_t* On, float* Ln, float* En) {
+    int c0, l0, ntok;
+    chunk_at(i, c0, l0, ntok);
+    if (i + 1 < nchunks) issue(i + 1, Qn, On, Ln, En);
+    // row qi (token c0 + qi/G) sees this lane's key iff qi >= (key - c0) * G
+    const bool need_mask = kmax > c0;
+    const int thr = (key - c0) * G - 4 * h;
+    auto block = [&](int qb) {
       f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
-        sc = mfma32(lds_row8(Qt, QS, 32 * qb + l32, 16 * s, h), kf[s], sc);
-        dp = mfma32(lds_row8(Dt, QS, 32 * qb + l32, 16 * s, h), vf[s], dp);
+        sc = mfma32(lds_row8<DP, true>(Qt, 32 * qb + l32, 16 * s, h), kf[s], sc);
+        dp = mfma32(lds_row8<DP, true>(Dt, 32 * qb + l32, 16 * s, h), vf[s], dp);
       }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = 32 * qb + 8 * (r >> 2) + 4 * h + (r & 3);
-        float pv = exp2_fast(fmaf(sc[r], sl2, -s_lse2[buf][qi]));
-        if (need_mask && key > s_pq[buf][qi]) pv = 0.f;
-        sc[r] = pv;
-        dp[r] = pv * (dp[r] - s_delta[buf][qi]);
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int q4 = 32 * qb + 8 * g4 + 4 * h;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + q4);
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(Et + q4);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = 4 * g4 + j;
+          float pv = exp2_fast(fmaf(sc[r], sl2, -l4[j]));
+          if (need_mask && 32 * qb + 8 * g4 + j < thr) pv = 0.f;
+          sc[r] = pv;
+          dp[r] = pv * (dp[r] - e4[j]);
+        }
       }
       const bf16x8 p0 = acc_to_bf16(sc, 0), p1 = acc_to_bf16(sc, 8);
       const bf16x8 s0 = acc_to_bf16(dp, 0), s1 = acc_to_bf16(dp, 8);
 #pragma unroll
       for (int db = 0; db < DP / 32; ++db) {
         const int r0 = 32 * qb + 4 * h;
-        dva[db] = mfma32(p0, lds_tr8(Dt, QS, r0, r0 + 8, 32 * db), dva[db]);
-        dva[db] = mfma32(p1, lds_tr8(Dt, QS, r0 + 16, r0 + 24, 32 * db), dva[db]);
-        dka[db] = mfma32(s0, lds_tr8(Qt, QS, r0, r0 + 8, 32 * db), dka[db]);
-        dka[db] = mfma32(s1, lds_tr8(Qt, QS, r0 + 16, r0 + 24, 32 * db), dka[db]);
+        dva[db] = mfma32(p0, lds_tr8<DP, true>(Dt, r0, r0 + 8, 32 * db), dva[db]);
+        dva[db] = mfma32(p1, lds_tr8<DP, true>(Dt, r0 + 16, r0 + 24, 32 * db), dva[db]);
+        dka[db] = mfma32(s0, lds_tr8<DP, true>(Qt, r0, r0 + 8, 32 * db), dka[db]);
+        dka[db] = mfma32(s1, lds_tr8<DP, true>(Qt, r0 + 16, r0 + 24, 32 * db), dka[db]);
       }
+    };
+    if (NQH == 1) {
+      block(0);
+      block(1);
+    } else {
+      block(qh);
     }
-    if (i + 1 < nchunks) stage(buf ^ 1);
-    __syncthreads();
+    lds_loads_barrier();
+  };
+  for (int i = 0; i < nchunks; i += 2) {
+    step(i, Q0, O0, L0, E0, Q1, O1, L1, E1);
+    if (i + 1 < nchunks) step(i + 1, Q1, O1, L1, E1, Q0, O0, L0, E0);
+  }
+
+  if (NQH == 2) {
+    // sum the two query halves: waves 4..7 hand their partial sums to waves 0..3 through LDS,
+    // JR of each lane's 16 accumulator values per round (the scratch is the Q0 tile)
+    constexpr int JR = QT::ELEMS * 2 >= 4 * 64 * 16 * 4 ? 16 : (QT::ELEMS * 2 >= 4 * 64 * 8 * 4 ? 8 : 4);
+    float* red = reinterpret_cast<float*>(Q0);
+#pragma unroll
+    for (int tsr = 0; tsr < 2; ++tsr)
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+        for (int j0 = 0; j0 < 16; j0 += JR) {
+          f32x16& a = tsr ? dva[db] : dka[db];
+          if (qh == 1)
+#pragma unroll
+            for (int j = 0; j < JR; j += 4)
+              *reinterpret_cast<f32x4*>(red + ((kw * (JR / 4) + j / 4) * 64 + lane) * 4) =
+                  f32x4{a[j0 + j], a[j0 + j + 1], a[j0 + j + 2], a[j0 + j + 3]};
+          __syncthreads();
+          if (qh == 0)
+#pragma unroll
+            for (int j = 0; j < JR; j += 4) {
+              const f32x4 b = *reinterpret_cast<const f32x4*>(red + ((kw * (JR / 4) + j / 4) * 64 + lane) * 4);
+              a[j0 + j] += b[0];
+              a[j0 + j + 1] += b[1];
+              a[j0 + j + 2] += b[2];
+              a[j0 + j + 3] += b[3];
+            }
+          __syncthreads();
+        }
+    if (qh == 1) return;
   }
 
   // dV[key][d] = C[i = key][j = d]: lane holds d = 32*db + l32 for 16 keys of its wave
@@ -347,7 +414,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkdv_kernel(
     if (d >= D) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int kl = wave * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      const int kl = kw * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (kl < kt.nkeys) {
         const int64_t row = (int64_t)(kt.k0 + kl) * Hkv + kvh;
         dv[row * D + d] = dva[db][r];
@@ -362,11 +429,15 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const float* lse, float* dq, float* dk, float* dv, char* ws, const PlanLayout& lay,
                       const AttnParams& prm, int32_t* status, unsigned grid_q, unsigned grid_kv,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
-  int e = launch(attn_bwd_dq_kernel<DP>, dim3(grid_q), dim3(256), 0, stream, ev, nev, 0, (const uint16_t*)q,
+  constexpr int QB = kDqRowBlocks;
+  int e = launch(attn_bwd_dq_kernel<DP, QB>, dim3(grid_q), dim3(64 * (8 / QB)), 0, stream, ev, nev, 0,
+                 (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse, dq, ws,
                  lay, prm, status);
   if (e) return e;
-  return launch(attn_bwd_dkdv_kernel<DP>, dim3(grid_kv), dim3(256), 0, stream, ev, nev, 1, (const uint16_t*)q,
+  constexpr int NQH = kDkdvQueryHalves;
+  return launch(attn_bwd_dkdv_kernel<DP, NQH>, dim3(grid_kv), dim3(256 * NQH), 0, stream, ev, nev, 1,
+                (const uint16_t*)q,
                 (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, dk, dv, (const char*)ws, lay,
                 prm, status);
 }

@@ -33,65 +33,104 @@ __device__ inline bool load_qtile(const char* ws, const PlanLayout& lay, int idx
   return true;
 }
 
-// LDS row strides (in bf16 elements) of natural [row][DP] tiles.  kNat keeps
-// 16 consecutive rows of a 16-byte-per-lane read on distinct banks; kTr puts
-// the 4 rows that one transpose read touches on disjoint 16-bank spans.
-template <int DP> struct Lds {
-  static constexpr int kNat = DP + 8;
-  static constexpr int kTr = DP + (DP == 32 ? 0 : 32);
+// ---------------------------------------------------------------------------
+// LDS tiles of 64 rows x DP bf16, staged straight from global memory
+// ---------------------------------------------------------------------------
+// Rows are DP + 8 elements apart (one 16-byte padding slot per row): 16
+// consecutive rows of a 16-byte-per-lane read then fall on distinct banks.
+// Tiles that are also read through the transpose read store logical row q at
+// row rho(q) (a 4x4 transpose inside each block of 16 rows), so the 4 logical
+// rows one transpose read touches sit 4 rows apart, on disjoint bank spans.
+__device__ inline int rho(int q) { return (q & ~15) | ((q & 3) << 2) | ((q >> 2) & 3); }
+
+template <int DP, bool PERM>
+struct LdsTile {
+  static constexpr int C = DP / 8;                 // 16-byte chunks of data per row
+  static constexpr int SPR = C + 1;                // 16-byte slots per row
+  static constexpr int STRIDE = DP + 8;            // elements per row
+  static constexpr int ELEMS = 64 * STRIDE;
+  static constexpr int NLOAD = SPR;                // 1 KiB wave loads per tile (64 * SPR slots)
+  __device__ static inline int row(int q) { return PERM ? rho(q) : q; }
 };
 
-// Per-thread register staging of an [NR rows x DP] bf16 tile: NPF 16-byte
-// chunks per thread, chunk c = tid + 256*u -> row c / (DP/8), column 8*(c % (DP/8)).
-template <int DP, int NR>
-struct TileRegs {
-  static constexpr int CH = DP / 8;
-  static constexpr int NPF = (NR * CH + 255) / 256;
-  u32x4 v[NPF];
+// Per-lane offsets of one work-group's direct loads of an LdsTile: of NW
+// waves, wave w issues loads u = w, w + NW, ...; lane l of load u fills 16-byte
+// slot 64u + l.  Padding slots, columns >= D and rows without data get an
+// offset past the buffer's range, which the hardware turns into zeros.
+template <int DP, bool PERM, int NW = 4>
+struct TileLoader {
+  using L = LdsTile<DP, PERM>;
+  static constexpr int NLW = (L::NLOAD + NW - 1) / NW;   // loads per wave
+  uint32_t voff[NLW];
 
-  // row_of(r) -> global row index (element offset / D) or -1 for a zero row
-  template <typename RowFn>
-  __device__ inline void load(const uint16_t* __restrict__ src, int D, RowFn row_of) {
+  // rowoff(q): byte offset of logical row q from the descriptor base, or < 0 for a zero row
+  template <typename RowOff>
+  __device__ inline void init(int wave, int lane, int D, RowOff rowoff) {
 #pragma unroll
-    for (int u = 0; u < NPF; ++u) {
-      const int c = threadIdx.x + 256 * u;
-      const int r = c / CH, ch = c - r * CH;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (r < NR) {
-        const int64_t g = row_of(r);
-        if (g >= 0 && ch * 8 < D) x = *reinterpret_cast<const u32x4*>(src + g * D + ch * 8);
+    for (int i = 0; i < NLW; ++i) {
+      const int u = wave + NW * i;
+      const int slot = 64 * u + lane;
+      const int R = slot / L::SPR, ch = slot - R * L::SPR;
+      uint32_t off = 0x80000000u;
+      if (u < L::NLOAD && ch < L::C && ch * 8 < D) {
+        const int64_t ro = rowoff(PERM ? rho(R) : R);
+        if (ro >= 0) off = (uint32_t)(ro + 16 * ch);
       }
-      v[u] = x;
+      voff[i] = off;
     }
   }
-  __device__ inline void store(uint16_t* lds, int stride) const {
+  __device__ inline void issue(__amdgpu_buffer_rsrc_t rsrc, uint16_t* tile, uint32_t soff, int wave) const {
 #pragma unroll
-    for (int u = 0; u < NPF; ++u) {
-      const int c = threadIdx.x + 256 * u;
-      const int r = c / CH, ch = c - r * CH;
-      if (r < NR) *reinterpret_cast<u32x4*>(lds + r * stride + ch * 8) = v[u];
+    for (int i = 0; i < NLW; ++i) {
+      const int u = wave + NW * i;
+      if (u < L::NLOAD)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + 512 * u), 16,
+                                                 voff[i], soff, 0, 0);
     }
   }
 };
 
-// Operand with the contraction index along a tile's rows' contiguous dimension:
-// lane l gets X[row][k0 + 8*(l/32) .. +7] (one 16-byte LDS read).
-__device__ inline bf16x8 lds_row8(const uint16_t* tile, int stride, int row, int k0, int half) {
-  return *reinterpret_cast<const bf16x8*>(tile + row * stride + k0 + 8 * half);
+// Buffer descriptor over `bytes` bytes from `base` (raw, no stride); loads past
+// the range read as zero.
+__device__ inline __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// Operand whose lane index runs along a tile's contiguous (column) dimension,
-// read from a natural [row][col] LDS tile with two gfx950 transpose reads
-// (ds_read_b64_tr_b16): lane l gets X[r0 + s][c0 + l%32] in slots s = 0..3 and
-// X[r1 + s][c0 + l%32] in slots 4..7.  Within each 16-lane group the hardware
-// hands output lane j, slot s, element j%4 of the 8 bytes addressed by lane
-// 4s + j/4, so lane i addresses row r + i/4, columns c + 4*(i%4) .. +3.
-__device__ inline bf16x8 lds_tr8(const uint16_t* tile, int stride, int r0, int r1, int c0) {
+// One 4-byte direct load per lane into LDS[base + 4*lane].
+__device__ inline void lds_load_dword(__amdgpu_buffer_rsrc_t rsrc, void* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 4, voff, 0, 0, 0);
+}
+
+// Wait for this wave's direct-to-LDS loads, then for the whole work-group.
+__device__ inline void lds_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// Operand with the contraction index along a row: lane l gets
+// X[q][k0 + 8*(l/32) .. +7] of logical row q (one 16-byte LDS read).
+template <int DP, bool PERM>
+__device__ inline bf16x8 lds_row8(const uint16_t* tile, int q, int k0, int half) {
+  using L = LdsTile<DP, PERM>;
+  return *reinterpret_cast<const bf16x8*>(tile + L::row(q) * L::STRIDE + k0 + 8 * half);
+}
+
+// Operand whose lane index runs along the columns, with two gfx950 transpose
+// reads (ds_read_b64_tr_b16): lane l gets X[q0 + s][c0 + l%32] in slots
+// s = 0..3 and X[q1 + s][c0 + l%32] in slots 4..7 (q0, q1 multiples of 4).
+// Within each 16-lane group the hardware hands output lane j, slot s, element
+// j%4 of the 8 bytes addressed by lane 4s + j/4, so lane i addresses logical
+// row q + i/4, columns c + 4*(i%4) .. +3.
+template <int DP, bool PERM>
+__device__ inline bf16x8 lds_tr8(const uint16_t* tile, int q0, int q1, int c0) {
+  using L = LdsTile<DP, PERM>;
   const int l = threadIdx.x & 63, sub = l & 15;
   const int col = c0 + 16 * ((l >> 4) & 1) + 4 * (sub & 3);
   typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (r0 + (sub >> 2)) * stride + col));
-  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(tile + (r1 + (sub >> 2)) * stride + col));
+  const i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + L::row(q0 + (sub >> 2)) * L::STRIDE + col));
+  const i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_i16x4*)(tile + L::row(q1 + (sub >> 2)) * L::STRIDE + col));
   typedef short i16x8 __attribute__((ext_vector_type(8)));
   const i16x8 v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8, v);

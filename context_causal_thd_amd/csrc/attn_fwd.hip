@@ -27,16 +27,25 @@
 namespace cpthd {
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
+#ifndef CPTHD_FWD_ROW_BLOCKS
+#define CPTHD_FWD_ROW_BLOCKS 1
+#endif
+constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
 
-template <int DP>
-__global__ __launch_bounds__(256, 1) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+template <int DP, int QB>
+__global__ __launch_bounds__(64 * (8 / QB), 1) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                                           float* __restrict__ lse, const char* __restrict__ ws,
                                                           PlanLayout lay, AttnParams prm, int32_t* status) {
-  constexpr int KS = Lds<DP>::kNat, VS = Lds<DP>::kTr;
-  __shared__ __align__(16) uint16_t Ks[2][kKvStep * KS];
-  __shared__ __align__(16) uint16_t Vs[2][kKvStep * VS];
+  constexpr int NW = 8 / QB;       // waves; QB 32-row blocks each, 256 rows in all
+  using KT = LdsTile<DP, false>;   // K: read by rows (S^T operand)
+  using VT = LdsTile<DP, true>;    // V: read through the transpose read (V^T operand)
+  // two separate buffers per tensor (not one 2-D array): with the step loop
+  // unrolled by two, every LDS access names its buffer statically, so the
+  // in-flight direct loads into the other buffer need no wait before it
+  __shared__ __align__(16) uint16_t K0[KT::ELEMS], K1[KT::ELEMS];
+  __shared__ __align__(16) uint16_t V0[VT::ELEMS], V1[VT::ELEMS];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   if (!plan_matches(hdr, prm)) {
@@ -55,14 +64,32 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(const uint16_t* __rest
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
 
-  // the lane's query row in each of the wave's two 32-row blocks
-  bool row_in[2], valid[2];
-  int p_q[2];
-  int64_t qrow[2];
-  bf16x8 qf[2][DP / 16];
+  // K/V rows [ds, kv_end) of kv head kvh; rows past kv_end read as zero
+  const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
+  const int kend = t.kv_end;
+  const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
+  TileLoader<DP, false, NW> kld;
+  TileLoader<DP, true, NW> vld;
+  {
+    auto rowoff = [&](int r) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
+    kld.init(wave, lane, D, rowoff);
+    vld.init(wave, lane, D, rowoff);
+  }
+  if (nsteps > 0) {
+    kld.issue(krs, K0, 0, wave);
+    vld.issue(vrs, V0, 0, wave);
+  }
+
+  // the lane's query row in each of the wave's 32-row blocks
+  bool row_in[QB], valid[QB];
+  int p_q[QB];
+  int64_t qrow[QB];
+  bf16x8 qf[QB][DP / 16];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int m = wave * kRowsPerWave + 32 * qb + l32;
+  for (int qb = 0; qb < QB; ++qb) {
+    const int m = wave * 32 * QB + 32 * qb + l32;
     const int tt = m / G, g = m - tt * G;
     row_in[qb] = m < bm * G && tt < t.ntok;
     p_q[qb] = t.p0 + tt;
@@ -77,70 +104,60 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(const uint16_t* __rest
     }
   }
 
-  float m_i[2] = {-INFINITY, -INFINITY}, l_i[2] = {0.f, 0.f};
-  f32x16 acc[2][DP / 32];
+  float m_i[QB], l_i[QB];
+  f32x16 acc[QB][DP / 32];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
+    m_i[qb] = -INFINITY;
+    l_i[qb] = 0.f;
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int db = 0; db < DP / 32; ++db) acc[qb][db] = f32x16{};
 
-  const int kend = t.kv_end;
-  TileRegs<DP, kKvStep> kr, vr;
-  auto fetch = [&](int kb) {
-    auto key_row = [&](int r) -> int64_t {
-      const int kabs = kb + r;
-      return kabs < kend ? (int64_t)kabs * Hkv + kvh : -1;
-    };
-    kr.load(k, D, key_row);
-    vr.load(v, D, key_row);
-  };
-
-  const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
-  if (nsteps > 0) {
-    fetch(t.ds);
-    kr.store(Ks[0], KS);
-    vr.store(Vs[0], VS);
-  }
-  __syncthreads();
+  lds_loads_barrier();
 
   const float sl2 = prm.scale_log2;
-  for (int it = 0; it < nsteps; ++it) {
+  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
     const int kb = t.ds + it * kKvStep;
-    const int buf = it & 1;
-    if (it + 1 < nsteps) fetch(kb + kKvStep);
-    const uint16_t* Kt = Ks[buf];
-    const uint16_t* Vt = Vs[buf];
+    if (it + 1 < nsteps) {
+      const uint32_t soff = (uint32_t)(it + 1) * kKvStep * row_bytes;
+      kld.issue(krs, Kn, soff, wave);
+      vld.issue(vrs, Vn, soff, wave);
+    }
 
-    f32x16 sc[2][2];
+    f32x16 sc[QB][2];
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      sc[0][b] = f32x16{};
-      sc[1][b] = f32x16{};
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb][b] = f32x16{};
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
-        const bf16x8 a = lds_row8(Kt, KS, 32 * b + l32, 16 * s, h);
-        sc[0][b] = mfma32(a, qf[0][s], sc[0][b]);
-        sc[1][b] = mfma32(a, qf[1][s], sc[1][b]);
+        const bf16x8 a = lds_row8<DP, false>(Kt, 32 * b + l32, 16 * s, h);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) sc[qb][b] = mfma32(a, qf[qb][s], sc[qb][b]);
       }
     }
 
     const bool need_mask = kb + kKvStep - 1 > t.p0;
-    bf16x8 pb[2][4];
+    bf16x8 pb[QB][4];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
+    for (int qb = 0; qb < QB; ++qb) {
+      if (need_mask) {
+        // key kb + 32b + 8(r/4) + 4h + r%4 is allowed iff it is <= the row's token
+        const int lim = p_q[qb] - kb - 4 * h;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (32 * b + 8 * (r >> 2) + (r & 3) > lim) sc[qb][b][r] = -INFINITY;
+      }
       float mx = -INFINITY;
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float x = sc[qb][b][r];
-          if (need_mask) {
-            const int key = kb + 32 * b + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (key > p_q[qb]) x = -INFINITY;
-          }
-          sc[qb][b][r] = x;
-          mx = fmaxf(mx, x);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][b][r]);
       mx = fmaxf(mx, xor32(mx)) * sl2;
       if (__any(mx > m_i[qb] + kRescaleThreshold)) {
         const float m_new = fmaxf(m_i[qb], mx);
@@ -169,20 +186,20 @@ __global__ __launch_bounds__(256, 1) void attn_fwd_kernel(const uint16_t* __rest
     for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = lds_tr8(Vt, VS, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
-        acc[0][db] = mfma32(a, pb[0][ks], acc[0][db]);
-        acc[1][db] = mfma32(a, pb[1][ks], acc[1][db]);
+        const bf16x8 a = lds_tr8<DP, true>(Vt, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][ks], acc[qb][db]);
       }
 
-    if (it + 1 < nsteps) {
-      kr.store(Ks[buf ^ 1], KS);
-      vr.store(Vs[buf ^ 1], VS);
-    }
-    __syncthreads();
+    lds_loads_barrier();
+  };
+  for (int it = 0; it < nsteps; it += 2) {
+    step(it, K0, V0, K1, V1);
+    if (it + 1 < nsteps) step(it + 1, K1, V1, K0, V0);
   }
 
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float l_tot = l_i[qb] + xor32(l_i[qb]);
     if (!row_in[qb]) continue;
     const float inv = (valid[qb] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
@@ -207,8 +224,9 @@ template <int DP>
 static int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const char* ws,
                       const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
-  return launch(attn_fwd_kernel<DP>, dim3(grid), dim3(256), 0, stream, ev, nev, 0, (const uint16_t*)q,
-                (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+  constexpr int QB = kFwdRowBlocks;
+  return launch(attn_fwd_kernel<DP, QB>, dim3(grid), dim3(64 * (8 / QB)), 0, stream, ev, nev, 0,
+                (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
 }
 
 int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32_t strategy, int32_t num_docs,

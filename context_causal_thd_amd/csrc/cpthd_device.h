@@ -25,8 +25,7 @@ constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual
 // ---------------------------------------------------------------------------
 // tiling constants shared by the plan and the attention kernels
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWave = 64;  // query rows per wave in the fwd / dq kernels (two 32-row MFMA blocks)
-constexpr int kRowsPerWG = 256;   // query rows (token x head pairs) per fwd / dq work-group (4 waves)
+constexpr int kRowsPerWG = 256;   // query rows (token x head pairs) per fwd / dq work-group
 constexpr int kKeysPerWG = 128;   // keys per dk/dv work-group
 constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
 constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
@@ -74,7 +73,7 @@ static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
 
 // Workspace layout (byte offsets), identical on host and device.
 struct PlanLayout {
-  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, delta, total;
+  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, delta, lse2, total;
   int64_t max_qtiles, max_kvtiles, max_docs;
 };
 
@@ -97,6 +96,7 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int 
   L.kvtiles_tmp = off;  off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
   L.docs = off;         off = align_up(off + (size_t)max_docs * sizeof(DocSeg), 256);
   L.delta = off;        off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
+  L.lse2 = off;         off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
   L.total = off;
   return L;
 }
