@@ -30,10 +30,10 @@ namespace cpthd {
 #define CPTHD_DQ_ROW_BLOCKS 1
 #endif
 constexpr int kDqRowBlocks = CPTHD_DQ_ROW_BLOCKS;   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
-#ifndef CPTHD_DKDV_QUERY_HALVES
-#define CPTHD_DKDV_QUERY_HALVES 1
+#ifndef CPTHD_DKDV_SPLIT
+#define CPTHD_DKDV_SPLIT 2
 #endif
-constexpr int kDkdvQueryHalves = CPTHD_DKDV_QUERY_HALVES;   // 1: 4 waves; 2: 8 waves splitting each step's rows
+constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-group pairs splitting dK/dV columns
 
 // ---------------------------------------------------------------------------
 // pass 1: delta and dQ over the query tiles
@@ -224,18 +224,22 @@ __device__ inline void issue_q_chunk(const TileLoader<DP, true, NW>& qld, const 
   if (wave == 1) lds_load_dword(make_rsrc(delta + base, (uint32_t)ntok * Hq * 4), En, ld_off);
 }
 
-template <int DP, int NQH>
-__global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
+template <int DP, int SD>
+__global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ dk,
     float* __restrict__ dv, const char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  // 4 * NQH waves: wave w owns keys k0 + 32*(w%4) .. +31 and, with NQH = 2, only
-  // query block w/4 of every 64-row step (the two halves' dK/dV are summed at the end)
-  constexpr int NW = 4 * NQH;
+  // 4 * SD waves.  Wave w owns keys k0 + 32*(w%4) .. +31.  With SD = 2 the two
+  // waves of a key group split the head dimension of dK/dV: wave w computes
+  // S and dP for query block w/4 of each 64-row step only, and the pair swaps
+  // its bf16 P and dS operands through LDS (same lane layout, a plain copy).
+  constexpr int NW = 4 * SD;
+  constexpr int NDB = DP / 32 / SD;   // 32-column blocks of dK/dV per wave
   using QT = LdsTile<DP, true>;   // Q and dO: read by rows (S, dP operands) and transposed (dK, dV operands)
   __shared__ __align__(16) uint16_t Q0[QT::ELEMS], Q1[QT::ELEMS];
   __shared__ __align__(16) uint16_t O0[QT::ELEMS], O1[QT::ELEMS];
   __shared__ __align__(16) float L0[kQChunk], L1[kQChunk], E0[kQChunk], E1[kQChunk];   // LSE*log2(e), delta
+  __shared__ __align__(16) bf16x8 X[SD == 2 ? 4 * 2 * 4 * 64 : 1];   // [key group][query block][P0,P1,dS0,dS1][lane]
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   if (!plan_matches(hdr, prm)) {
@@ -256,7 +260,7 @@ __global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv, S = prm.S;
-  const int kw = wave & 3, qh = wave >> 2;
+  const int kw = wave & 3, dh = wave >> 2;
   const int key = kt.k0 + kw * 32 + l32;            // this lane's key (B operand column)
   const bool key_in = kw * 32 + l32 < kt.nkeys;
   const int64_t krow = (int64_t)key * Hkv + kvh;
@@ -287,16 +291,17 @@ __global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
   // Q / dO rows of a chunk: tile row r = token r/G, head r%G; LSE / delta: one float per row
   const uint32_t tok_bytes = (uint32_t)Hq * D * 2;
   TileLoader<DP, true, NW> qld;
-  qld.init(wave, lane, D, [&](int r) -> int64_t {
+  auto qrowoff = [&](int r) -> int64_t {
     const int t2 = r / G;
     return r < tpc * G ? (int64_t)t2 * tok_bytes + (int64_t)(kvh * G + r - t2 * G) * D * 2 : -1;
-  });
+  };
+  qld.init(wave, lane, D, qrowoff);
   const uint32_t ld_off = lane < tpc * G ? (uint32_t)((lane / G) * Hq + kvh * G + lane % G) * 4u : 0x80000000u;
   auto issue = [&](int i, uint16_t* Qn, uint16_t* On, float* Ln, float* En) {
     int c0, l0, ntok;
     chunk_at(i, c0, l0, ntok);
-    issue_q_chunk<DP, NW>(qld, q, dout, lse2w, delta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn, On, Ln,
-                      En);
+    issue_q_chunk<DP, NW>(qld, q, dout, lse2w, delta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn,
+                          On, Ln, En);
   };
   if (nchunks > 0) issue(0, Q0, O0, L0, E0);
 
@@ -312,11 +317,11 @@ __global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
     kf[s] = as_bf16x8(a);
     vf[s] = as_bf16x8(b);
   }
-  f32x16 dka[DP / 32], dva[DP / 32];
+  f32x16 dka[NDB], dva[NDB];
 #pragma unroll
-  for (int db = 0; db < DP / 32; ++db) {
-    dka[db] = f32x16{};
-    dva[db] = f32x16{};
+  for (int j = 0; j < NDB; ++j) {
+    dka[j] = f32x16{};
+    dva[j] = f32x16{};
   }
   lds_loads_barrier();
 
@@ -330,7 +335,8 @@ __global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
     // row qi (token c0 + qi/G) sees this lane's key iff qi >= (key - c0) * G
     const bool need_mask = kmax > c0;
     const int thr = (key - c0) * G - 4 * h;
-    auto block = [&](int qb) {
+    // P and dS of one 32-row query block as bf16 operands (key as the lane index)
+    auto scores = [&](int qb, bf16x8 (&pd)[4]) {
       f32x16 sc = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
@@ -351,22 +357,40 @@ __global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
           dp[r] = pv * (dp[r] - e4[j]);
         }
       }
-      const bf16x8 p0 = acc_to_bf16(sc, 0), p1 = acc_to_bf16(sc, 8);
-      const bf16x8 s0 = acc_to_bf16(dp, 0), s1 = acc_to_bf16(dp, 8);
+      pd[0] = acc_to_bf16(sc, 0);
+      pd[1] = acc_to_bf16(sc, 8);
+      pd[2] = acc_to_bf16(dp, 0);
+      pd[3] = acc_to_bf16(dp, 8);
+    };
+    // dV += P^T dO, dK += dS^T Q for one query block over this wave's column blocks
+    auto accumulate = [&](int qb, const bf16x8 (&pd)[4]) {
+      const int r0 = 32 * qb + 4 * h;
 #pragma unroll
-      for (int db = 0; db < DP / 32; ++db) {
-        const int r0 = 32 * qb + 4 * h;
-        dva[db] = mfma32(p0, lds_tr8<DP, true>(Dt, r0, r0 + 8, 32 * db), dva[db]);
-        dva[db] = mfma32(p1, lds_tr8<DP, true>(Dt, r0 + 16, r0 + 24, 32 * db), dva[db]);
-        dka[db] = mfma32(s0, lds_tr8<DP, true>(Qt, r0, r0 + 8, 32 * db), dka[db]);
-        dka[db] = mfma32(s1, lds_tr8<DP, true>(Qt, r0 + 16, r0 + 24, 32 * db), dka[db]);
+      for (int j = 0; j < NDB; ++j) {
+        const int c0l = 32 * (dh * NDB + j);
+        dva[j] = mfma32(pd[0], lds_tr8<DP, true>(Dt, r0, r0 + 8, c0l), dva[j]);
+        dva[j] = mfma32(pd[1], lds_tr8<DP, true>(Dt, r0 + 16, r0 + 24, c0l), dva[j]);
+        dka[j] = mfma32(pd[2], lds_tr8<DP, true>(Qt, r0, r0 + 8, c0l), dka[j]);
+        dka[j] = mfma32(pd[3], lds_tr8<DP, true>(Qt, r0 + 16, r0 + 24, c0l), dka[j]);
       }
     };
-    if (NQH == 1) {
-      block(0);
-      block(1);
+    if (SD == 1) {
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        bf16x8 pd[4];
+        scores(qb, pd);
+        accumulate(qb, pd);
+      }
     } else {
-      block(qh);
+      bf16x8 own[4], other[4];
+      scores(dh, own);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) X[((kw * 2 + dh) * 4 + j) * 64 + lane] = own[j];
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) other[j] = X[((kw * 2 + (dh ^ 1)) * 4 + j) * 64 + lane];
+      accumulate(dh, own);
+      accumulate(dh ^ 1, other);
     }
     lds_loads_barrier();
   };
@@ -375,50 +399,18 @@ __global__ __launch_bounds__(256 * NQH, 1) void attn_bwd_dkdv_kernel(
     if (i + 1 < nchunks) step(i + 1, Q1, O1, L1, E1, Q0, O0, L0, E0);
   }
 
-  if (NQH == 2) {
-    // sum the two query halves: waves 4..7 hand their partial sums to waves 0..3 through LDS,
-    // JR of each lane's 16 accumulator values per round (the scratch is the Q0 tile)
-    constexpr int JR = QT::ELEMS * 2 >= 4 * 64 * 16 * 4 ? 16 : (QT::ELEMS * 2 >= 4 * 64 * 8 * 4 ? 8 : 4);
-    float* red = reinterpret_cast<float*>(Q0);
+  // dV[key][d] = C[i = key][j = d]: lane holds d = 32*(dh*NDB + j) + l32 for 16 keys of its key group
 #pragma unroll
-    for (int tsr = 0; tsr < 2; ++tsr)
-#pragma unroll
-      for (int db = 0; db < DP / 32; ++db)
-#pragma unroll
-        for (int j0 = 0; j0 < 16; j0 += JR) {
-          f32x16& a = tsr ? dva[db] : dka[db];
-          if (qh == 1)
-#pragma unroll
-            for (int j = 0; j < JR; j += 4)
-              *reinterpret_cast<f32x4*>(red + ((kw * (JR / 4) + j / 4) * 64 + lane) * 4) =
-                  f32x4{a[j0 + j], a[j0 + j + 1], a[j0 + j + 2], a[j0 + j + 3]};
-          __syncthreads();
-          if (qh == 0)
-#pragma unroll
-            for (int j = 0; j < JR; j += 4) {
-              const f32x4 b = *reinterpret_cast<const f32x4*>(red + ((kw * (JR / 4) + j / 4) * 64 + lane) * 4);
-              a[j0 + j] += b[0];
-              a[j0 + j + 1] += b[1];
-              a[j0 + j + 2] += b[2];
-              a[j0 + j + 3] += b[3];
-            }
-          __syncthreads();
-        }
-    if (qh == 1) return;
-  }
-
-  // dV[key][d] = C[i = key][j = d]: lane holds d = 32*db + l32 for 16 keys of its wave
-#pragma unroll
-  for (int db = 0; db < DP / 32; ++db) {
-    const int d = 32 * db + l32;
+  for (int j = 0; j < NDB; ++j) {
+    const int d = 32 * (dh * NDB + j) + l32;
     if (d >= D) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kl = kw * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (kl < kt.nkeys) {
         const int64_t row = (int64_t)(kt.k0 + kl) * Hkv + kvh;
-        dv[row * D + d] = dva[db][r];
-        dk[row * D + d] = dka[db][r] * prm.scale;
+        dv[row * D + d] = dva[j][r];
+        dk[row * D + d] = dka[j][r] * prm.scale;
       }
     }
   }
@@ -435,8 +427,8 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* o
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse, dq, ws,
                  lay, prm, status);
   if (e) return e;
-  constexpr int NQH = kDkdvQueryHalves;
-  return launch(attn_bwd_dkdv_kernel<DP, NQH>, dim3(grid_kv), dim3(256 * NQH), 0, stream, ev, nev, 1,
+  constexpr int SD = DP >= 64 ? kDkdvSplit : 1;
+  return launch(attn_bwd_dkdv_kernel<DP, SD>, dim3(grid_kv), dim3(256 * SD), 0, stream, ev, nev, 1,
                 (const uint16_t*)q,
                 (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, dk, dv, (const char*)ws, lay,
                 prm, status);
