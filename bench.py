@@ -84,6 +84,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calibration-copy", action="store_true",
+                    help="after the timed region, run one plain copy of the K/V buffers (known bytes) through the "
+                         "restoration kernel in contiguous mode, as the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU's rank share only; run it with --gpus 1 (the multi-GPU all-gather / "
@@ -187,6 +190,12 @@ def main():
             acc[i, 3] += hevs[i][0].elapsed_ms(0, 1)
             acc[i, 4] += hevs[i][1].elapsed_ms(0, 1)
             acc[i, 5] += hevs[i][1].elapsed_ms(2, 3)
+
+    if args.calibration_copy:
+        k2, v2 = torch.empty_like(k_phys), torch.empty_like(v_phys)
+        cpthd.reorder_kv(k_phys, v_phys, cu_p, T, cp, 1, k_out=k2, v_out=v2, dev_status=status)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {2 * k_phys.numel() * 2} bytes read and written")
 
     # pure-GPU step time: the per-kernel event durations of one step
     per_kernel_ms = acc / args.steps

@@ -76,7 +76,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void attn_bwd_dq_kernel(
   TileLoader<DP, true, NW> kld;
   TileLoader<DP, false, NW> vld;
   {
-    auto rowoff = [&](int r) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
+    auto rowoff = [&](int r) __attribute__((always_inline)) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
     kld.init(wave, lane, D, rowoff);
     vld.init(wave, lane, D, rowoff);
   }
@@ -134,7 +134,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void attn_bwd_dq_kernel(
   lds_loads_barrier();
 
   const float sl2 = prm.scale_log2;
-  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
+  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
     const int kb = t.ds + it * kKvStep;
     if (it + 1 < nsteps) {
       const uint32_t soff = (uint32_t)(it + 1) * kKvStep * row_bytes;
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
   }
   const int nchunks = nch[0] + nch[1];
   // chunk i: first token c0 and first local row l0
-  auto chunk_at = [&](int i, int& c0, int& l0, int& ntok) {
+  auto chunk_at = [&](int i, int& c0, int& l0, int& ntok) __attribute__((always_inline)) {
     const int si = i < nch[0] ? 0 : 1;
     c0 = plo[si] + (i - (si ? nch[0] : 0)) * tpc;
     l0 = sl[si] + (c0 - sp[si]);
@@ -291,13 +291,13 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
   // Q / dO rows of a chunk: tile row r = token r/G, head r%G; LSE / delta: one float per row
   const uint32_t tok_bytes = (uint32_t)Hq * D * 2;
   TileLoader<DP, true, NW> qld;
-  auto qrowoff = [&](int r) -> int64_t {
+  auto qrowoff = [&](int r) __attribute__((always_inline)) -> int64_t {
     const int t2 = r / G;
     return r < tpc * G ? (int64_t)t2 * tok_bytes + (int64_t)(kvh * G + r - t2 * G) * D * 2 : -1;
   };
   qld.init(wave, lane, D, qrowoff);
   const uint32_t ld_off = lane < tpc * G ? (uint32_t)((lane / G) * Hq + kvh * G + lane % G) * 4u : 0x80000000u;
-  auto issue = [&](int i, uint16_t* Qn, uint16_t* On, float* Ln, float* En) {
+  auto issue = [&](int i, uint16_t* Qn, uint16_t* On, float* Ln, float* En) __attribute__((always_inline)) {
     int c0, l0, ntok;
     chunk_at(i, c0, l0, ntok);
     issue_q_chunk<DP, NW>(qld, q, dout, lse2w, delta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn,
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
   const float sl2 = prm.scale_log2;
   const int kmax = kt.k0 + kt.nkeys - 1;
   auto step = [&](int i, const uint16_t* Qt, const uint16_t* Dt, const float* Lt, const float* Et, uint16_t* Qn,
-                  uint16_t* On, float* Ln, float* En) {
+                  uint16_t* On, float* Ln, float* En) __attribute__((always_inline)) {
     int c0, l0, ntok;
     chunk_at(i, c0, l0, ntok);
     if (i + 1 < nchunks) issue(i + 1, Qn, On, Ln, En);

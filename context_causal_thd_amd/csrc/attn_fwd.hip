@@ -73,7 +73,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void attn_fwd_kernel(const uint16
   TileLoader<DP, false, NW> kld;
   TileLoader<DP, true, NW> vld;
   {
-    auto rowoff = [&](int r) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
+    auto rowoff = [&](int r) __attribute__((always_inline)) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
     kld.init(wave, lane, D, rowoff);
     vld.init(wave, lane, D, rowoff);
   }
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(64 * (8 / QB), 1) void attn_fwd_kernel(const uint16
   lds_loads_barrier();
 
   const float sl2 = prm.scale_log2;
-  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) {
+  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
     const int kb = t.ds + it * kKvStep;
     if (it + 1 < nsteps) {
       const uint32_t soff = (uint32_t)(it + 1) * kKvStep * row_bytes;
