@@ -40,6 +40,29 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_config3_hbm_traffic.json")
+KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
+KERNEL_SYMBOL = {"attn_fwd": "attn_fwd_kernel", "attn_bwd_dq": "attn_bwd_dq_kernel",
+                 "attn_bwd_dkdv": "attn_bwd_dkdv_kernel"}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
+    calibrated on a plain copy), or None when the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    src = b"".join(open(os.path.join(ROOT, "context_causal_thd_amd", "csrc", f), "rb").read() for f in KERNEL_SOURCES)
+    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+        return None
+    for name, v in rec["kernels"].items():
+        if KERNEL_SYMBOL[kernel] in name:
+            return v["fetch_bytes_per_launch"] + v["write_bytes_per_launch"]
+    return None
+
+
 def useful_pairs(idx, cu_p, cu_a):
     """Allowed (query, key) pairs for the rank's query rows: sum over actual rows of (position + 1)."""
     cu_p = cu_p.astype(np.int64)
@@ -216,7 +239,8 @@ def main():
     j = names.index(dominant)
     achieved = float(np.sum(algo[dominant]) / (kernel_ms[dominant] * 1e-3) / 1e12)
     roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dominant),
+                "traffic_unit": "bytes per launch (HBM, calibrated FETCH_SIZE + WRITE_SIZE)",
                 "avg_launch_us": float(per_kernel_ms[:, j].mean() * 1e3)}
 
     dcs = [i for i, sh in enumerate(shares) if sh["s"] == 0]
