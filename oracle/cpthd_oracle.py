@@ -14,6 +14,10 @@ constraints", and its commit messages and review thread):
   r and 2*cp_size-1-r.  NO_LOAD_BALANCE ("What changed", "Why"): the whole
   physical buffer is cut into cp_size contiguous chunks and rank r owns chunk r;
   documents stay separated only through the sequence metadata.
+  PACKED_SUPER_SEQUENCE (the commit messages' earlier packed policy): the whole
+  physical buffer is treated as one partitioning sequence, cut into 2*cp_size
+  chunks with the same mirrored pairing, documents again separated only by the
+  sequence metadata.
 * ``all_gather`` / ``restore``  the rank-major concatenation that an all-gather
   of per-rank K/V produces, and its inverse ("K/V restoration" in the review
   thread; rank-major ownership "needs no KV reorder" in the commit messages).
@@ -44,6 +48,8 @@ import numpy as np
 
 DUAL_CHUNK_SWAP = 0
 NO_LOAD_BALANCE = 1
+PACKED_SUPER_SEQUENCE = 2
+STRATEGIES = (DUAL_CHUNK_SWAP, NO_LOAD_BALANCE, PACKED_SUPER_SEQUENCE)
 
 _ROW_BLOCK = 1024
 
@@ -79,7 +85,9 @@ def check_layout(cu_padded, cu_actual, cp_size: int, strategy: int) -> None:
             raise ValueError(f"document {i}: padded length {L} not divisible by 2*cp_size")
     if strategy == NO_LOAD_BALANCE and cu_p[-1] % cp_size:
         raise ValueError("T not divisible by cp_size")
-    if strategy not in (DUAL_CHUNK_SWAP, NO_LOAD_BALANCE):
+    if strategy == PACKED_SUPER_SEQUENCE and cu_p[-1] % (2 * cp_size):
+        raise ValueError("T not divisible by 2*cp_size")
+    if strategy not in STRATEGIES:
         raise ValueError("unknown strategy")
 
 
@@ -124,6 +132,9 @@ def partition_indices(cu_padded, cp_size: int, rank: int, strategy: int) -> np.n
             raise ValueError("T not divisible by cp_size")
         S = T // cp_size
         return np.arange(rank * S, (rank + 1) * S, dtype=np.int64)
+    if strategy == PACKED_SUPER_SEQUENCE:
+        # the physical buffer as a single partitioning sequence
+        return partition_indices([0, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)
     raise ValueError("unknown strategy")
 
 

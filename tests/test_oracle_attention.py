@@ -50,7 +50,8 @@ def _inputs(wl, rank, strategy):
 
 
 SMALL = [W.small_random(s, cp, st, max_docs=4, max_len=16, Hq=2, Hkv=1, D=4)
-         for s, cp, st in [(1, 2, 0), (2, 2, 1), (3, 3, 0), (4, 3, 1), (5, 1, 0), (6, 4, 1), (7, 2, 0)]]
+         for s, cp, st in [(1, 2, 0), (2, 2, 1), (3, 3, 0), (4, 3, 1), (5, 1, 0), (6, 4, 1), (7, 2, 0),
+                           (8, 2, 2), (9, 3, 2)]]
 
 
 @pytest.mark.parametrize("wl", SMALL, ids=lambda w: f"{w.name}-cp{w.cp}")
@@ -145,7 +146,7 @@ def _packed_autograd(q, k, v, do, cu_p, cu_a, scale):
     return o, dq, kt.grad.numpy(), vt.grad.numpy()
 
 
-@pytest.mark.parametrize("wl", [W.config1()] + SMALL[:4], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [W.config1()] + SMALL[:4] + SMALL[-2:], ids=lambda w: w.name)
 def test_union_of_ranks_equals_unpartitioned_and_autograd(wl):
     T = wl.T
     q, k, v, do = wl.q(), wl.k(), wl.v(), wl.do()

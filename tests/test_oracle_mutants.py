@@ -35,6 +35,8 @@ MUTANTS = [
     ("ds_sign", "ds = p * (dp - delta[:, None])", "ds = p * (delta[:, None] - dp)"),
     ("dv_wrong_operand", "dv[start:start + a, g] += p.T @ dout", "dv[start:start + a, g] += ds.T @ dout"),
     ("delta_dropped", "delta = np.sum(dout * o, axis=1)", "delta = np.sum(dout * o, axis=1) * 0"),
+    ("packed_per_half", "return partition_indices([0, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)",
+     "return partition_indices([0, cu_p[-1] // 2, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)"),
 ]
 
 
@@ -48,6 +50,7 @@ PINS = [
     TP.test_config1_golden_indices_and_pairs,
     TP.test_config1_golden_gather_restore_maps,
     lambda: [TP.test_partition_invariants(w) for w in TP._random_layouts()[::7]],
+    lambda: [TP.test_packed_super_sequence_on_one_document_is_dual_chunk_swap(cp) for cp in (2, 3)],
     lambda: [TP.test_restore_inverts_all_gather(w) for w in TP._random_layouts()[1::9]],
     lambda: [TP.test_dcs_balances_causal_work_on_unpadded_documents(cp) for cp in (2, 3)],
     lambda: [TA.test_fwd_matches_brute_force(w) for w in TA.SMALL[:3]],

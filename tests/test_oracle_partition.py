@@ -16,6 +16,7 @@ import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "config1.txt")
 STRAT = {"dcs": oracle.DUAL_CHUNK_SWAP, "contiguous": oracle.NO_LOAD_BALANCE}
+PACKED = oracle.PACKED_SUPER_SEQUENCE
 
 
 def _golden():
@@ -53,7 +54,7 @@ def _random_layouts():
     cases = []
     for seed in range(40):
         for cp in (1, 2, 3, 4):
-            for s in (oracle.DUAL_CHUNK_SWAP, oracle.NO_LOAD_BALANCE):
+            for s in (oracle.DUAL_CHUNK_SWAP, oracle.NO_LOAD_BALANCE, PACKED):
                 cases.append(W.small_random(seed, cp, s, max_docs=6, max_len=40))
     return cases
 
@@ -73,6 +74,12 @@ def test_partition_invariants(wl):
         S = T // cp
         for r, p in enumerate(parts):
             assert np.array_equal(p, r * S + np.arange(S))       # closed form: one contiguous chunk
+    elif s == PACKED:
+        c = T // (2 * cp)
+        for r, p in enumerate(parts):
+            # exactly the tokens of whole-buffer chunks r and 2cp-1-r, whatever the documents
+            want = [x for x in range(T) if c and x // c in (r, 2 * cp - 1 - r)]
+            assert p.tolist() == want
     else:
         L = np.diff(wl.cu_padded.astype(np.int64))
         for r, p in enumerate(parts):
@@ -159,3 +166,24 @@ def test_workload_layouts_are_valid():
     cu_p, cu_a = W.config5b()
     assert cu_p[-1] == 1 << 20 and cu_p.size == 10001
     oracle.check_layout(cu_p, cu_a, 4, oracle.DUAL_CHUNK_SWAP)
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4])
+def test_packed_super_sequence_on_one_document_is_dual_chunk_swap(cp):
+    # with a single document filling the buffer the two mirrored policies coincide
+    T = 2 * cp * 7
+    cu = np.array([0, T], dtype=np.int32)
+    for r in range(cp):
+        assert np.array_equal(oracle.partition_indices(cu, cp, r, PACKED),
+                              oracle.partition_indices(cu, cp, r, oracle.DUAL_CHUNK_SWAP))
+
+
+def test_packed_super_sequence_accepts_indivisible_documents():
+    cu = np.array([0, 5, 11, 16], dtype=np.int32)          # no length divisible by 2*cp = 4, T = 16 is
+    oracle.check_layout(cu, cu, 2, PACKED)
+    with pytest.raises(ValueError):
+        oracle.check_layout(cu, cu, 2, oracle.DUAL_CHUNK_SWAP)
+    with pytest.raises(ValueError):
+        oracle.check_layout(np.array([0, 5, 14], dtype=np.int32), None, 2, PACKED)   # 14 % 4 != 0
+    idx0 = oracle.partition_indices(cu, 2, 0, PACKED)
+    assert idx0.tolist() == [0, 1, 2, 3, 12, 13, 14, 15]

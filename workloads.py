@@ -188,7 +188,7 @@ class Workload:
         return normal_rows(self.seed_key, TID_DO, self.T, self.Hq, self.D, self.do_scale, rows, self.bf16)
 
 
-DCS, CONTIG = 0, 1   # strategy codes as passed to both sides (enum values of the C ABI)
+DCS, CONTIG, PACKED = 0, 1, 2   # strategy codes as passed to both sides (enum values of the C ABI)
 
 
 def config1(bf16=False) -> Workload:
@@ -250,8 +250,9 @@ def small_random(seed, cp, strategy, max_docs=5, max_len=32, Hq=2, Hkv=1, D=16, 
         padded.append(L)
         actual.append(a)
     T = sum(padded)
-    if strategy == CONTIG and T % cp:
-        extra = cp - T % cp
+    unit = {CONTIG: cp, PACKED: 2 * cp}.get(strategy, 1)
+    if T % unit:
+        extra = unit - T % unit
         padded[-1] += extra
         if not pads:
             actual[-1] += extra
