@@ -22,6 +22,7 @@ from . import _lib
 
 DUAL_CHUNK_SWAP = 0
 NO_LOAD_BALANCE = 1
+PACKED_SUPER_SEQUENCE = 2
 
 _DEV_BITS = {1: "cu_seqlens_padded not non-decreasing or not starting at 0",
              2: "cu_seqlens_padded[B] != T",

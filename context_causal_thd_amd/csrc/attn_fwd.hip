@@ -235,6 +235,7 @@ int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32
   if (cp < 1 || rank < 0 || rank >= cp) return CPTHD_ERR_RANK;
   if (int e = check_strategy(strategy)) return e;
   if (int e = check_tokens(T, capacity, cp, num_docs)) return e;
+  if (int e = check_strategy_tokens(strategy, T, cp)) return e;
   if (int e = check_heads(Hq, Hkv, D)) return e;
   if (causal != 1 || wl != -1 || wr != 0) return CPTHD_ERR_MASK;
   lay = plan_layout(capacity, cp, Hq, Hkv, num_docs);
@@ -256,7 +257,7 @@ int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32
 // holds the exact count; surplus work-groups exit at once).
 unsigned qtile_grid(const AttnParams& prm) {
   const int64_t bm = tokens_per_qtile(prm.G);
-  const int64_t seg = (prm.strategy == CPTHD_DUAL_CHUNK_SWAP ? 2 : 1) * (int64_t)prm.num_docs;
+  const int64_t seg = (prm.strategy == CPTHD_NO_LOAD_BALANCE ? 1 : 2) * (int64_t)prm.num_docs;
   return (unsigned)(((prm.S + bm - 1) / bm + seg) * prm.Hkv);
 }
 

@@ -70,6 +70,18 @@ __device__ inline DocSeg doc_segments(const int32_t* cu_a, const int32_t* cu_p, 
     d.lb = d.la + c;
     d.pb = ds + (2 * cp - 1 - rank) * c;
     d.nb = c;
+  } else if (strategy == kPacked) {
+    // the document's pieces inside whole-buffer chunks r and 2cp-1-r (c = T / 2cp = S / 2)
+    const int c = S / 2;
+    const int a0 = rank * c, b0 = (2 * cp - 1 - rank) * c;
+    const int alo = max(ds, a0), ahi = min(ds + L, a0 + c);
+    const int blo = max(ds, b0), bhi = min(ds + L, b0 + c);
+    d.na = max(0, ahi - alo);
+    d.pa = alo;
+    d.la = alo - a0;
+    d.nb = max(0, bhi - blo);
+    d.pb = blo;
+    d.lb = c + (blo - b0);
   } else {
     const int lo = max(ds, rank * S), hi = min(ds + L, rank * S + S);
     d.na = max(0, hi - lo);
@@ -280,6 +292,7 @@ extern "C" int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seql
   if (cp_size < 1 || rank < 0 || rank >= cp_size) return CPTHD_ERR_RANK;
   if (int e = check_strategy(strategy)) return e;
   if (int e = check_tokens(total_tokens, capacity_tokens, cp_size, num_docs)) return e;
+  if (int e = check_strategy_tokens(strategy, total_tokens, cp_size)) return e;
   if (int e = check_heads(num_q_heads, num_kv_heads, head_dim)) return e;
   const PlanLayout lay = plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, num_docs);
   if (!workspace || workspace_bytes < lay.total || reinterpret_cast<uintptr_t>(workspace) % 256)

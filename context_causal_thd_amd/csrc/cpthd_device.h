@@ -18,6 +18,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kDCS = 0;      // DualChunkSwap
 constexpr int kContig = 1;   // NO_LOAD_BALANCE
+constexpr int kPacked = 2;   // PACKED_SUPER_SEQUENCE
 
 // status bits (mirror the public header)
 constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual = 8, kDevPlan = 16;

@@ -35,8 +35,15 @@ inline int launch(void (*kernel)(Params...), dim3 grid, dim3 block, size_t shmem
 }
 
 inline int check_strategy(int32_t strategy) {
-  return (strategy == CPTHD_DUAL_CHUNK_SWAP || strategy == CPTHD_NO_LOAD_BALANCE) ? CPTHD_OK
-                                                                                  : CPTHD_ERR_STRATEGY;
+  return (strategy == CPTHD_DUAL_CHUNK_SWAP || strategy == CPTHD_NO_LOAD_BALANCE ||
+          strategy == CPTHD_PACKED_SUPER_SEQUENCE)
+             ? CPTHD_OK
+             : CPTHD_ERR_STRATEGY;
+}
+
+// The whole-buffer mirrored strategy cuts T into 2*cp_size equal chunks.
+inline int check_strategy_tokens(int32_t strategy, int64_t T, int32_t cp) {
+  return (strategy == CPTHD_PACKED_SUPER_SEQUENCE && T % (2 * (int64_t)cp)) ? CPTHD_ERR_TOKENS : CPTHD_OK;
 }
 
 inline int check_tokens(int64_t T, int64_t capacity, int32_t cp, int32_t num_docs) {

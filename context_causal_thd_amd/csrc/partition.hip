@@ -46,6 +46,12 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
   int32_t res[4];
   if (strategy == kContig) {
     for (int u = 0; u < 4; ++u) res[u] = rank * S + (int)j0 + u;
+  } else if (strategy == kPacked) {
+    const int c = T / (2 * cp);   // whole-buffer chunks r and 2cp-1-r
+    for (int u = 0; u < 4; ++u) {
+      const int j = (int)j0 + u;
+      res[u] = j < c ? rank * c + j : (2 * cp - 1 - rank) * c + (j - c);
+    }
   } else {
     // document of output j: cu[i] <= j*cp < cu[i+1]
     int i = upper_index(cu, B - 1, j0 * cp);
@@ -72,9 +78,12 @@ constexpr int kReorderRowsPerWave = 4;
 
 __device__ inline int64_t gathered_row_of(const int32_t* cu, int B, int S, int cp, int strategy, int p) {
   if (strategy == kContig) return p;
-  const int i = upper_index(cu, B - 1, p);       // document holding physical row p
-  const int start = cu[i];
-  const int L = cu[i + 1] - start;
+  int start = 0, L = cp * S;                      // whole buffer as one sequence (packed strategy)
+  if (strategy == kDCS) {
+    const int i = upper_index(cu, B - 1, p);     // document holding physical row p
+    start = cu[i];
+    L = cu[i + 1] - start;
+  }
   const int c = L / (2 * cp);
   if (c <= 0) return p;                           // only for a rejected layout
   const int pos = p - start;
@@ -126,6 +135,7 @@ extern "C" int cpthd_partition_indices(const int32_t* cu_seqlens_padded, int32_t
   if (cp_size < 1 || rank < 0 || rank >= cp_size) return CPTHD_ERR_RANK;
   if (int e = check_strategy(strategy)) return e;
   if (int e = check_tokens(total_tokens, total_tokens, cp_size, num_docs)) return e;
+  if (int e = check_strategy_tokens(strategy, total_tokens, cp_size)) return e;
   const int64_t S = total_tokens / cp_size;
   const int64_t threads = (S + 3) / 4;
   dim3 grid((unsigned)((threads + 255) / 256));
@@ -141,6 +151,7 @@ extern "C" int cpthd_reorder_kv(const void* k_gathered, const void* v_gathered, 
   if (cp_size < 1) return CPTHD_ERR_RANK;
   if (int e = check_strategy(strategy)) return e;
   if (int e = check_tokens(total_tokens, capacity_tokens, cp_size, num_docs)) return e;
+  if (int e = check_strategy_tokens(strategy, total_tokens, cp_size)) return e;
   if (row_bytes <= 0 || row_bytes % 16) return CPTHD_ERR_ALIGN;
   for (const void* p : {k_gathered, v_gathered, (const void*)k_out, (const void*)v_out})
     if (reinterpret_cast<uintptr_t>(p) % 16) return CPTHD_ERR_ALIGN;

@@ -39,8 +39,10 @@
  * - Rank r's local order: DualChunkSwap cuts every document into 2*cp_size
  *   equal chunks and rank r owns chunk r followed by chunk 2*cp_size-1-r of
  *   document 0, then of document 1, ...; NO_LOAD_BALANCE gives rank r the
- *   physical rows [r*S, (r+1)*S).  Either way the local rows are increasing
- *   in physical index.
+ *   physical rows [r*S, (r+1)*S); PACKED_SUPER_SEQUENCE gives rank r the
+ *   physical rows [r*c, (r+1)*c) followed by [(2*cp_size-1-r)*c,
+ *   (2*cp_size-r)*c) with c = T / (2*cp_size).  In every case the local rows
+ *   are increasing in physical index.
  * - Every call is asynchronous on the caller's HIP stream; there is no
  *   device or stream synchronisation inside the library.  The library holds
  *   no mutable global state; concurrent calls on different buffers are safe.
@@ -67,16 +69,21 @@ extern "C" {
 #endif
 
 /* Load-balancing strategy (PR #3221 "How to use": DUAL_CHUNK_SWAP is the
- * default, NO_LOAD_BALANCE the experimental contiguous strategy). */
+ * default, NO_LOAD_BALANCE the experimental contiguous strategy; the commit
+ * messages' earlier packed policy, PACKED_SUPER_SEQUENCE, cuts the whole
+ * physical buffer into 2*cp_size mirrored chunks as one partitioning sequence
+ * and keeps documents apart only through the sequence metadata). */
 #define CPTHD_DUAL_CHUNK_SWAP 0
 #define CPTHD_NO_LOAD_BALANCE 1
+#define CPTHD_PACKED_SUPER_SEQUENCE 2
 
 /* Host-detected status codes (nothing was launched). */
 #define CPTHD_OK 0
 #define CPTHD_ERR_NULL (-1)       /* a required pointer is NULL */
 #define CPTHD_ERR_RANK (-2)       /* cp_size < 1 or rank outside [0, cp_size) */
 #define CPTHD_ERR_STRATEGY (-3)   /* unknown strategy */
-#define CPTHD_ERR_TOKENS (-4)     /* T <= 0, T > capacity, T % cp_size, num_docs < 1, T/cp_size > INT32_MAX */
+#define CPTHD_ERR_TOKENS (-4)     /* T <= 0, T > capacity, T % cp_size (T % (2*cp_size) for PACKED_SUPER_SEQUENCE),
+                                     num_docs < 1, capacity > INT32_MAX */
 #define CPTHD_ERR_HEADS (-5)      /* Hq % Hkv, Hq/Hkv > 64, head_dim not in {16,32,64,128} */
 #define CPTHD_ERR_MASK (-6)       /* causal != 1 or window != (-1, 0) */
 #define CPTHD_ERR_WORKSPACE (-7)  /* workspace NULL / too small / misaligned */
@@ -95,7 +102,9 @@ extern "C" {
  * cpthd_partition_indices -- the physical token indices rank `rank` owns
  * (PR #3221 "Why": DualChunkSwap gives each rank two mirrored chunks of every
  * document; NO_LOAD_BALANCE one contiguous chunk of the physical buffer;
- * "What changed": the native partition-index routine used for batch slicing).
+ * commit messages: PACKED_SUPER_SEQUENCE two mirrored chunks of the whole
+ * buffer; "What changed": the native partition-index routine used for batch
+ * slicing).
  *
  *   cu_seqlens_padded  device int32 [num_docs + 1]
  *   total_tokens       T (must equal cu_seqlens_padded[num_docs]; checked on device)
@@ -117,8 +126,9 @@ int cpthd_partition_indices(const int32_t* cu_seqlens_padded, int32_t num_docs, 
  *   k_out, v_out            device [T rows x row_bytes], physical order
  *   row_bytes               bytes per token row (Hkv * D * sizeof(elem));
  *                           multiple of 16, pointers 16-byte aligned
- * DualChunkSwap: out[idx_s[j]] = gathered[s*S + j] for every rank s, j
- * (bit-exact copy; outputs must not overlap inputs).  NO_LOAD_BALANCE: the
+ * DualChunkSwap and PACKED_SUPER_SEQUENCE: out[idx_s[j]] = gathered[s*S + j]
+ * for every rank s, j (bit-exact copy; outputs must not overlap inputs).
+ * NO_LOAD_BALANCE: the
  * gathered buffer is already in physical order; the call copies it when
  * out != in and does nothing when out == in.
  * Errors: NULL, RANK (cp_size < 1), STRATEGY, TOKENS, ALIGN, ALIAS, LAUNCH;

@@ -62,6 +62,8 @@ def test_partition_host_errors(lib):
     assert f(FAKE, 3, 0, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
     assert f(FAKE, 0, 28, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
     assert f(FAKE, 3, 1 << 33, 2, 0, 1, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]
+    assert f(FAKE, 3, 30, 2, 0, 2, FAKE, None, None) == d["CPTHD_ERR_TOKENS"]      # packed: 30 % 4 != 0
+    assert f(FAKE, 3, 28, 2, 0, 3, FAKE, None, None) == d["CPTHD_ERR_STRATEGY"]
 
 
 def test_reorder_host_errors(lib):
@@ -106,7 +108,8 @@ def test_attention_host_errors(lib):
 
     assert plan(None, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, P, ws_bytes, None, None) == d["CPTHD_ERR_NULL"]
     assert call_plan(r=2) == d["CPTHD_ERR_RANK"]
-    assert call_plan(s=2) == d["CPTHD_ERR_STRATEGY"]
+    assert call_plan(s=3) == d["CPTHD_ERR_STRATEGY"]
+    assert call_plan(s=2, T=62, cap=64) == d["CPTHD_ERR_TOKENS"]   # packed: T % (2*cp) != 0
     assert call_plan(T=66) == d["CPTHD_ERR_TOKENS"]
     assert call_plan(T=128) == d["CPTHD_ERR_TOKENS"]        # above capacity
     assert call_plan(hkv=3) == d["CPTHD_ERR_HEADS"]

@@ -106,7 +106,7 @@ def _small_cases():
     seed = 0
     for D in (16, 32, 64, 128):
         for Hq, Hkv in ((2, 2), (4, 1), (8, 2), (6, 2), (16, 2)):
-            for cp, s in ((1, 0), (2, 0), (3, 1), (4, 1), (2, 1), (4, 0)):
+            for cp, s in ((1, 0), (2, 0), (3, 1), (4, 1), (2, 1), (4, 0), (2, 2), (3, 2)):
                 seed += 1
                 if (seed % 3) and D != 128:
                     continue
@@ -156,7 +156,7 @@ def _sample_docs(wl, idx, n=3):
     return sorted(pick)[:n]
 
 
-@pytest.mark.parametrize("s", [0, 1])
+@pytest.mark.parametrize("s", [0, 1, 2])
 @pytest.mark.parametrize("r", [0, 3])
 def test_config3_sampled(s, r):
     wl = W.config3()
@@ -167,11 +167,12 @@ def test_config3_sampled(s, r):
     sh.compare(docs=docs, kv_heads=[0, 7])
 
 
+@pytest.mark.parametrize("s", [1, 2])
 @pytest.mark.parametrize("r", [0, 7])
-def test_config4_sampled(r):
+def test_config4_sampled(s, r):
     wl = W.config4()
-    log(f"config4 r={r}")
-    sh = Share(wl, 1, r)
+    log(f"config4 s={s} r={r}")
+    sh = Share(wl, s, r)
     doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
     touched = np.unique(doc[sh.idx])
     L = np.diff(wl.cu_padded.astype(np.int64))[touched]
@@ -184,7 +185,7 @@ def test_config5_capacity_microbatches():
     """Fixed-capacity buffers, NaN-poisoned beyond the active T, canaries on output tails."""
     for m in (0, 5, 11):
         wl = W.config5(m)
-        for s in wl.strategies:
+        for s in wl.strategies + (2,):
             for r in (0, 3):
                 log(f"config5 mb={m} T={wl.T} s={s} r={r}")
                 sh = Share(wl, s, r, capacity=W.CONFIG5_CAPACITY, poison=True)

@@ -17,7 +17,7 @@ def _layouts():
     out += [(f"config5.mb{m}", W.config5(m)) for m in range(W.CONFIG5_MICROBATCHES)]
     for seed in range(12):
         for cp in (1, 2, 3, 4, 8):
-            for s in (0, 1):
+            for s in (0, 1, 2):
                 out.append((f"small{seed}.cp{cp}.s{s}", W.small_random(seed, cp, s, max_docs=7, max_len=200)))
     return out
 
@@ -39,7 +39,7 @@ def _gpu_indices(cu_p, T, cp, r, s):
 @pytest.mark.parametrize("name,wl", LAYOUTS, ids=[n for n, _ in LAYOUTS])
 def test_partition_bit_exact(name, wl):
     log(f"partition {name}")
-    for s in (0, 1):
+    for s in (0, 1, 2):
         try:
             oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
         except ValueError:
@@ -53,7 +53,7 @@ def test_partition_bit_exact(name, wl):
 def test_partition_million_tokens_ten_thousand_docs():
     cu_p, _ = W.config5b()
     T = int(cu_p[-1])
-    for s in (0, 1):
+    for s in (0, 1, 2):
         for r in range(4):
             log(f"partition 5b s={s} r={r}")
             np.testing.assert_array_equal(_gpu_indices(cu_p, T, 4, r, s), oracle.partition_indices(cu_p, 4, r, s))
@@ -74,6 +74,10 @@ def test_partition_device_status_bits():
     st = status_dev()
     cpthd.cpthd_partition_indices(i32_dev([0, 8, 12]), 2, 16, 2, 0, 1, out, st)
     assert int(st.item()) & 2
+    st = status_dev()
+    cpthd.cpthd_partition_indices(i32_dev([0, 5, 11, 16]), 3, 16, 2, 1, 2, out, st)   # packed: any lengths
+    assert int(st.item()) == 0
+    assert out[:8].cpu().tolist() == [4, 5, 6, 7, 8, 9, 10, 11]
     torch.cuda.synchronize()
 
 
@@ -91,7 +95,7 @@ def test_reorder_bit_exact(name, wl):
     log(f"reorder {name}")
     row_elems = 1024 if wl.T >= 4096 else 8 * (1 + wl.T % 3)
     cap = max(wl.T, wl.capacity) + 16
-    for s in (0, 1):
+    for s in (0, 1, 2):
         try:
             oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
         except ValueError:
