@@ -28,7 +28,8 @@ _DEV_BITS = {1: "cu_seqlens_padded not non-decreasing or not starting at 0",
              2: "cu_seqlens_padded[B] != T",
              4: "DualChunkSwap: a padded document length is not divisible by 2*cp_size",
              8: "cu_seqlens not non-decreasing, or an actual length exceeds its padded length",
-             16: "workspace does not hold a plan for these arguments"}
+             16: "workspace does not hold a plan for these arguments",
+             32: "a gather index lies outside the source rows"}
 
 
 def _p(t):
@@ -72,6 +73,11 @@ def cpthd_reorder_kv(k_gathered, v_gathered, k_out, v_out, row_bytes, cu_seqlens
     return _lib.call("cpthd_reorder_kv", _p(k_gathered), _p(v_gathered), _p(k_out), _p(v_out), row_bytes,
                      _p(cu_seqlens_padded), num_docs, total_tokens, capacity_tokens, cp_size, strategy,
                      _p(dev_status), _s(stream))
+
+
+def cpthd_gather_rows(src, src_rows, row_bytes, index, n, dst, dev_status=None, stream=None):
+    return _lib.call("cpthd_gather_rows", _p(src), src_rows, row_bytes, _p(index), n, _p(dst), _p(dev_status),
+                     _s(stream))
 
 
 def cpthd_attn_workspace_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs):
@@ -157,6 +163,23 @@ def partition_indices(cu_seqlens_padded, total_tokens, cp_size, rank, strategy, 
         out = torch.empty(total_tokens // cp_size, dtype=torch.int32, device=cu_seqlens_padded.device)
     cpthd_partition_indices(cu_seqlens_padded, num_docs, total_tokens, cp_size, rank, strategy, out, dev_status)
     return out
+
+
+def gather_rows(src, index, out=None, dev_status=None):
+    """out[j] = src[index[j]] along the first dimension (any dtype)."""
+    n = index.numel()
+    if out is None:
+        out = torch.empty((n,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    row_bytes = (src[0].numel() if src.dim() > 1 else 1) * src.element_size()
+    cpthd_gather_rows(src, src.shape[0], row_bytes, index, n, out, dev_status)
+    return out
+
+
+def get_batch_on_this_cp_rank(cu_seqlens_padded, total_tokens, cp_size, rank, strategy, *tensors, dev_status=None):
+    """The rank's slice of per-token tensors (e.g. input_ids, labels, position_ids), partitioned with the
+    same strategy as attention: rows at the rank's partition indices, in local order."""
+    idx = partition_indices(cu_seqlens_padded, total_tokens, cp_size, rank, strategy, dev_status=dev_status)
+    return tuple(gather_rows(t, idx, dev_status=dev_status) for t in tensors)
 
 
 def reorder_kv(k_gathered, v_gathered, cu_seqlens_padded, total_tokens, cp_size, strategy, k_out=None, v_out=None,

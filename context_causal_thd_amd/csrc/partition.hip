@@ -11,6 +11,8 @@
 // (every earlier document contributed L/cp_size rows), so an output position
 // finds its document with one binary search over cu_seqlens_padded, without a
 // prefix sum.
+#include <algorithm>
+
 #include "cpthd_device.h"
 #include "cpthd_host.h"
 
@@ -124,9 +126,53 @@ __global__ __launch_bounds__(256) void reorder_kernel(const char* __restrict__ k
   }
 }
 
+// Row gather dst[j] = src[index[j]]: thread u moves VEC-byte piece u % PR of row u / PR
+// (PR = row_bytes / VEC pieces per row), so consecutive threads read and write
+// consecutive bytes of a row and consecutive rows.
+template <typename V>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, int64_t src_rows,
+                                                          int64_t row_bytes, const int32_t* __restrict__ index,
+                                                          int64_t n, char* __restrict__ dst, int32_t* status) {
+  const int64_t PR = row_bytes / (int64_t)sizeof(V);
+  const int64_t total = n * PR;
+  bool bad = false;
+  for (int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; u < total; u += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t j = u / PR, piece = u - j * PR;
+    const int64_t i = index[j];
+    V val{};
+    if (i >= 0 && i < src_rows)
+      val = *reinterpret_cast<const V*>(src + i * row_bytes + piece * (int64_t)sizeof(V));
+    else
+      bad = true;
+    *reinterpret_cast<V*>(dst + j * row_bytes + piece * (int64_t)sizeof(V)) = val;
+  }
+  if (bad && status) atomicOr(status, kDevIndex);
+}
+
 }  // namespace cpthd
 
 using namespace cpthd;
+
+extern "C" int cpthd_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, const int32_t* index,
+                                 int64_t n, void* dst, int32_t* dev_status, hipStream_t stream) {
+  if (n < 0 || src_rows < 0) return CPTHD_ERR_TOKENS;
+  if (n == 0) return CPTHD_OK;
+  if (!src || !index || !dst) return CPTHD_ERR_NULL;
+  if (row_bytes <= 0 || row_bytes % 4) return CPTHD_ERR_ALIGN;
+  const bool wide = row_bytes % 16 == 0 && reinterpret_cast<uintptr_t>(src) % 16 == 0 &&
+                    reinterpret_cast<uintptr_t>(dst) % 16 == 0;
+  if (reinterpret_cast<uintptr_t>(src) % 4 || reinterpret_cast<uintptr_t>(dst) % 4) return CPTHD_ERR_ALIGN;
+  const char* s0 = (const char*)src;
+  const char* d0 = (const char*)dst;
+  if (d0 < s0 + src_rows * row_bytes && s0 < d0 + n * row_bytes) return CPTHD_ERR_ALIAS;
+  const int64_t units = n * (row_bytes / (wide ? 16 : 4));
+  const unsigned grid = (unsigned)std::min<int64_t>((units + 255) / 256, 65536);
+  if (wide)
+    return launch(gather_rows_kernel<u32x4>, dim3(grid), dim3(256), 0, stream, nullptr, 0, 0, (const char*)src,
+                  src_rows, row_bytes, index, n, (char*)dst, dev_status);
+  return launch(gather_rows_kernel<uint32_t>, dim3(grid), dim3(256), 0, stream, nullptr, 0, 0, (const char*)src,
+                src_rows, row_bytes, index, n, (char*)dst, dev_status);
+}
 
 extern "C" int cpthd_partition_indices(const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
                                        int32_t cp_size, int32_t rank, int32_t strategy, int32_t* out_indices,

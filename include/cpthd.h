@@ -89,7 +89,7 @@ extern "C" {
 #define CPTHD_ERR_WORKSPACE (-7)  /* workspace NULL / too small / misaligned */
 #define CPTHD_ERR_LAUNCH (-8)     /* a HIP launch failed */
 #define CPTHD_ERR_ALIGN (-9)      /* reorder rows not a multiple of 16 bytes or pointers not 16-byte aligned */
-#define CPTHD_ERR_ALIAS (-10)     /* reorder output overlaps its input under DualChunkSwap */
+#define CPTHD_ERR_ALIAS (-10)     /* an output buffer overlaps an input buffer */
 
 /* Device-detected status bits, OR-ed into *dev_status. */
 #define CPTHD_DEV_CU_ORDER 1      /* cu_seqlens_padded not non-decreasing, or [0] != 0 */
@@ -97,6 +97,7 @@ extern "C" {
 #define CPTHD_DEV_DCS_DIVISIBLE 4 /* DualChunkSwap: a padded length not divisible by 2*cp_size */
 #define CPTHD_DEV_ACTUAL 8        /* cu_seqlens not non-decreasing, or an actual length > padded length */
 #define CPTHD_DEV_PLAN 16         /* the workspace does not hold a plan for these arguments */
+#define CPTHD_DEV_INDEX 32        /* a gather index outside [0, src_rows) (that row is written as zeros) */
 
 /*
  * cpthd_partition_indices -- the physical token indices rank `rank` owns
@@ -138,6 +139,23 @@ int cpthd_reorder_kv(const void* k_gathered, const void* v_gathered, void* k_out
                      int64_t row_bytes, const int32_t* cu_seqlens_padded, int32_t num_docs,
                      int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t strategy,
                      int32_t* dev_status, hipStream_t stream);
+
+/*
+ * cpthd_gather_rows -- dst[j] = src[index[j]] for j in [0, n): the rank's
+ * slice of per-token tensors (PR #3221 "How to use": input_ids, labels and
+ * position_ids are partitioned with the same strategy as attention, by the
+ * rank's partition indices; position ids stay global positions).  Works on
+ * raw rows of any element type.
+ *
+ *   src        device, src_rows rows of row_bytes bytes
+ *   index      device int32 [n] (e.g. from cpthd_partition_indices)
+ *   dst        device, n rows of row_bytes bytes; must not overlap src
+ *   row_bytes  multiple of 4; pointers 4-byte aligned (16 for 16-byte rows)
+ * An index outside [0, src_rows) writes a zero row and sets CPTHD_DEV_INDEX.
+ * Errors: NULL, TOKENS (n < 0, src_rows < 0), ALIGN, ALIAS, LAUNCH.
+ */
+int cpthd_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, const int32_t* index, int64_t n,
+                      void* dst, int32_t* dev_status, hipStream_t stream);
 
 /*
  * cpthd_attn_workspace_bytes -- workspace size for cpthd_attn_plan /

@@ -156,6 +156,14 @@ def restore(gathered: np.ndarray, parts) -> np.ndarray:
     return out
 
 
+def batch_on_rank(cu_padded, cp_size: int, rank: int, strategy: int, *tensors):
+    """The rank's slice of per-token tensors (input ids, labels, position ids, ...): rows
+    ``x[idx_r]`` in local order ("How to use": input partitioning uses the same strategy as
+    attention)."""
+    idx = partition_indices(cu_padded, cp_size, rank, strategy)
+    return tuple(np.asarray(x)[idx] for x in tensors)
+
+
 def useful_pairs(idx, cu_padded, cu_actual) -> int:
     """Number of (query, key) pairs the causal mask allows for these query rows."""
     _, pos, valid = token_map(cu_padded, cu_actual)

@@ -146,3 +146,16 @@ def test_product_path_has_no_oracle_or_cpu_fallback():
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"^\s*(import|from)\s+oracle", text, flags=re.M), f
                 assert "numpy" not in text, f
+
+
+def test_gather_host_errors(lib):
+    d = _defines()
+    f = lib.cpthd_gather_rows
+    A, B, I = 0x100000, 0x200000, 0x300000
+    assert f(A, 10, 8, I, 0, B, None, None) == 0                         # nothing to gather
+    assert f(None, 10, 8, I, 4, B, None, None) == d["CPTHD_ERR_NULL"]
+    assert f(A, 10, 8, None, 4, B, None, None) == d["CPTHD_ERR_NULL"]
+    assert f(A, 10, 6, I, 4, B, None, None) == d["CPTHD_ERR_ALIGN"]
+    assert f(A + 2, 10, 8, I, 4, B, None, None) == d["CPTHD_ERR_ALIGN"]
+    assert f(A, 10, 8, I, 4, A + 16, None, None) == d["CPTHD_ERR_ALIAS"]
+    assert f(A, 10, 8, I, -1, B, None, None) == d["CPTHD_ERR_TOKENS"]

@@ -122,3 +122,53 @@ def test_reorder_bit_exact(name, wl):
                                    wl.cp, s, st)
             assert torch.equal(kg, before)
     torch.cuda.synchronize()
+
+
+SLICE = [(n, wl) for n, wl in LAYOUTS if n.startswith(("config1", "config3", "config5.mb3")) or n.endswith(".cp3.s2")]
+
+
+@pytest.mark.parametrize("name,wl", SLICE, ids=[n for n, _ in SLICE])
+def test_batch_slicing_bit_exact(name, wl):
+    """input_ids / labels / position_ids of a rank, sliced with the rank's partition indices."""
+    log(f"slice {name}")
+    rng = np.random.default_rng(7)
+    ids = rng.integers(0, 1 << 40, size=wl.T, dtype=np.int64)
+    labels = rng.integers(-100, 50000, size=wl.T, dtype=np.int64)
+    _, pos, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    dev = [torch.from_numpy(x).to("cuda") for x in (ids, labels, pos.astype(np.int64))]
+    for s in (0, 1, 2):
+        try:
+            oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
+        except ValueError:
+            continue
+        for r in range(wl.cp):
+            st = status_dev()
+            got = cpthd.get_batch_on_this_cp_rank(i32_dev(wl.cu_padded), wl.T, wl.cp, r, s, *dev, dev_status=st)
+            ref = oracle.batch_on_rank(wl.cu_padded, wl.cp, r, s, ids, labels, pos.astype(np.int64))
+            assert int(st.item()) == 0
+            for g, x in zip(got, ref):
+                np.testing.assert_array_equal(g.cpu().numpy(), x)
+
+
+def test_gather_rows_widths_and_bad_index():
+    rng = np.random.default_rng(1)
+    for shape in [(300, 4, 16), (300, 3), (300, 5, 2)]:     # 128-byte bf16 rows, 12-byte and 40-byte rows
+        x = rng.integers(-(1 << 30), 1 << 30, size=shape, dtype=np.int32)
+        if shape == (300, 4, 16):
+            src = torch.from_numpy(x.astype(np.int16)).to("cuda")
+            ref_src = x.astype(np.int16)
+        else:
+            src = torch.from_numpy(x).to("cuda")
+            ref_src = x
+        idx = rng.integers(0, 300, size=517).astype(np.int32)
+        st = status_dev()
+        out = cpthd.gather_rows(src, i32_dev(idx), dev_status=st)
+        assert int(st.item()) == 0
+        np.testing.assert_array_equal(out.cpu().numpy(), ref_src[idx])
+    bad = np.array([0, 5, 300, -1, 7], dtype=np.int32)
+    st = status_dev()
+    out = cpthd.gather_rows(src, i32_dev(bad), dev_status=st)
+    assert int(st.item()) & 32
+    o = out.cpu().numpy()
+    np.testing.assert_array_equal(o[[0, 1, 4]], ref_src[[0, 5, 7]])
+    assert (o[2] == 0).all() and (o[3] == 0).all()

@@ -187,3 +187,23 @@ def test_packed_super_sequence_accepts_indivisible_documents():
         oracle.check_layout(np.array([0, 5, 14], dtype=np.int32), None, 2, PACKED)   # 14 % 4 != 0
     idx0 = oracle.partition_indices(cu, 2, 0, PACKED)
     assert idx0.tolist() == [0, 1, 2, 3, 12, 13, 14, 15]
+
+
+@pytest.mark.parametrize("wl", _random_layouts()[2::7], ids=lambda w: f"{w.name}-cp{w.cp}-s{w.strategies[0]}")
+def test_batch_on_rank_keeps_global_positions(wl):
+    # Slicing (ids, labels, positions) per rank: concatenating the ranks' slices and putting
+    # every row back at its physical index recovers the batch, and each rank's position ids
+    # are the within-document positions of its physical tokens (positions stay global).
+    cp, s = wl.cp, wl.strategies[0]
+    rng = np.random.default_rng(3)
+    ids = rng.integers(0, 50000, size=wl.T)
+    labels = rng.integers(0, 50000, size=wl.T)
+    _, pos, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    slices = [oracle.batch_on_rank(wl.cu_padded, cp, r, s, ids, labels, pos) for r in range(cp)]
+    parts = [oracle.partition_indices(wl.cu_padded, cp, r, s) for r in range(cp)]
+    for j, full in enumerate((ids, labels, pos)):
+        assert np.array_equal(oracle.restore(np.concatenate([sl[j] for sl in slices]), parts), full)
+    for r in range(cp):
+        cu = wl.cu_padded.astype(np.int64)
+        doc = np.searchsorted(cu, parts[r], side="right") - 1
+        assert np.array_equal(slices[r][2], parts[r] - cu[doc])
