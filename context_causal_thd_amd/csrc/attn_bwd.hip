@@ -39,11 +39,11 @@ constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-gr
 // pass 1: delta and dQ over the query tiles
 // ---------------------------------------------------------------------------
 template <int DP, int QB>
-__global__ __launch_bounds__(64 * (8 / QB), 1) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  constexpr int NW = 8 / QB;       // waves; QB 32-row blocks each, 256 rows in all
+  constexpr int NW = kQWaves / QB;  // waves, QB 32-row blocks each
   using KT = LdsTile<DP, true>;    // K: read by rows (S^T operand) and transposed (K^T operand of dQ^T)
   using VT = LdsTile<DP, false>;   // V: read by rows (dP^T operand)
   __shared__ __align__(16) uint16_t K0[KT::ELEMS], K1[KT::ELEMS];
@@ -422,7 +422,7 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const AttnParams& prm, int32_t* status, unsigned grid_q, unsigned grid_kv,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kDqRowBlocks;
-  int e = launch(attn_bwd_dq_kernel<DP, QB>, dim3(grid_q), dim3(64 * (8 / QB)), 0, stream, ev, nev, 0,
+  int e = launch(attn_bwd_dq_kernel<DP, QB>, dim3(grid_q), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
                  (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse, dq, ws,
                  lay, prm, status);

@@ -33,12 +33,12 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
 
 template <int DP, int QB>
-__global__ __launch_bounds__(64 * (8 / QB), 1) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                                           float* __restrict__ lse, const char* __restrict__ ws,
                                                           PlanLayout lay, AttnParams prm, int32_t* status) {
-  constexpr int NW = 8 / QB;       // waves; QB 32-row blocks each, 256 rows in all
+  constexpr int NW = kQWaves / QB;  // waves, QB 32-row blocks each
   using KT = LdsTile<DP, false>;   // K: read by rows (S^T operand)
   using VT = LdsTile<DP, true>;    // V: read through the transpose read (V^T operand)
   // two separate buffers per tensor (not one 2-D array): with the step loop
@@ -225,7 +225,7 @@ static int launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kFwdRowBlocks;
-  return launch(attn_fwd_kernel<DP, QB>, dim3(grid), dim3(64 * (8 / QB)), 0, stream, ev, nev, 0,
+  return launch(attn_fwd_kernel<DP, QB>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
 }
 

@@ -27,7 +27,12 @@ constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual
 // ---------------------------------------------------------------------------
 // tiling constants shared by the plan and the attention kernels
 // ---------------------------------------------------------------------------
-constexpr int kRowsPerWG = 256;   // query rows (token x head pairs) per fwd / dq work-group
+#ifndef CPTHD_ROWS_PER_WG
+#define CPTHD_ROWS_PER_WG 256
+#endif
+constexpr int kRowsPerWG = CPTHD_ROWS_PER_WG;   // query rows (token x head pairs) per fwd / dq work-group
+constexpr int kQWaves = kRowsPerWG / 32;        // fwd / dq waves (one 32-row MFMA block each)
+constexpr int kQMinBlocks = kQWaves >= 8 ? 1 : 8 / kQWaves;   // work-groups per CU the launch bounds ask for
 constexpr int kKeysPerWG = 128;   // keys per dk/dv work-group
 constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
 constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
