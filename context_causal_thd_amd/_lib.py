@@ -27,6 +27,9 @@ SIGNATURES = {
                                c_vp, c_i32]),
     "cpthd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
+# K/V in rank-major all-gathered order: same arguments as the physical-order calls
+SIGNATURES["cpthd_attn_fwd_allgathered"] = SIGNATURES["cpthd_attn_fwd"]
+SIGNATURES["cpthd_attn_bwd_allgathered"] = SIGNATURES["cpthd_attn_bwd"]
 
 _lib = None
 

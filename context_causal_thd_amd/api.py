@@ -92,25 +92,62 @@ def cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capac
                      workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream))
 
 
-def cpthd_attn_fwd(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
-                   num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
-                   workspace, dev_status=None, stream=None, events=None):
+def _attn_fwd_call(name, q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy,
+                   num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local,
+                   lse_local, workspace, dev_status, stream, events):
     ev, nev = _ev(events)
-    return _lib.call("cpthd_attn_fwd", _p(q_local), _p(k), _p(v), total_tokens, capacity_tokens, num_docs, cp_size,
+    return _lib.call(name, _p(q_local), _p(k), _p(v), total_tokens, capacity_tokens, num_docs, cp_size,
                      rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
                      window_right, _p(o_local), _p(lse_local), _p(workspace),
                      workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream), ev, nev)
 
 
-def cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
-                   rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                   window_right, dq_local, dk, dv, workspace, dev_status=None, stream=None, events=None):
+def _attn_bwd_call(name, q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs,
+                   cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                   window_right, dq_local, dk, dv, workspace, dev_status, stream, events):
     ev, nev = _ev(events)
-    return _lib.call("cpthd_attn_bwd", _p(q_local), _p(k), _p(v), _p(o_local), _p(do_local), _p(lse_local),
+    return _lib.call(name, _p(q_local), _p(k), _p(v), _p(o_local), _p(do_local), _p(lse_local),
                      total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads,
                      head_dim, softmax_scale, causal, window_left, window_right, _p(dq_local), _p(dk), _p(dv),
                      _p(workspace), workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream),
                      ev, nev)
+
+
+def cpthd_attn_fwd(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
+                   num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
+                   workspace, dev_status=None, stream=None, events=None):
+    return _attn_fwd_call("cpthd_attn_fwd", q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank,
+                          strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                          window_right, o_local, lse_local, workspace, dev_status, stream, events)
+
+
+def cpthd_attn_fwd_allgathered(q_local, k_gathered, v_gathered, total_tokens, capacity_tokens, num_docs, cp_size,
+                               rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
+                               window_left, window_right, o_local, lse_local, workspace, dev_status=None,
+                               stream=None, events=None):
+    return _attn_fwd_call("cpthd_attn_fwd_allgathered", q_local, k_gathered, v_gathered, total_tokens,
+                          capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
+                          softmax_scale, causal, window_left, window_right, o_local, lse_local, workspace,
+                          dev_status, stream, events)
+
+
+def cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
+                   rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                   window_right, dq_local, dk, dv, workspace, dev_status=None, stream=None, events=None):
+    return _attn_bwd_call("cpthd_attn_bwd", q_local, k, v, o_local, do_local, lse_local, total_tokens,
+                          capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
+                          softmax_scale, causal, window_left, window_right, dq_local, dk, dv, workspace, dev_status,
+                          stream, events)
+
+
+def cpthd_attn_bwd_allgathered(q_local, k_gathered, v_gathered, o_local, do_local, lse_local, total_tokens,
+                               capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads,
+                               head_dim, softmax_scale, causal, window_left, window_right, dq_local, dk_gathered,
+                               dv_gathered, workspace, dev_status=None, stream=None, events=None):
+    return _attn_bwd_call("cpthd_attn_bwd_allgathered", q_local, k_gathered, v_gathered, o_local, do_local,
+                          lse_local, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
+                          num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, dq_local,
+                          dk_gathered, dv_gathered, workspace, dev_status, stream, events)
 
 
 # ----------------------------------------------------------------------------
@@ -227,7 +264,9 @@ class AttnPlan:
 
 
 def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, lse_local=None, dev_status=None,
-             events=None):
+             events=None, kv_allgathered=False):
+    """O and LSE of the rank's query rows.  ``kv_allgathered``: k and v are in rank-major all-gathered order
+    (as an all-gather of the ranks' local K/V leaves them) instead of physical order."""
     S = plan.built["total_tokens"] // plan.cp_size
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
@@ -235,13 +274,16 @@ def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, ls
         o_local = torch.empty((S, plan.Hq, plan.D), dtype=torch.bfloat16, device=q_local.device)
     if lse_local is None:
         lse_local = torch.empty((S, plan.Hq), dtype=torch.float32, device=q_local.device)
-    cpthd_attn_fwd(q_local, k, v, *plan._args(), softmax_scale, 1, -1, 0, o_local, lse_local, plan.workspace,
-                   dev_status, events=events)
+    call = cpthd_attn_fwd_allgathered if kv_allgathered else cpthd_attn_fwd
+    call(q_local, k, v, *plan._args(), softmax_scale, 1, -1, 0, o_local, lse_local, plan.workspace, dev_status,
+         events=events)
     return o_local, lse_local
 
 
 def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softmax_scale=None, dq_local=None,
-             dk=None, dv=None, dev_status=None, events=None):
+             dk=None, dv=None, dev_status=None, events=None, kv_allgathered=False):
+    """dQ of the rank's rows and its partial dK, dV (fp32).  With ``kv_allgathered`` k, v and the returned
+    dk, dv are in rank-major all-gathered order."""
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
     if dq_local is None:
@@ -250,8 +292,9 @@ def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softma
         dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
     if dv is None:
         dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
-    cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, *plan._args(), softmax_scale, 1, -1, 0, dq_local,
-                   dk, dv, plan.workspace, dev_status, events=events)
+    call = cpthd_attn_bwd_allgathered if kv_allgathered else cpthd_attn_bwd
+    call(q_local, k, v, o_local, do_local, lse_local, *plan._args(), softmax_scale, 1, -1, 0, dq_local, dk, dv,
+         plan.workspace, dev_status, events=events)
     return dq_local, dk, dv
 
 
@@ -259,11 +302,12 @@ class CPAttention(torch.autograd.Function):
     """Causal THD attention of one CP rank; backward reuses the plan (and strategy) captured in forward."""
 
     @staticmethod
-    def forward(ctx, q_local, k, v, plan: AttnPlan, softmax_scale):
-        o, lse = attn_fwd(q_local, k, v, plan, softmax_scale)
+    def forward(ctx, q_local, k, v, plan: AttnPlan, softmax_scale, kv_allgathered=False):
+        o, lse = attn_fwd(q_local, k, v, plan, softmax_scale, kv_allgathered=kv_allgathered)
         ctx.plan = plan
         ctx.layout = dict(plan.built)
         ctx.scale = softmax_scale
+        ctx.kv_allgathered = kv_allgathered
         ctx.save_for_backward(q_local, k, v, o, lse)
         return o
 
@@ -272,11 +316,14 @@ class CPAttention(torch.autograd.Function):
         q_local, k, v, o, lse = ctx.saved_tensors
         if ctx.plan.built != ctx.layout:
             raise RuntimeError("the plan was rebuilt for another layout between forward and backward")
-        dq, dk, dv = attn_bwd(q_local, k, v, o, do.contiguous(), lse, ctx.plan, ctx.scale)
-        return dq.to(q_local.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None
+        dq, dk, dv = attn_bwd(q_local, k, v, o, do.contiguous(), lse, ctx.plan, ctx.scale,
+                              kv_allgathered=ctx.kv_allgathered)
+        return dq.to(q_local.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
 
 
-def attention(q_local, k, v, plan: AttnPlan, softmax_scale=None):
+def attention(q_local, k, v, plan: AttnPlan, softmax_scale=None, kv_allgathered=False):
+    """Autograd attention of one CP rank; k and v in physical order, or in rank-major all-gathered order with
+    ``kv_allgathered`` (their gradients then come back in the same order)."""
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
-    return CPAttention.apply(q_local, k, v, plan, softmax_scale)
+    return CPAttention.apply(q_local, k, v, plan, softmax_scale, kv_allgathered)

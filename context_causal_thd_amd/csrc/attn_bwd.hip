@@ -38,14 +38,14 @@ constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-gr
 // ---------------------------------------------------------------------------
 // pass 1: delta and dQ over the query tiles
 // ---------------------------------------------------------------------------
-template <int DP, int QB>
+template <int DP, int QB, bool AG>
 __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
   constexpr int NW = kQWaves / QB;  // waves, QB 32-row blocks each
   using KT = LdsTile<DP, true>;    // K: read by rows (S^T operand) and transposed (K^T operand of dQ^T)
-  using VT = LdsTile<DP, false>;   // V: read by rows (dP^T operand)
+  using VT = LdsTile<DP, true>;    // V: read by rows (dP^T operand), in K's row order (one loader for both)
   __shared__ __align__(16) uint16_t K0[KT::ELEMS], K1[KT::ELEMS];
   __shared__ __align__(16) uint16_t V0[VT::ELEMS], V1[VT::ELEMS];
 
@@ -68,22 +68,27 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
 
+  // K/V rows [ds, kv_end) as in the forward (physical or all-gathered order)
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
   const int kend = t.kv_end;
   const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
-  TileLoader<DP, true, NW> kld;
-  TileLoader<DP, false, NW> vld;
-  {
+  const int64_t kv0 = AG ? 0 : (int64_t)t.ds * Hkv * D;
+  const uint32_t kv_bytes = AG ? (uint32_t)prm.T * row_bytes : (uint32_t)(kend - t.ds) * row_bytes;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kv0, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kv0, kv_bytes);
+  TileLoader<DP, true, NW> kvld;
+  AgMap agm;
+  if constexpr (AG) agm = ag_map(reinterpret_cast<const DocSeg*>(ws + lay.docs)[t.doc], prm);
+  auto issue_kv = [&](int kb, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
+    issue_kv_step<AG>(kvld, krs, vrs, agm, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
+  };
+  if constexpr (AG) {
+    kvld.init_slots(wave, lane, D);
+  } else {
     auto rowoff = [&](int r) __attribute__((always_inline)) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
-    kld.init(wave, lane, D, rowoff);
-    vld.init(wave, lane, D, rowoff);
+    kvld.init(wave, lane, D, rowoff);
   }
-  if (nsteps > 0) {
-    kld.issue(krs, K0, 0, wave);
-    vld.issue(vrs, V0, 0, wave);
-  }
+  if (nsteps > 0) issue_kv(t.ds, K0, V0);
 
   bool row_in[QB], valid[QB];
   int p_q[QB];
@@ -136,11 +141,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_
   const float sl2 = prm.scale_log2;
   auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
     const int kb = t.ds + it * kKvStep;
-    if (it + 1 < nsteps) {
-      const uint32_t soff = (uint32_t)(it + 1) * kKvStep * row_bytes;
-      kld.issue(krs, Kn, soff, wave);
-      vld.issue(vrs, Vn, soff, wave);
-    }
+    if (it + 1 < nsteps) issue_kv(kb + kKvStep, Kn, Vn);
     const bool need_mask = kb + kKvStep - 1 > t.p0;
     bf16x8 dsb[QB][4];
 #pragma unroll
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
         const bf16x8 ka = lds_row8<DP, true>(Kt, 32 * b + l32, 16 * s, h);
-        const bf16x8 va = lds_row8<DP, false>(Vt, 32 * b + l32, 16 * s, h);
+        const bf16x8 va = lds_row8<DP, true>(Vt, 32 * b + l32, 16 * s, h);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           sc[qb] = mfma32(ka, qf[qb][s], sc[qb]);
@@ -217,14 +218,16 @@ __device__ inline void issue_q_chunk(const TileLoader<DP, true, NW>& qld, const 
                                      const float* lse2w, const float* delta, int64_t base, int ntok,
                                      uint32_t tok_bytes, int Hq, int D, uint32_t ld_off, int wave, uint16_t* Qn,
                                      uint16_t* On, float* Ln, float* En) {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource builtins: device pass only
   const uint32_t nrec = (uint32_t)ntok * tok_bytes;
   qld.issue(make_rsrc(q + base * D, nrec), Qn, 0, wave);
   qld.issue(make_rsrc(dout + base * D, nrec), On, 0, wave);
   if (wave == 0) lds_load_dword(make_rsrc(lse2w + base, (uint32_t)ntok * Hq * 4), Ln, ld_off);
   if (wave == 1) lds_load_dword(make_rsrc(delta + base, (uint32_t)ntok * Hq * 4), En, ld_off);
+#endif
 }
 
-template <int DP, int SD>
+template <int DP, int SD, bool AG>
 __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ dk,
@@ -263,7 +266,14 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
   const int kw = wave & 3, dh = wave >> 2;
   const int key = kt.k0 + kw * 32 + l32;            // this lane's key (B operand column)
   const bool key_in = kw * 32 + l32 < kt.nkeys;
-  const int64_t krow = (int64_t)key * Hkv + kvh;
+  AgMap agm;
+  if constexpr (AG) agm = ag_map(ds, prm);
+  // K/V/dK/dV row of a key: physical, or its rank-major all-gathered row
+  auto kv_row = [&](int p) __attribute__((always_inline)) -> int64_t {
+    if constexpr (AG) return (int64_t)agm.row(p) * Hkv + kvh;
+    return (int64_t)p * Hkv + kvh;
+  };
+  const int64_t krow = kv_row(key);
 
   // the rank's rows of the document that see the tile: suffixes (token >= k0)
   // of the document's segments, cut into steps of tpc tokens
@@ -408,7 +418,7 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
     for (int r = 0; r < 16; ++r) {
       const int kl = kw * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
       if (kl < kt.nkeys) {
-        const int64_t row = (int64_t)(kt.k0 + kl) * Hkv + kvh;
+        const int64_t row = kv_row(kt.k0 + kl);
         dv[row * D + d] = dva[j][r];
         dk[row * D + d] = dka[j][r] * prm.scale;
       }
@@ -416,22 +426,64 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
   }
 }
 
-template <int DP>
+template <int DP, bool AG>
 static int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, float* dq, float* dk, float* dv, char* ws, const PlanLayout& lay,
                       const AttnParams& prm, int32_t* status, unsigned grid_q, unsigned grid_kv,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kDqRowBlocks;
-  int e = launch(attn_bwd_dq_kernel<DP, QB>, dim3(grid_q), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
+  int e = launch(attn_bwd_dq_kernel<DP, QB, AG>, dim3(grid_q), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
                  (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse, dq, ws,
                  lay, prm, status);
   if (e) return e;
   constexpr int SD = DP >= 64 ? kDkdvSplit : 1;
-  return launch(attn_bwd_dkdv_kernel<DP, SD>, dim3(grid_kv), dim3(256 * SD), 0, stream, ev, nev, 1,
+  return launch(attn_bwd_dkdv_kernel<DP, SD, AG>, dim3(grid_kv), dim3(256 * SD), 0, stream, ev, nev, 1,
                 (const uint16_t*)q,
                 (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, dk, dv, (const char*)ws, lay,
                 prm, status);
+}
+
+template <bool AG>
+static int dispatch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                        const float* lse, float* dq, float* dk, float* dv, char* ws, const PlanLayout& lay,
+                        const AttnParams& prm, int32_t* status, unsigned gq, unsigned gkv, hipStream_t stream,
+                        hipEvent_t* ev, int nev) {
+  switch (prm.D) {
+    case 16:
+    case 32: return launch_bwd<32, AG>(q, k, v, o, dout, lse, dq, dk, dv, ws, lay, prm, status, gq, gkv, stream, ev, nev);
+    case 64: return launch_bwd<64, AG>(q, k, v, o, dout, lse, dq, dk, dv, ws, lay, prm, status, gq, gkv, stream, ev, nev);
+    default: return launch_bwd<128, AG>(q, k, v, o, dout, lse, dq, dk, dv, ws, lay, prm, status, gq, gkv, stream, ev, nev);
+  }
+}
+
+static int attn_bwd_entry(const void* q_local, const void* k, const void* v, const void* o_local,
+                          const void* do_local, const float* lse_local, int64_t total_tokens, int64_t capacity_tokens,
+                          int32_t num_docs, int32_t cp_size, int32_t rank, int32_t strategy, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                          int32_t window_left, int32_t window_right, float* dq_local, float* dk, float* dv,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+                          hipEvent_t* events, int32_t n_events, bool allgathered) {
+  if (!q_local || !k || !v || !o_local || !do_local || !lse_local || !dq_local || !dk || !dv) return CPTHD_ERR_NULL;
+  PlanLayout lay;
+  AttnParams prm;
+  if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
+                              num_kv_heads, head_dim, causal, window_left, window_right, workspace,
+                              workspace_bytes, lay, prm))
+    return e;
+  const bool ag = allgathered && strategy != CPTHD_NO_LOAD_BALANCE;
+  if (ag) {
+    if (int e = check_allgathered_bytes(total_tokens, num_kv_heads, head_dim)) return e;
+  }
+  prm.scale = softmax_scale;
+  prm.scale_log2 = softmax_scale * 1.4426950408889634f;
+  const unsigned gq = qtile_grid(prm);
+  const unsigned gkv = (unsigned)(((total_tokens + kKeysPerWG - 1) / kKeysPerWG + num_docs) * num_kv_heads);
+  char* ws = (char*)workspace;
+  return ag ? dispatch_bwd<true>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm,
+                                 dev_status, gq, gkv, stream, events, n_events)
+            : dispatch_bwd<false>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm,
+                                  dev_status, gq, gkv, stream, events, n_events);
 }
 
 }  // namespace cpthd
@@ -445,28 +497,22 @@ extern "C" int cpthd_attn_bwd(const void* q_local, const void* k, const void* v,
                               float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
                               float* dq_local, float* dk, float* dv, void* workspace, size_t workspace_bytes,
                               int32_t* dev_status, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
-  if (!q_local || !k || !v || !o_local || !do_local || !lse_local || !dq_local || !dk || !dv) return CPTHD_ERR_NULL;
-  PlanLayout lay;
-  AttnParams prm;
-  if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
-                              num_kv_heads, head_dim, causal, window_left, window_right, workspace,
-                              workspace_bytes, lay, prm))
-    return e;
-  prm.scale = softmax_scale;
-  prm.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const unsigned gq = qtile_grid(prm);
-  const unsigned gkv = (unsigned)(((total_tokens + kKeysPerWG - 1) / kKeysPerWG + num_docs) * num_kv_heads);
-  char* ws = (char*)workspace;
-  switch (head_dim) {
-    case 16:
-    case 32:
-      return launch_bwd<32>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm, dev_status,
-                            gq, gkv, stream, events, n_events);
-    case 64:
-      return launch_bwd<64>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm, dev_status,
-                            gq, gkv, stream, events, n_events);
-    default:
-      return launch_bwd<128>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm,
-                             dev_status, gq, gkv, stream, events, n_events);
-  }
+  return attn_bwd_entry(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
+                        rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                        window_right, dq_local, dk, dv, workspace, workspace_bytes, dev_status, stream, events,
+                        n_events, false);
+}
+
+extern "C" int cpthd_attn_bwd_allgathered(const void* q_local, const void* k, const void* v, const void* o_local,
+                                          const void* do_local, const float* lse_local, int64_t total_tokens,
+                                          int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
+                                          int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                                          int32_t window_right, float* dq_local, float* dk, float* dv,
+                                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
+                                          hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+  return attn_bwd_entry(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
+                        rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                        window_right, dq_local, dk, dv, workspace, workspace_bytes, dev_status, stream, events,
+                        n_events, true);
 }

@@ -30,7 +30,48 @@ __device__ inline bool load_qtile(const char* ws, const PlanLayout& lay, int idx
   t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[idx];
   if (t.lrow0 < 0 || t.ntok < 0 || t.lrow0 > p.S - t.ntok) return false;
   if (t.ds < 0 || t.ds > p.T || t.kv_end < t.ds || t.kv_end > p.T || t.p0 < 0 || t.p0 > p.T - t.ntok) return false;
+  if (t.doc < 0 || t.doc >= p.num_docs) return false;
   return true;
+}
+
+// Row of the rank-major all-gathered K/V buffer (rank 0's local rows, then
+// rank 1's, ...) that holds physical token p.  A partition unit (one document
+// under DualChunkSwap, the whole buffer under the packed strategy) starting at
+// physical token u0 is cut into 2*cp chunks of c tokens; rank j < cp holds
+// chunk j at local rows lb.., and chunk 2cp-1-j right after it at lb + c..,
+// where lb is the unit's first local row (the same on every rank).  The chunk
+// index comes from a float reciprocal plus one correction step: p - u0 < 2^31
+// and the quotient is below 2*cp, so the estimate is off by at most one.
+struct AgMap {
+  int u0, c, lb, S, cp;
+  float rc;
+  __device__ inline int row(int p) const {
+    const int pos = p - u0;
+    const int j0 = (int)((float)pos * rc);
+    const int o0 = pos - j0 * c;
+    const int j = o0 < 0 ? j0 - 1 : (o0 >= c ? j0 + 1 : j0);
+    const int off = o0 < 0 ? o0 + c : (o0 >= c ? o0 - c : o0);
+    const bool first = j < cp;
+    return (first ? j : 2 * cp - 1 - j) * S + lb + (first ? off : c + off);
+  }
+};
+
+// The map of a document's keys (contiguous strategy: the identity, c = S).
+__device__ inline AgMap ag_map(const DocSeg& d, const AttnParams& p) {
+  AgMap m;
+  m.S = p.S;
+  m.cp = p.cp;
+  if (p.strategy == kDCS) {
+    m.u0 = d.ds;
+    m.c = d.na;
+    m.lb = d.la;
+  } else {
+    m.u0 = 0;
+    m.c = p.strategy == kPacked ? p.S / 2 : p.S;
+    m.lb = 0;
+  }
+  m.rc = m.c > 0 ? 1.0f / (float)m.c : 0.f;
+  return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -77,6 +118,32 @@ struct TileLoader {
         if (ro >= 0) off = (uint32_t)(ro + 16 * ch);
       }
       voff[i] = off;
+    }
+  }
+  // Loads whose rows move from step to step: each load's logical row (-1 for
+  // a slot without data) and column byte offset, fixed per lane; set_rows()
+  // then derives the offsets from a per-step row offset function.
+  int srow[NLW];
+  uint32_t scol[NLW];
+  __device__ inline void init_slots(int wave, int lane, int D) {
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int u = wave + NW * i;
+      const int slot = 64 * u + lane;
+      const int R = slot / L::SPR, ch = slot - R * L::SPR;
+      const bool ok = u < L::NLOAD && ch < L::C && ch * 8 < D;
+      srow[i] = ok ? (PERM ? rho(R) : R) : -1;
+      scol[i] = 16u * (uint32_t)ch;
+    }
+  }
+  // off(r): byte offset of logical row r >= 0 (any r: the caller selects), valid(r): row has data
+  template <typename Off, typename Valid>
+  __device__ inline void set_rows(Off off, Valid valid) {
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int r = srow[i];
+      const uint32_t o = off(r < 0 ? 0 : r) + scol[i];
+      voff[i] = (r >= 0 && valid(r)) ? o : 0x80000000u;
     }
   }
   __device__ inline void issue(__amdgpu_buffer_rsrc_t rsrc, uint16_t* tile, uint32_t soff, int wave) const {
@@ -144,6 +211,34 @@ __device__ inline bf16x8 acc_to_bf16(const f32x16& a, int r0) {
   v.z = pack_bf16x2(a[r0 + 4], a[r0 + 5]);
   v.w = pack_bf16x2(a[r0 + 6], a[r0 + 7]);
   return as_bf16x8(v);
+}
+
+// Direct loads of the K and V rows of keys [kb, kb + 64) of kv head kvh into
+// one step's tiles (same rows, same lane offsets, two descriptors); keys from
+// kend on read as zero.  Physical order: the descriptors start at the
+// document's first key ds and the lane offsets were set once, so a step only
+// moves the scalar offset.  Rank-major all-gathered order (AG): the
+// descriptors cover all T rows (T * row_bytes < 2^31) and every lane's row
+// offsets go through the map, per step.
+template <bool AG, int DP, int NW>
+__device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buffer_rsrc_t krs,
+                                     __amdgpu_buffer_rsrc_t vrs, const AgMap& agm, int kb, int ds, int kend,
+                                     uint32_t row_bytes, int kvh, int D, int wave, int lane, uint16_t* Kn,
+                                     uint16_t* Vn) {
+#if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource builtins: device pass only
+  if constexpr (AG) {
+    const uint32_t col = (uint32_t)kvh * D * 2;
+    const int last = kend - 1;
+    ld.set_rows([&](int r) __attribute__((always_inline)) { return (uint32_t)agm.row(min(kb + r, last)) * row_bytes + col; },
+                [&](int r) __attribute__((always_inline)) { return kb + r < kend; });
+    ld.issue(krs, Kn, 0, wave);
+    ld.issue(vrs, Vn, 0, wave);
+  } else {
+    const uint32_t soff = (uint32_t)(kb - ds) * row_bytes;
+    ld.issue(krs, Kn, soff, wave);
+    ld.issue(vrs, Vn, soff, wave);
+  }
+#endif
 }
 
 // Host helpers shared by the forward and backward entry points.

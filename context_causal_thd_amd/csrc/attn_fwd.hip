@@ -32,15 +32,18 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 #endif
 constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
 
-template <int DP, int QB>
+template <int DP, int QB, bool AG>
 __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                                           float* __restrict__ lse, const char* __restrict__ ws,
                                                           PlanLayout lay, AttnParams prm, int32_t* status) {
   constexpr int NW = kQWaves / QB;  // waves, QB 32-row blocks each
-  using KT = LdsTile<DP, false>;   // K: read by rows (S^T operand)
-  using VT = LdsTile<DP, true>;    // V: read through the transpose read (V^T operand)
+  // K: read by rows (S^T operand); V: read through the transpose read (V^T
+  // operand).  Both use the transpose-friendly row order, so one loader with
+  // the same lane offsets fills both.
+  using KT = LdsTile<DP, true>;
+  using VT = LdsTile<DP, true>;
   // two separate buffers per tensor (not one 2-D array): with the step loop
   // unrolled by two, every LDS access names its buffer statically, so the
   // in-flight direct loads into the other buffer need no wait before it
@@ -64,23 +67,30 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
 
-  // K/V rows [ds, kv_end) of kv head kvh; rows past kv_end read as zero
+  // K/V rows [ds, kv_end) of kv head kvh; rows past kv_end read as zero.
+  // Physical order: one descriptor over the document's rows, a scalar offset
+  // per step.  All-gathered order: a descriptor over all T rows and per-step
+  // row offsets through the map.
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
   const int kend = t.kv_end;
   const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
-  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + (int64_t)t.ds * Hkv * D, (uint32_t)(kend - t.ds) * row_bytes);
-  TileLoader<DP, false, NW> kld;
-  TileLoader<DP, true, NW> vld;
-  {
+  const int64_t kv0 = AG ? 0 : (int64_t)t.ds * Hkv * D;
+  const uint32_t kv_bytes = AG ? (uint32_t)prm.T * row_bytes : (uint32_t)(kend - t.ds) * row_bytes;
+  const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kv0, kv_bytes);
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kv0, kv_bytes);
+  TileLoader<DP, true, NW> kvld;
+  AgMap agm;
+  if constexpr (AG) agm = ag_map(reinterpret_cast<const DocSeg*>(ws + lay.docs)[t.doc], prm);
+  auto issue_kv = [&](int kb, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
+    issue_kv_step<AG>(kvld, krs, vrs, agm, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
+  };
+  if constexpr (AG) {
+    kvld.init_slots(wave, lane, D);
+  } else {
     auto rowoff = [&](int r) __attribute__((always_inline)) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
-    kld.init(wave, lane, D, rowoff);
-    vld.init(wave, lane, D, rowoff);
+    kvld.init(wave, lane, D, rowoff);
   }
-  if (nsteps > 0) {
-    kld.issue(krs, K0, 0, wave);
-    vld.issue(vrs, V0, 0, wave);
-  }
+  if (nsteps > 0) issue_kv(t.ds, K0, V0);
 
   // the lane's query row in each of the wave's 32-row blocks
   bool row_in[QB], valid[QB];
@@ -121,11 +131,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
   const float sl2 = prm.scale_log2;
   auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
     const int kb = t.ds + it * kKvStep;
-    if (it + 1 < nsteps) {
-      const uint32_t soff = (uint32_t)(it + 1) * kKvStep * row_bytes;
-      kld.issue(krs, Kn, soff, wave);
-      vld.issue(vrs, Vn, soff, wave);
-    }
+    if (it + 1 < nsteps) issue_kv(kb + kKvStep, Kn, Vn);
 
     f32x16 sc[QB][2];
 #pragma unroll
@@ -134,7 +140,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
       for (int qb = 0; qb < QB; ++qb) sc[qb][b] = f32x16{};
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
-        const bf16x8 a = lds_row8<DP, false>(Kt, 32 * b + l32, 16 * s, h);
+        const bf16x8 a = lds_row8<DP, true>(Kt, 32 * b + l32, 16 * s, h);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) sc[qb][b] = mfma32(a, qf[qb][s], sc[qb][b]);
       }
@@ -220,13 +226,25 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
   }
 }
 
-template <int DP>
+template <int DP, bool AG>
 static int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const char* ws,
                       const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kFwdRowBlocks;
-  return launch(attn_fwd_kernel<DP, QB>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
+  return launch(attn_fwd_kernel<DP, QB, AG>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+}
+
+template <bool AG>
+static int dispatch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const char* ws,
+                        const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
+                        hipStream_t stream, hipEvent_t* ev, int nev) {
+  switch (prm.D) {
+    case 16:
+    case 32: return launch_fwd<32, AG>(q, k, v, o, lse, ws, lay, prm, status, grid, stream, ev, nev);
+    case 64: return launch_fwd<64, AG>(q, k, v, o, lse, ws, lay, prm, status, grid, stream, ev, nev);
+    default: return launch_fwd<128, AG>(q, k, v, o, lse, ws, lay, prm, status, grid, stream, ev, nev);
+  }
 }
 
 int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32_t strategy, int32_t num_docs,
@@ -265,12 +283,12 @@ unsigned qtile_grid(const AttnParams& prm) {
 
 using namespace cpthd;
 
-extern "C" int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, int64_t total_tokens,
-                              int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
-                              int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                              float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
-                              void* o_local, float* lse_local, void* workspace, size_t workspace_bytes,
-                              int32_t* dev_status, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+static int attn_fwd_entry(const void* q_local, const void* k, const void* v, int64_t total_tokens,
+                          int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank, int32_t strategy,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                          int32_t causal, int32_t window_left, int32_t window_right, void* o_local, float* lse_local,
+                          void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+                          hipEvent_t* events, int32_t n_events, bool allgathered) {
   if (!q_local || !k || !v || !o_local || !lse_local) return CPTHD_ERR_NULL;
   PlanLayout lay;
   AttnParams prm;
@@ -278,14 +296,40 @@ extern "C" int cpthd_attn_fwd(const void* q_local, const void* k, const void* v,
                               num_kv_heads, head_dim, causal, window_left, window_right, workspace,
                               workspace_bytes, lay, prm))
     return e;
+  // the gathered order differs from the physical one unless ownership is contiguous
+  const bool ag = allgathered && strategy != CPTHD_NO_LOAD_BALANCE;
+  if (ag) {
+    if (int e = check_allgathered_bytes(total_tokens, num_kv_heads, head_dim)) return e;
+  }
   prm.scale = softmax_scale;
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
   const unsigned grid = qtile_grid(prm);
   const char* ws = (const char*)workspace;
-  switch (head_dim) {
-    case 16:
-    case 32: return launch_fwd<32>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events, n_events);
-    case 64: return launch_fwd<64>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events, n_events);
-    default: return launch_fwd<128>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events, n_events);
-  }
+  return ag ? dispatch_fwd<true>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events,
+                                 n_events)
+            : dispatch_fwd<false>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events,
+                                  n_events);
+}
+
+extern "C" int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, int64_t total_tokens,
+                              int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
+                              int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+                              void* o_local, float* lse_local, void* workspace, size_t workspace_bytes,
+                              int32_t* dev_status, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
+  return attn_fwd_entry(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
+                        num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
+                        workspace, workspace_bytes, dev_status, stream, events, n_events, false);
+}
+
+extern "C" int cpthd_attn_fwd_allgathered(const void* q_local, const void* k, const void* v, int64_t total_tokens,
+                                          int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
+                                          int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
+                                          int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                                          int32_t window_right, void* o_local, float* lse_local, void* workspace,
+                                          size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+                                          hipEvent_t* events, int32_t n_events) {
+  return attn_fwd_entry(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
+                        num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
+                        workspace, workspace_bytes, dev_status, stream, events, n_events, true);
 }

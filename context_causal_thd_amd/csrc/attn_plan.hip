@@ -8,7 +8,7 @@
 //
 // Here the two steps become *segments*: maximal runs of the rank's local rows
 // that are consecutive physical tokens of one document.  A query tile is up to
-// 128/G tokens of one segment (times the G q heads of a kv head); its causal key
+// 256/G tokens of one segment (times the G q heads of a kv head); its causal key
 // range is [document start, last actual token of the tile].  A key tile is up
 // to 128 keys of one document's slot; the rank's rows that see it are the
 // suffixes (physical token >= first key) of the document's segments.  Both

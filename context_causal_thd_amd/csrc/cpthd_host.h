@@ -54,6 +54,12 @@ inline int check_tokens(int64_t T, int64_t capacity, int32_t cp, int32_t num_doc
   return CPTHD_OK;
 }
 
+// Kernels reading the rank-major all-gathered K/V address all T rows through
+// one 32-bit buffer descriptor.
+inline int check_allgathered_bytes(int64_t T, int32_t Hkv, int32_t D) {
+  return T * Hkv * D * 2 < ((int64_t)1 << 31) ? CPTHD_OK : CPTHD_ERR_TOKENS;
+}
+
 inline int check_heads(int32_t Hq, int32_t Hkv, int32_t D) {
   if (Hq < 1 || Hkv < 1 || Hq % Hkv) return CPTHD_ERR_HEADS;
   if (Hq / Hkv > 64) return CPTHD_ERR_HEADS;

@@ -55,7 +55,7 @@
  *   touches memory outside its arguments' ranges.
  * - Optional timing: `events` may point to n_events caller-created hipEvent_t
  *   handles, used in (start, stop) pairs around each kernel the call launches,
- *   in launch order (recorded by hipExtLaunchKernelGGL).  NULL / 0 = none.
+ *   in launch order (recorded by hipExtLaunchKernel).  NULL / 0 = none.
  */
 #ifndef CPTHD_H
 #define CPTHD_H
@@ -232,6 +232,40 @@ int cpthd_attn_bwd(const void* q_local, const void* k, const void* v, const void
                    int32_t causal, int32_t window_left, int32_t window_right, float* dq_local,
                    float* dk, float* dv, void* workspace, size_t workspace_bytes, int32_t* dev_status,
                    hipStream_t stream, hipEvent_t* events, int32_t n_events);
+
+/*
+ * cpthd_attn_fwd_allgathered / cpthd_attn_bwd_allgathered -- cpthd_attn_fwd and
+ * cpthd_attn_bwd with k and v (and, backward, dk and dv) in the rank-major
+ * all-gathered order instead of physical order: row s*S + j holds the token
+ * at local row j of rank s, which is what an all-gather of the ranks' local
+ * K/V produces (PR #3221 "Why": rank-major contiguous ownership needs no K/V
+ * reorder; the other strategies pay a restoration).  The kernels read every
+ * key through the inverse of the partition, so no restoration pass
+ * (cpthd_reorder_kv) and no physical-order copy of K/V are needed.  dk/dv are
+ * written in the same gathered order, which is the layout a reduce-scatter
+ * over the ranks splits into per-rank slices.  Results are identical to
+ * cpthd_reorder_kv + cpthd_attn_fwd / cpthd_attn_bwd with dk/dv permuted.
+ * Under NO_LOAD_BALANCE the two orders coincide.
+ *
+ * Arguments, plan and errors as cpthd_attn_fwd / cpthd_attn_bwd, plus:
+ * under DUAL_CHUNK_SWAP and PACKED_SUPER_SEQUENCE, T * Hkv * D * 2 must be
+ * below 2^31 bytes (CPTHD_ERR_TOKENS otherwise).
+ */
+int cpthd_attn_fwd_allgathered(const void* q_local, const void* k_gathered, const void* v_gathered,
+                               int64_t total_tokens, int64_t capacity_tokens, int32_t num_docs, int32_t cp_size,
+                               int32_t rank, int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                               int32_t window_right, void* o_local, float* lse_local, void* workspace,
+                               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+                               hipEvent_t* events, int32_t n_events);
+int cpthd_attn_bwd_allgathered(const void* q_local, const void* k_gathered, const void* v_gathered,
+                               const void* o_local, const void* do_local, const float* lse_local,
+                               int64_t total_tokens, int64_t capacity_tokens, int32_t num_docs, int32_t cp_size,
+                               int32_t rank, int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
+                               int32_t window_right, float* dq_local, float* dk_gathered, float* dv_gathered,
+                               void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+                               hipEvent_t* events, int32_t n_events);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* cpthd_status_string(int status);

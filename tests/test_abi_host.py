@@ -159,3 +159,26 @@ def test_gather_host_errors(lib):
     assert f(A + 2, 10, 8, I, 4, B, None, None) == d["CPTHD_ERR_ALIGN"]
     assert f(A, 10, 8, I, 4, A + 16, None, None) == d["CPTHD_ERR_ALIAS"]
     assert f(A, 10, 8, I, -1, B, None, None) == d["CPTHD_ERR_TOKENS"]
+
+
+def test_allgathered_attention_host_errors(lib):
+    """The rank-major K/V entry points validate like the physical-order ones, plus the 2 GiB K/V bound."""
+    d = _defines()
+    P = 0x100000
+    fwd, bwd = lib.cpthd_attn_fwd_allgathered, lib.cpthd_attn_bwd_allgathered
+    ws_small = lib.cpthd_attn_workspace_bytes(64, 2, 4, 2, 16, 4)
+    assert fwd(P, None, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, ws_small, None, None, None, 0) \
+        == d["CPTHD_ERR_NULL"]
+    assert fwd(P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 0, -1, 0, P, P, P, ws_small, None, None, None, 0) \
+        == d["CPTHD_ERR_MASK"]
+    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, P, 16, None, None,
+               None, 0) == d["CPTHD_ERR_WORKSPACE"]
+    # T * Hkv * D * 2 = 2^31 bytes: the gathered K/V would not fit one 32-bit buffer range
+    T, cp, hq, hkv, D = 1 << 20, 4, 32, 8, 128
+    wsb = lib.cpthd_attn_workspace_bytes(T, cp, hq, hkv, D, 16)
+    assert wsb > 0
+    for s in (0, 2):
+        assert fwd(P, P, P, T, T, 16, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, wsb, None, None, None, 0) \
+            == d["CPTHD_ERR_TOKENS"]
+        assert bwd(P, P, P, P, P, P, T, T, 16, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, P, wsb, None, None,
+                   None, 0) == d["CPTHD_ERR_TOKENS"]

@@ -22,7 +22,7 @@ cpthd = pytest.importorskip("context_causal_thd_amd")
 class Share:
     """One rank's share on the GPU: plan, forward and (optionally) backward."""
 
-    def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False):
+    def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False, allgathered=False):
         self.wl, self.s, self.r = wl, strategy, rank
         T, cp = wl.T, wl.cp
         S = T // cp
@@ -32,6 +32,11 @@ class Share:
         q = wl.q(self.idx)
         k, v = wl.k(), wl.v()
         self.q_np, self.k_np, self.v_np = q, k, v
+        # rank-major all-gathered K/V (the simulated all-gather of every rank's local rows)
+        self.allgathered = allgathered
+        self.parts = [oracle.partition_indices(wl.cu_padded, cp, rr, strategy) for rr in range(cp)]
+        if allgathered:
+            k, v = oracle.all_gather(k, self.parts), oracle.all_gather(v, self.parts)
         fill = float("nan") if poison else 0.0
 
         def buf(shape_tail, src, dtype=torch.bfloat16, rows=cap):
@@ -50,7 +55,8 @@ class Share:
         canary = 7.0
         self.o = torch.full((capS, wl.Hq, wl.D), canary, dtype=torch.bfloat16, device="cuda")
         self.lse = torch.full((capS, wl.Hq), canary, dtype=torch.float32, device="cuda")
-        cpthd.attn_fwd(self.q, self.k, self.v, self.plan, wl.softmax_scale, self.o, self.lse, self.st)
+        cpthd.attn_fwd(self.q, self.k, self.v, self.plan, wl.softmax_scale, self.o, self.lse, self.st,
+                       kv_allgathered=allgathered)
         self.S, self.capS, self.cap = S, capS, cap
         if backward:
             do = wl.do(self.idx)
@@ -60,7 +66,7 @@ class Share:
             self.dk = torch.full((cap, wl.Hkv, wl.D), canary, dtype=torch.float32, device="cuda")
             self.dv = torch.full((cap, wl.Hkv, wl.D), canary, dtype=torch.float32, device="cuda")
             cpthd.attn_bwd(self.q, self.k, self.v, self.o, self.do, self.lse, self.plan, wl.softmax_scale,
-                           self.dq, self.dk, self.dv, self.st)
+                           self.dq, self.dk, self.dv, self.st, kv_allgathered=allgathered)
         torch.cuda.synchronize()
         assert int(self.st.item()) == 0, cpthd.api.describe_dev_status(int(self.st.item()))
 
@@ -93,6 +99,8 @@ class Share:
         dq = to_np64(self.dq[:S])
         dk = to_np64(self.dk[:T])
         dv = to_np64(self.dv[:T])
+        if self.allgathered:   # back to physical order
+            dk, dv = oracle.restore(dk, self.parts), oracle.restore(dv, self.parts)
         for name, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
             assert np.isfinite(x).all(), f"{name} must be finite everywhere"
         assert (dq[~vq] == 0).all() and (dk[~valid_tok] == 0).all() and (dv[~valid_tok] == 0).all()
@@ -192,6 +200,55 @@ def test_config5_capacity_microbatches():
                 sh.check_tails()
                 docs = _sample_docs(wl, sh.idx, n=2)
                 sh.compare(docs=docs, kv_heads=[3])
+
+
+# ---------------------------------------------------------------------------
+# K/V read straight from the rank-major all-gathered buffer (no restoration pass)
+# ---------------------------------------------------------------------------
+def test_config1_allgathered_all_shares():
+    wl = W.config1(bf16=True)
+    for s in wl.strategies + (2,):
+        for r in wl.ranks:
+            log(f"config1 allgathered s={s} r={r}")
+            Share(wl, s, r, allgathered=True).compare()
+
+
+SMALL_AG = [w for w in SMALL if w.strategies[0] != 1][::2] + [w for w in SMALL if w.strategies[0] == 1][:2]
+
+
+@pytest.mark.parametrize("wl", SMALL_AG, ids=lambda w: f"{w.name}-D{w.D}-h{w.Hq}x{w.Hkv}-cp{w.cp}-s{w.strategies[0]}")
+def test_small_allgathered_parity(wl):
+    s = wl.strategies[0]
+    for r in range(wl.cp):
+        log(f"{wl.name} allgathered T={wl.T} s={s} r={r}")
+        Share(wl, s, r, allgathered=True).compare()
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("case", ["config3-s0-r0", "config3-s0-r3", "config3-s2-r1", "config5.mb5-s0-r2"])
+def test_allgathered_bitwise_equals_physical(case):
+    """Same arithmetic, other addresses: O, LSE, dQ bit-identical; dK/dV are the physical ones permuted
+    into rank-major order."""
+    name, s, r = case.split("-")
+    s, r = int(s[1:]), int(r[1:])
+    if name == "config3":
+        wl, kw = W.config3(), {}
+    else:
+        wl, kw = W.config5(int(name.split("mb")[1])), dict(capacity=W.CONFIG5_CAPACITY, poison=True)
+    log(f"{case} physical")
+    a = Share(wl, s, r, **kw)
+    log(f"{case} allgathered")
+    b = Share(wl, s, r, allgathered=True, **kw)
+    b.check_tails()
+    S, T = wl.T // wl.cp, wl.T
+    for x, y in ((a.o, b.o), (a.lse, b.lse), (a.dq, b.dq)):
+        assert torch.equal(_bits(x[:S]), _bits(y[:S]))
+    order = torch.from_numpy(oracle.all_gather(np.arange(T), a.parts)).to("cuda")
+    assert torch.equal(_bits(a.dk[:T][order]), _bits(b.dk[:T]))
+    assert torch.equal(_bits(a.dv[:T][order]), _bits(b.dv[:T]))
 
 
 def test_plan_mismatch_sets_status_and_writes_nothing():
