@@ -11,7 +11,10 @@ cp_size = 4, ranks 0 and 3, both strategies).  For every share:
 Inputs are resident in HBM before the timed region.  The metric is useful
 causal attention FLOP/s: forward 4*D*Hq*N, backward 10*D*Hq*N, with N the
 number of (query, key) pairs the causal document mask allows for the share's
-actual query rows.  Prints one JSON line; progress goes to stderr.
+actual query rows.  The same shares are then timed once more with attention
+reading the rank-major gathered K/V directly (no restoration pass), reported
+under breakdown.allgathered_path.  Prints one JSON line; progress goes to
+stderr.
 """
 from __future__ import annotations
 
@@ -214,6 +217,36 @@ def main():
             acc[i, 4] += hevs[i][1].elapsed_ms(0, 1)
             acc[i, 5] += hevs[i][1].elapsed_ms(2, 3)
 
+    # the same shares with attention reading the rank-major gathered K/V directly (no restoration pass)
+    def step_allgathered(he):
+        for i, sh in enumerate(shares):
+            cpthd.partition_indices(cu_p, T, cp, sh["r"], sh["s"], out=sh["idx"], dev_status=status)
+            sh["plan"].build(cu_a, cu_p, T, sh["r"], sh["s"], status)
+            cpthd.attn_fwd(sh["q"], sh["kg"], sh["vg"], sh["plan"], wl.softmax_scale, sh["o"], sh["lse"], status,
+                           events=he[i][0] if he else None, kv_allgathered=True)
+            cpthd.attn_bwd(sh["q"], sh["kg"], sh["vg"], sh["o"], sh["do"], sh["lse"], sh["plan"], wl.softmax_scale,
+                           sh["dq"], sh["dk"], sh["dv"], status, events=he[i][1] if he else None,
+                           kv_allgathered=True)
+
+    for _ in range(args.warmup):
+        step_allgathered(None)
+    ag_events = [[[cpthd.HipEvents(2), cpthd.HipEvents(4)] for _ in shares] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k_step in range(args.steps):
+        step_allgathered(ag_events[k_step])
+    torch.cuda.synchronize()
+    ag_elapsed = time.perf_counter() - t0
+    cpthd.check_dev_status(status)
+    ag_acc = np.zeros((len(shares), 3))
+    for he in ag_events:
+        for i in range(len(shares)):
+            ag_acc[i, 0] += he[i][0].elapsed_ms(0, 1)
+            ag_acc[i, 1] += he[i][1].elapsed_ms(0, 1)
+            ag_acc[i, 2] += he[i][1].elapsed_ms(2, 3)
+    ag_acc /= args.steps
+    log(f"allgathered path: {args.steps} steps in {ag_elapsed:.3f} s")
+
     if args.calibration_copy:
         k2, v2 = torch.empty_like(k_phys), torch.empty_like(v_phys)
         cpthd.reorder_kv(k_phys, v_phys, cu_p, T, cp, 1, k_out=k2, v_out=v2, dev_status=status)
@@ -261,6 +294,14 @@ def main():
         "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
         "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
         "gpu_kernel_ms_per_step": gpu_step_ms,
+        # attention reading the all-gathered (rank-major) K/V through the inverse partition map: partition +
+        # plan + fwd + bwd per share, no restoration pass; dK/dV come out in the gathered order
+        "allgathered_path": {
+            "ms_per_step": ag_elapsed * 1e3 / args.steps,
+            "tflops": step_flops / (ag_elapsed / args.steps) / 1e12,
+            "kernel_ms_per_step": {n: float(ag_acc[:, jj].sum())
+                                   for jj, n in enumerate(["attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"])},
+        },
     }
 
     cpu = None
