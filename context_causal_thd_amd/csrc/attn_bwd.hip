@@ -34,12 +34,18 @@ constexpr int kDqRowBlocks = CPTHD_DQ_ROW_BLOCKS;   // 32-row blocks per wave (1
 #define CPTHD_DKDV_SPLIT 2
 #endif
 constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-group pairs splitting dK/dV columns
+#ifndef CPTHD_DQ_PIPE
+#define CPTHD_DQ_PIPE 1   // read-ahead scheduling hints in the dQ pass
+#endif
+#ifndef CPTHD_DKDV_REVERSE
+#define CPTHD_DKDV_REVERSE 1   // dK/dV: visit a key tile's query chunks last first
+#endif
 
 // ---------------------------------------------------------------------------
 // pass 1: delta and dQ over the query tiles
 // ---------------------------------------------------------------------------
 template <int DP, int QB, bool AG>
-__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_EU(kQWaves / QB * kQMinBlocks / 4) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
@@ -122,7 +128,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_
                  __uint_as_float(a & 0xFFFF0000u) * __uint_as_float(b & 0xFFFF0000u);
       }
     }
-    dlt[qb] = dpart + xor32(dpart);
+    dlt[qb] = sum_xor32(dpart);
     lse2[qb] = valid[qb] ? lse[qrow[qb]] * 1.4426950408889634f : INFINITY;
     if (row_in[qb] && h == 0) {
       delta[qrow[qb]] = valid[qb] ? dlt[qb] : 0.f;
@@ -162,6 +168,9 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_
           dp[qb] = mfma32(va, df[qb][s], dp[qb]);
         }
       }
+#if CPTHD_DQ_PIPE
+      if constexpr (QB == 1) pipeline_reads_mfma<2 * (DP / 16), 4>();
+#endif
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         const int lim = p_q[qb] - kb - 32 * b - 4 * h;   // key offset 8(r/4) + r%4 allowed iff <= lim
@@ -183,6 +192,9 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_bwd_dq_
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, dsb[qb][ks], acc[qb][db]);
       }
+#if CPTHD_DQ_PIPE
+    if constexpr (QB == 1) pipeline_reads_mfma<4 * (DP / 32), 2, 2>();
+#endif
     lds_loads_barrier();
   };
   for (int it = 0; it < nsteps; it += 2) {
@@ -228,7 +240,7 @@ __device__ inline void issue_q_chunk(const TileLoader<DP, true, NW>& qld, const 
 }
 
 template <int DP, int SD, bool AG>
-__global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ dk,
     float* __restrict__ dv, const char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
@@ -292,6 +304,11 @@ __global__ __launch_bounds__(256 * SD, 1) void attn_bwd_dkdv_kernel(
   const int nchunks = nch[0] + nch[1];
   // chunk i: first token c0 and first local row l0
   auto chunk_at = [&](int i, int& c0, int& l0, int& ntok) __attribute__((always_inline)) {
+#if CPTHD_DKDV_REVERSE
+    // last chunk first: every key tile of a document starts on the document's
+    // last rows, so concurrently running tiles share their Q / dO reads in L2
+    i = nchunks - 1 - i;
+#endif
     const int si = i < nch[0] ? 0 : 1;
     c0 = plo[si] + (i - (si ? nch[0] : 0)) * tpc;
     l0 = sl[si] + (c0 - sp[si]);

@@ -203,6 +203,21 @@ __device__ inline bf16x8 lds_tr8(const uint16_t* tile, int q0, int q1, int c0) {
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Scheduling hint for a run of N MFMAs that consume R LDS reads each, in
+// order: keep the reads of AHEAD products in flight ahead of the products, so
+// a product waits for reads issued AHEAD products earlier rather than for the
+// ones just issued.  Place it after the run's code.
+template <int N, int AHEAD, int R = 1>
+__device__ inline void pipeline_reads_mfma() {
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R, 0);   // LDS reads
+#pragma unroll
+  for (int i = 0; i < N - AHEAD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, R, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, AHEAD, 0);
+}
+
 // Eight accumulator entries r0..r0+7 of a 32x32 result as a bf16 operand.
 __device__ inline bf16x8 acc_to_bf16(const f32x16& a, int r0) {
   u32x4 v;

@@ -30,10 +30,13 @@ constexpr float kRescaleThreshold = 8.0f;   // log2 units
 #ifndef CPTHD_FWD_ROW_BLOCKS
 #define CPTHD_FWD_ROW_BLOCKS 1
 #endif
-constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
+constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;
+#ifndef CPTHD_FWD_PREFETCH
+#define CPTHD_FWD_PREFETCH 1
+#endif   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
 
 template <int DP, int QB, bool AG>
-__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_kernel(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_EU(kQWaves / QB * kQMinBlocks / 4) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                                           float* __restrict__ lse, const char* __restrict__ ws,
@@ -129,11 +132,34 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
   lds_loads_barrier();
 
   const float sl2 = prm.scale_log2;
-  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
-    const int kb = t.ds + it * kKvStep;
-    if (it + 1 < nsteps) issue_kv(kb + kKvStep, Kn, Vn);
-
-    f32x16 sc[QB][2];
+  f32x16 sc[QB][2];   // scores of one step (key as the VGPR index, query as the lane)
+  // S^T of a step's 64 keys against the wave's rows
+  auto s_products = [&](const uint16_t* Kt) __attribute__((always_inline)) {
+#if CPTHD_FWD_PREFETCH
+    // all K operands of key block 0 first, then block 1's reads overlap block 0's products
+    bf16x8 ka[DP / 16], kb1[DP / 16];
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) ka[s] = lds_row8<DP, true>(Kt, l32, 16 * s, h);
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) sc[qb][0] = sc[qb][1] = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) {
+      kb1[s] = lds_row8<DP, true>(Kt, 32 + l32, 16 * s, h);
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb][0] = mfma32(ka[s], qf[qb][s], sc[qb][0]);
+    }
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, QB, 0);  // then the products of one operand
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int s = 0; s < DP / 16; ++s)
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) sc[qb][1] = mfma32(kb1[s], qf[qb][s], sc[qb][1]);
+#else
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -145,9 +171,11 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
         for (int qb = 0; qb < QB; ++qb) sc[qb][b] = mfma32(a, qf[qb][s], sc[qb][b]);
       }
     }
-
+#endif
+  };
+  // online softmax of the step from key kb on: P (bf16 operands) and the running max / sum
+  auto softmax = [&](int kb, bf16x8 (&pb)[QB][4]) __attribute__((always_inline)) {
     const bool need_mask = kb + kKvStep - 1 > t.p0;
-    bf16x8 pb[QB][4];
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) {
       if (need_mask) {
@@ -164,7 +192,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
       for (int b = 0; b < 2; ++b)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[qb][b][r]);
-      mx = fmaxf(mx, xor32(mx)) * sl2;
+      mx = max_xor32(mx) * sl2;
       if (__any(mx > m_i[qb] + kRescaleThreshold)) {
         const float m_new = fmaxf(m_i[qb], mx);
         const float alpha = exp2_fast(m_i[qb] - (m_new == -INFINITY ? 0.f : m_new));
@@ -187,7 +215,9 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) pb[qb][ks] = acc_to_bf16(sc[qb][ks >> 1], 8 * (ks & 1));
     }
-
+  };
+  // O^T += V^T P^T
+  auto pv_products = [&](const uint16_t* Vt, const bf16x8 (&pb)[QB][4]) __attribute__((always_inline)) {
 #pragma unroll
     for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
@@ -196,7 +226,14 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][ks], acc[qb][db]);
       }
-
+  };
+  auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
+    const int kb = t.ds + it * kKvStep;
+    if (it + 1 < nsteps) issue_kv(kb + kKvStep, Kn, Vn);
+    bf16x8 pb[QB][4];
+    s_products(Kt);
+    softmax(kb, pb);
+    pv_products(Vt, pb);
     lds_loads_barrier();
   };
   for (int it = 0; it < nsteps; it += 2) {
@@ -206,7 +243,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) void attn_fwd_ker
 
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float l_tot = l_i[qb] + xor32(l_i[qb]);
+    const float l_tot = sum_xor32(l_i[qb]);
     if (!row_in[qb]) continue;
     const float inv = (valid[qb] && l_tot > 0.f) ? 1.f / l_tot : 0.f;
 #pragma unroll

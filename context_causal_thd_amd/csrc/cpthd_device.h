@@ -33,6 +33,17 @@ constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual
 constexpr int kRowsPerWG = CPTHD_ROWS_PER_WG;   // query rows (token x head pairs) per fwd / dq work-group
 constexpr int kQWaves = kRowsPerWG / 32;        // fwd / dq waves (one 32-row MFMA block each)
 constexpr int kQMinBlocks = kQWaves >= 8 ? 1 : 8 / kQWaves;   // work-groups per CU the launch bounds ask for
+// Register-budget hint: a kernel that runs as one work-group of W waves per CU
+// has W/4 waves per SIMD and never more, so the scheduler may spend the whole
+// 512/(W/4) registers on latency hiding instead of chasing occupancy it cannot get.
+#ifndef CPTHD_WAVES_HINT
+#define CPTHD_WAVES_HINT 1
+#endif
+#if CPTHD_WAVES_HINT
+#define CPTHD_WAVES_PER_EU(n) __attribute__((amdgpu_waves_per_eu(n, n)))
+#else
+#define CPTHD_WAVES_PER_EU(n)
+#endif
 constexpr int kKeysPerWG = 128;   // keys per dk/dv work-group
 constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
 constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
@@ -114,7 +125,18 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int 
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
-__device__ inline float xor32(float x) { return __shfl_xor(x, 32, 64); }
+// Reductions of x with the value of the lane 32 apart, the same bits in both
+// lanes.  v_permlane32_swap (a VALU op, no LDS round trip) with x as both
+// operands returns, in lanes 0-31, (own, lane + 32) and in lanes 32-63,
+// (lane - 32, own) -- lane layout checked on gfx950.
+__device__ inline float max_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float sum_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // fp32 -> bf16 bits, round to nearest even (inputs are finite)
 __device__ inline uint16_t f2bf(float f) {
