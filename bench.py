@@ -51,16 +51,28 @@ KERNEL_SYMBOL = {"attn_fwd": "cpthd::attn_fwd_kernel<128, 1, false>",
                  "attn_bwd_dkdv": "cpthd::attn_bwd_dkdv_kernel<128, 2, false>"}
 
 
+def kernel_source_hash(root=ROOT):
+    """sha256 of the attention kernels' code: the sources with comments removed and whitespace collapsed, so a
+    comment edit does not invalidate counters taken on the same code."""
+    import hashlib
+    import re
+    code = []
+    for f in KERNEL_SOURCES:
+        text = open(os.path.join(root, "context_causal_thd_amd", "csrc", f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        code.append(" ".join(text.split()))
+    return hashlib.sha256("\n".join(code).encode()).hexdigest()
+
+
 def measured_traffic(kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
     calibrated on a plain copy), or None when the kernel sources changed since the counters were taken."""
-    import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    src = b"".join(open(os.path.join(ROOT, "context_causal_thd_amd", "csrc", f), "rb").read() for f in KERNEL_SOURCES)
-    if hashlib.sha256(src).hexdigest() != rec.get("source_sha256"):
+    if kernel_source_hash() != rec.get("source_sha256"):
         return None
     v = rec["kernels"].get(KERNEL_SYMBOL[kernel])
     return None if v is None else v["fetch_bytes_per_launch"] + v["write_bytes_per_launch"]

@@ -10,17 +10,20 @@
 // T physical rows; a reduce-scatter over the ranks would sum them.
 //
 // Two passes, no atomics, deterministic:
-//   1. query tiles (the forward's tiles, 64 rows per wave): delta from O and
+//   1. query tiles (the forward's tiles, 32 rows per wave): delta from O and
 //      dO, then per 64-key step S^T = K Q^T, P^T = exp2(S^T - LSE),
 //      dP^T = V dO^T, dS^T = P^T (dP^T - delta), dQ^T += K^T dS^T (the K^T
 //      operand comes from the natural K tile through the transpose LDS read);
-//   2. key tiles (128 keys of one document, 32 per wave): for every query row
-//      of the rank that sees the tile, 64 rows per step, S = Q K^T and
-//      dP = dO V^T with the key as the lane index, dS = P (dP - delta),
-//      dV += P^T dO and dK += dS^T Q (dO^T and Q^T operands through the
-//      transpose read of the natural tiles).
-// Both passes load the next step's rows into registers while computing the
-// current one and double-buffer their LDS tiles.
+//   2. key tiles (128 keys of one document; 8 waves, each pair of waves
+//      sharing 32 keys and splitting the dK/dV columns): for every query row
+//      of the rank that sees the tile, 64 rows per step, last rows first,
+//      S = Q K^T and dP = dO V^T with the key as the lane index,
+//      dS = P (dP - delta), dV += P^T dO and dK += dS^T Q (dO^T and Q^T
+//      operands through the transpose read of the natural tiles).
+// Both passes load the next step's rows straight into the other half of
+// double-buffered LDS tiles while computing the current one.  K/V (and dK/dV)
+// rows are in physical order, or in rank-major all-gathered order for the
+// all-gathered entry point.
 #include "attn_common.h"
 #include "cpthd_host.h"
 

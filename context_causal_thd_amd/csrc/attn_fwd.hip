@@ -7,20 +7,22 @@
 // document d attends to the actual keys of d at positions <= p's position.
 //
 // One work-group = one query tile of the plan (<= 256/G tokens of one segment
-// times the G q heads of one kv head: 256 rows, 64 per wave as two 32-row MFMA
-// blocks) against its key range [document start, last actual token of the
+// times the G q heads of one kv head: 256 rows, 8 waves of one 32-row MFMA
+// block each) against its key range [document start, last actual token of the
 // tile], 64 keys per step:
-//   S^T = K Q^T (bf16 MFMA 32x32x16; K read from LDS once per key block and
-//   used for both row blocks; Q in registers),
+//   S^T = K Q^T (bf16 MFMA 32x32x16; K operands read by rows from LDS, all of
+//   a 32-key block's ahead of its products; Q in registers),
 //   online softmax in fp32 / exp2 with the query as the lane index and a
 //   rescale of the running output only when a row maximum grows by more than
 //   2^8 (the exponentials stay <= 256, the final normalisation is exact),
 //   O^T += V^T P^T (V^T operand straight from the natural V tile through the
 //   transpose LDS read; P^T straight from the score registers).
-// The next step's K/V rows are loaded into registers while the current step
-// computes, then written to the other half of a double-buffered LDS tile.
-// Key steps past the causal diagonal are never visited; only steps that
-// straddle it apply the per-element mask.
+// The next step's K/V rows go straight from global memory into the other half
+// of double-buffered LDS tiles (buffer loads with an LDS destination) while the
+// current step computes.  K/V rows are in physical order, or, for the
+// all-gathered entry point, in rank-major order and read through the inverse
+// of the partition.  Key steps past the causal diagonal are never visited;
+// only steps that straddle it apply the per-element mask.
 #include "attn_common.h"
 #include "cpthd_host.h"
 
