@@ -40,6 +40,9 @@ constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-gr
 #ifndef CPTHD_DQ_PIPE
 #define CPTHD_DQ_PIPE 1   // read-ahead scheduling hints in the dQ pass
 #endif
+#ifndef CPTHD_DKDV_PIPE
+#define CPTHD_DKDV_PIPE 2   // dK/dV score products: row reads kept this many ahead (0: no hint)
+#endif
 #ifndef CPTHD_DKDV_REVERSE
 #define CPTHD_DKDV_REVERSE 1   // dK/dV: visit a key tile's query chunks last first
 #endif
@@ -373,6 +376,9 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
         sc = mfma32(lds_row8<DP, true>(Qt, 32 * qb + l32, 16 * s, h), kf[s], sc);
         dp = mfma32(lds_row8<DP, true>(Dt, 32 * qb + l32, 16 * s, h), vf[s], dp);
       }
+#if CPTHD_DKDV_PIPE
+      pipeline_reads_mfma<2 * (DP / 16), CPTHD_DKDV_PIPE>();
+#endif
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int q4 = 32 * qb + 8 * g4 + 4 * h;
@@ -412,15 +418,17 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
         accumulate(qb, pd);
       }
     } else {
-      bf16x8 own[4], other[4];
-      scores(dh, own);
+      // the wave's own block first (before the exchange barrier), then the partner's:
+      // only one set of operands is live at a time
+      bf16x8 pd[4];
+      scores(dh, pd);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) X[((kw * 2 + dh) * 4 + j) * 64 + lane] = own[j];
+      for (int j = 0; j < 4; ++j) X[((kw * 2 + dh) * 4 + j) * 64 + lane] = pd[j];
+      accumulate(dh, pd);
       __syncthreads();
 #pragma unroll
-      for (int j = 0; j < 4; ++j) other[j] = X[((kw * 2 + (dh ^ 1)) * 4 + j) * 64 + lane];
-      accumulate(dh, own);
-      accumulate(dh ^ 1, other);
+      for (int j = 0; j < 4; ++j) pd[j] = X[((kw * 2 + (dh ^ 1)) * 4 + j) * 64 + lane];
+      accumulate(dh ^ 1, pd);
     }
     lds_loads_barrier();
   };
