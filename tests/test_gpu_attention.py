@@ -251,6 +251,35 @@ def test_allgathered_bitwise_equals_physical(case):
     assert torch.equal(_bits(a.dv[:T][order]), _bits(b.dv[:T]))
 
 
+def _degenerate_cases():
+    """Hand-made layouts: empty documents (first, in the middle, last), documents with no actual token, a
+    document with one actual token, DualChunkSwap documents of exactly 2*cp tokens (one token per chunk)."""
+    out = []
+    for cp in (1, 2, 3):
+        u = 2 * cp
+        docs = [(0, 0), (u, 1), (0, 0), (2 * u, 0), (u, u), (3 * u + 2 * u * 40, 3 * u + 2 * u * 40 - 1), (0, 0)]
+        padded = [p for p, _ in docs]
+        actual = [a for _, a in docs]
+        for s in (0, 1, 2):
+            wl = W.Workload(f"degenerate-cp{cp}-s{s}", [77, cp, s], sum(padded), 8, 2, 64, W._cu(padded),
+                            W._cu(actual), cp, (s,), tuple(range(cp)), True, qkv_scale=0.5, do_scale=1.0, bf16=True)
+            oracle.check_layout(wl.cu_padded, wl.cu_actual, cp, s)
+            out.append(wl)
+    return out
+
+
+DEGENERATE = _degenerate_cases()
+
+
+@pytest.mark.parametrize("wl", DEGENERATE, ids=lambda w: w.name)
+@pytest.mark.parametrize("allgathered", [False, True])
+def test_degenerate_layouts(wl, allgathered):
+    s = wl.strategies[0]
+    for r in range(wl.cp):
+        log(f"{wl.name} allgathered={allgathered} r={r}")
+        Share(wl, s, r, allgathered=allgathered).compare()
+
+
 def test_plan_mismatch_sets_status_and_writes_nothing():
     wl = W.config1(bf16=True)
     sh = Share(wl, 0, 0)
