@@ -29,7 +29,8 @@ _DEV_BITS = {1: "cu_seqlens_padded not non-decreasing or not starting at 0",
              4: "DualChunkSwap: a padded document length is not divisible by 2*cp_size",
              8: "cu_seqlens not non-decreasing, or an actual length exceeds its padded length",
              16: "workspace does not hold a plan for these arguments",
-             32: "a gather index lies outside the source rows"}
+             32: "a gather index lies outside the source rows",
+             64: "a document's K/V rows reach 2 GiB (one 32-bit buffer range per document)"}
 
 
 def _p(t):

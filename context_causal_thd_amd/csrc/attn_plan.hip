@@ -158,6 +158,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (p1 < p0) bits |= kDevCuOrder;
     if (a1 < a0 || a1 - a0 > p1 - p0) bits |= kDevActual;
     if (strategy == kDCS && ((p1 - p0) % (2 * cp)) != 0) bits |= kDevDcsDivisible;
+    if ((int64_t)(p1 - p0) * Hkv * D * 2 >= ((int64_t)1 << 31)) bits |= kDevDocBytes;
   }
   if (tid == 0) {
     if (cu_p[0] != 0) bits |= kDevCuOrder;

@@ -22,7 +22,7 @@ constexpr int kPacked = 2;   // PACKED_SUPER_SEQUENCE
 
 // status bits (mirror the public header)
 constexpr int kDevCuOrder = 1, kDevCuTotal = 2, kDevDcsDivisible = 4, kDevActual = 8, kDevPlan = 16,
-              kDevIndex = 32;
+              kDevIndex = 32, kDevDocBytes = 64;
 
 // ---------------------------------------------------------------------------
 // tiling constants shared by the plan and the attention kernels

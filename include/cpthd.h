@@ -98,6 +98,7 @@ extern "C" {
 #define CPTHD_DEV_ACTUAL 8        /* cu_seqlens not non-decreasing, or an actual length > padded length */
 #define CPTHD_DEV_PLAN 16         /* the workspace does not hold a plan for these arguments */
 #define CPTHD_DEV_INDEX 32        /* a gather index outside [0, src_rows) (that row is written as zeros) */
+#define CPTHD_DEV_DOC_BYTES 64    /* a document's K/V rows (padded length * Hkv * head_dim * 2 bytes) reach 2 GiB */
 
 /*
  * cpthd_partition_indices -- the physical token indices rank `rank` owns
@@ -178,7 +179,8 @@ size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp_size, int3
  *   workspace                      device, >= cpthd_attn_workspace_bytes(...)
  *                                  for capacity_tokens and num_docs, 256-byte aligned
  * Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, WORKSPACE, LAUNCH; device bits
- * CU_ORDER, CU_TOTAL, DCS_DIVISIBLE, ACTUAL.
+ * CU_ORDER, CU_TOTAL, DCS_DIVISIBLE, ACTUAL, DOC_BYTES (the kernels address a
+ * document's K/V rows through one 32-bit buffer range).
  */
 int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t num_docs,
                     int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,

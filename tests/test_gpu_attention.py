@@ -306,3 +306,16 @@ def test_plan_rejects_bad_layouts():
     plan.build(i32_dev([0, 9, 17, 24]), i32_dev(wl.cu_padded), 28, 0, 0, st)   # actual 9 > padded 8
     torch.cuda.synchronize()
     assert int(st.item()) & 8
+
+
+def test_plan_rejects_documents_of_2gib_kv():
+    """A document whose K/V rows reach 2 GiB (2^20 tokens x 8 kv heads x 128 x 2 bytes) is refused with a
+    device status bit; one just below the limit plans cleanly."""
+    T = 1 << 20
+    plan = cpthd.AttnPlan(T, 1, 8, 8, 128, max_docs=2)
+    for lengths, bit in (([T], 64), ([T - 64, 64], 0)):
+        cu = i32_dev(np.concatenate([[0], np.cumsum(lengths)]))
+        st = status_dev()
+        plan.build(cu, cu, T, 0, 1, st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == bit, lengths
