@@ -264,23 +264,35 @@ def main():
         log(f"allgathered path: {args.steps} steps in {ag_elapsed:.3f} s")
         ag = {"ms_per_step": ag_elapsed * 1e3 / args.steps}
 
-    # practical HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V),
-    # with a 512 MiB write between reps so the 256 MiB last-level cache holds none of the source
+    # HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V), and the
+    # restoration alone, each cold (a 512 MiB write before every rep evicts the 256 MiB last-level cache) and
+    # the copy also warm (the source left in that cache, as inside the step)
     copy_src = torch.cat([k_phys.reshape(-1), v_phys.reshape(-1)])
     copy_dst = torch.empty_like(copy_src)
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    copy_ms = []
-    for rep in range(6):
-        flush.fill_(rep)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        copy_dst.copy_(copy_src)
-        e1.record()
-        torch.cuda.synchronize()
-        if rep:
-            copy_ms.append(e0.elapsed_time(e1))
+    sh0 = next(sh for sh in shares if sh["s"] == 0)
+
+    def median_ms(fn, cold):
+        ms = []
+        for rep in range(7):
+            if cold:
+                flush.fill_(rep)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if rep:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    moved = 2.0 * 2.0 * T * Hkv * D * 2     # K and V, read + write
+    copy_cold = moved / (median_ms(lambda: copy_dst.copy_(copy_src), True) * 1e-3) / 1e9
+    copy_warm = moved / (median_ms(lambda: copy_dst.copy_(copy_src), False) * 1e-3) / 1e9
+    reorder_cold = moved / (median_ms(lambda: cpthd.reorder_kv(sh0["kg"], sh0["vg"], cu_p, T, cp, 0, k_out=sh0["k"],
+                                                              v_out=sh0["v"], dev_status=status), True) * 1e-3) / 1e9
+    cpthd.check_dev_status(status)
     del flush, copy_dst, copy_src
-    copy_gbs = 2.0 * 2.0 * T * Hkv * D * 2 / (float(np.median(copy_ms)) * 1e-3) / 1e9
 
     if args.calibration_copy:
         k2, v2 = torch.empty_like(k_phys), torch.empty_like(v_phys)
@@ -328,7 +340,8 @@ def main():
         "partition_gbs": float(part_bytes / (per_kernel_ms[:, 0].mean() * 1e-3) / 1e9),
         "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
         "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
-        "device_copy_gbs_same_bytes": copy_gbs,
+        "reorder_gbs_cold": reorder_cold,
+        "device_copy_gbs_same_bytes": {"cold": copy_cold, "warm": copy_warm},
         "gpu_kernel_ms_per_step": gpu_step_ms,
         # attention reading the all-gathered (rank-major) K/V through the inverse partition map: partition +
         # plan + fwd + bwd per share, no restoration pass; dK/dV come out in the gathered order

@@ -37,6 +37,10 @@ constexpr int kDqRowBlocks = CPTHD_DQ_ROW_BLOCKS;   // 32-row blocks per wave (1
 #define CPTHD_DKDV_SPLIT 2
 #endif
 constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-group pairs splitting dK/dV columns
+#ifndef CPTHD_DQ_SPLIT
+#define CPTHD_DQ_SPLIT 2   // work-groups per query tile in the dQ pass (two 4-wave groups per CU)
+#endif
+constexpr int kDqSplit = CPTHD_DQ_SPLIT;
 #ifndef CPTHD_DQ_PIPE
 #define CPTHD_DQ_PIPE 1   // read-ahead scheduling hints in the dQ pass
 #endif
@@ -51,11 +55,12 @@ constexpr int kDkdvSplit = CPTHD_DKDV_SPLIT;   // 1: 4 waves; 2: 8 waves, key-gr
 // pass 1: delta and dQ over the query tiles
 // ---------------------------------------------------------------------------
 template <int DP, int QB, bool AG>
-__global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_EU(kQWaves / QB * kQMinBlocks / 4) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSplit)
+    CPTHD_WAVES_PER_EU(kQWaves / QB * kQMinBlocks / 4) void attn_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const uint16_t* __restrict__ o, const uint16_t* __restrict__ dout, const float* __restrict__ lse,
     float* __restrict__ dq, char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
-  constexpr int NW = kQWaves / QB;  // waves, QB 32-row blocks each
+  constexpr int NW = kQWaves / QB / kDqSplit;  // waves, QB 32-row blocks each
   using KT = LdsTile<DP, true>;    // K: read by rows (S^T operand) and transposed (K^T operand of dQ^T)
   using VT = LdsTile<DP, true>;    // V: read by rows (dP^T operand), in K's row order (one loader for both)
   __shared__ __align__(16) uint16_t K0[KT::ELEMS], K1[KT::ELEMS];
@@ -66,7 +71,10 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
     return;
   }
-  const int tile = blockIdx.x / prm.Hkv, kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
+  // kDqSplit work-groups per query tile, each with kRowsPerWG / kDqSplit of its rows; the kv head stays
+  // blockIdx mod Hkv
+  const int kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
+  const int tile = blockIdx.x / (prm.Hkv * kDqSplit), part = (blockIdx.x / prm.Hkv) % kDqSplit;
   if (tile >= hdr->n_qtiles) return;
   QTile t;
   if (!load_qtile(ws, lay, tile, prm, t)) {
@@ -109,7 +117,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   bf16x8 qf[QB][DP / 16], df[QB][DP / 16];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const int m = wave * 32 * QB + 32 * qb + l32;
+    const int m = part * (kRowsPerWG / kDqSplit) + wave * 32 * QB + 32 * qb + l32;
     const int tt = m / G, g = m - tt * G;
     row_in[qb] = m < bm * G && tt < t.ntok;
     p_q[qb] = t.p0 + tt;
@@ -460,7 +468,8 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* o
                       const AttnParams& prm, int32_t* status, unsigned grid_q, unsigned grid_kv,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kDqRowBlocks;
-  int e = launch(attn_bwd_dq_kernel<DP, QB, AG>, dim3(grid_q), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
+  int e = launch(attn_bwd_dq_kernel<DP, QB, AG>, dim3(grid_q * kDqSplit), dim3(64 * (kQWaves / QB / kDqSplit)), 0,
+                 stream, ev, nev, 0,
                  (const uint16_t*)q,
                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse, dq, ws,
                  lay, prm, status);
