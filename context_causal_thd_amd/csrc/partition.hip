@@ -74,9 +74,24 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
   }
 }
 
-// Restoration: each wave copies whole token rows.  Row p of the output (physical
-// order) comes from gathered row s*S + (local index of p on its owner s).
-constexpr int kReorderRowsPerWave = 4;
+// Restoration: each wave copies kReorderRowsPerWave whole token rows.  Row p of
+// the output (physical order) comes from gathered row s*S + (local index of p on
+// its owner s).  A lane issues the loads of kReorderChunks 16-byte pieces of
+// every row before any store, so a wave keeps rows x chunks x 1 KiB in flight.
+#ifndef CPTHD_REORDER_ROWS
+#define CPTHD_REORDER_ROWS 2
+#endif
+#ifndef CPTHD_REORDER_CHUNKS
+#define CPTHD_REORDER_CHUNKS 2
+#endif
+constexpr int kReorderRowsPerWave = CPTHD_REORDER_ROWS;
+#ifndef CPTHD_REORDER_LOAD
+#define CPTHD_REORDER_LOAD __builtin_nontemporal_load   // streamed once: no cache retention
+#endif
+#ifndef CPTHD_REORDER_STORE
+#define CPTHD_REORDER_STORE __builtin_nontemporal_store
+#endif
+constexpr int kReorderChunks = CPTHD_REORDER_CHUNKS;
 
 __device__ inline int64_t gathered_row_of(const int32_t* cu, int B, int S, int cp, int strategy, int p) {
   if (strategy == kContig) return p;
@@ -100,29 +115,41 @@ __global__ __launch_bounds__(256) void reorder_kernel(const char* __restrict__ k
                                                       char* __restrict__ ko, char* __restrict__ vo,
                                                       int64_t row_bytes, const int32_t* __restrict__ cu, int B,
                                                       int T, int cp, int strategy, int32_t* status) {
+  constexpr int R = kReorderRowsPerWave, U = kReorderChunks;
   if (blockIdx.y == 0) validate_cu_padded(cu, B, T, cp, strategy, status);
   const char* src = blockIdx.y == 0 ? kg : vg;
   char* dst = blockIdx.y == 0 ? ko : vo;
   const int S = T / cp;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * kReorderRowsPerWave;
-  const int64_t n16 = row_bytes / 16;
-  int64_t g[kReorderRowsPerWave];
-  for (int rr = 0; rr < kReorderRowsPerWave; ++rr) {
+  const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R;
+  const int nrows = (int)min((int64_t)R, (int64_t)T - row0);
+  if (nrows <= 0) return;
+  int64_t g[R];
+#pragma unroll
+  for (int rr = 0; rr < R; ++rr) {
     const int64_t p = min(row0 + rr, (int64_t)T - 1);
     const int64_t gr = gathered_row_of(cu, B, S, cp, strategy, (int)p);
     g[rr] = __builtin_amdgcn_readfirstlane((int)min(max(gr, (int64_t)0), (int64_t)T - 1));
   }
-  const int nrows = (int)min((int64_t)kReorderRowsPerWave, (int64_t)T - row0);
-  if (nrows <= 0) return;
-  for (int64_t e = lane; e < n16; e += 64) {
-    u32x4 val[kReorderRowsPerWave];
+  const int64_t n16 = row_bytes / 16;
+  for (int64_t e0 = lane; e0 < n16; e0 += 64 * U) {
+    u32x4 val[R][U];
 #pragma unroll
-    for (int rr = 0; rr < kReorderRowsPerWave; ++rr)
-      if (rr < nrows) val[rr] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + g[rr] * row_bytes) + e);
+    for (int rr = 0; rr < R; ++rr)
 #pragma unroll
-    for (int rr = 0; rr < kReorderRowsPerWave; ++rr)
-      if (rr < nrows) __builtin_nontemporal_store(val[rr], reinterpret_cast<u32x4*>(dst + (row0 + rr) * row_bytes) + e);
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 64 * u;
+        if (rr < nrows && e < n16)
+          val[rr][u] = CPTHD_REORDER_LOAD(reinterpret_cast<const u32x4*>(src + g[rr] * row_bytes) + e);
+      }
+#pragma unroll
+    for (int rr = 0; rr < R; ++rr)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t e = e0 + 64 * u;
+        if (rr < nrows && e < n16)
+          CPTHD_REORDER_STORE(val[rr][u], reinterpret_cast<u32x4*>(dst + (row0 + rr) * row_bytes) + e);
+      }
   }
 }
 
