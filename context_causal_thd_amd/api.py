@@ -44,6 +44,16 @@ def _p(t):
     return t.data_ptr()
 
 
+def _need(t, name, dtype, rows, tail):
+    """t must be a `dtype` tensor of shape [>= rows, *tail]: the kernels touch rows [0, rows) and trust the row
+    layout, so a wrong dtype or shape is refused here instead of being read out of bounds."""
+    if t.dtype != dtype:
+        raise ValueError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != 1 + len(tail) or tuple(t.shape[1:]) != tuple(tail) or t.shape[0] < rows:
+        want = ", ".join([f">= {rows}"] + [str(x) for x in tail])
+        raise ValueError(f"{name}: expected shape [{want}], got {tuple(t.shape)}")
+
+
 def _s(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -196,18 +206,22 @@ def check_dev_status(dev_status) -> None:
 
 def partition_indices(cu_seqlens_padded, total_tokens, cp_size, rank, strategy, out=None, dev_status=None):
     """int32 [T/cp_size] physical token indices of ``rank`` (device tensor)."""
+    _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 2, ())
     num_docs = cu_seqlens_padded.numel() - 1
     if out is None:
         out = torch.empty(total_tokens // cp_size, dtype=torch.int32, device=cu_seqlens_padded.device)
+    _need(out, "out", torch.int32, total_tokens // cp_size, ())
     cpthd_partition_indices(cu_seqlens_padded, num_docs, total_tokens, cp_size, rank, strategy, out, dev_status)
     return out
 
 
 def gather_rows(src, index, out=None, dev_status=None):
     """out[j] = src[index[j]] along the first dimension (any dtype)."""
+    _need(index, "index", torch.int32, 0, ())
     n = index.numel()
     if out is None:
         out = torch.empty((n,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    _need(out, "out", src.dtype, n, tuple(src.shape[1:]))
     row_bytes = (src[0].numel() if src.dim() > 1 else 1) * src.element_size()
     cpthd_gather_rows(src, src.shape[0], row_bytes, index, n, out, dev_status)
     return out
@@ -223,10 +237,16 @@ def get_batch_on_this_cp_rank(cu_seqlens_padded, total_tokens, cp_size, rank, st
 def reorder_kv(k_gathered, v_gathered, cu_seqlens_padded, total_tokens, cp_size, strategy, k_out=None, v_out=None,
                dev_status=None):
     """Physical-order K and V from the rank-major all-gathered buffers."""
+    tail = tuple(k_gathered.shape[1:])
+    _need(k_gathered, "k_gathered", k_gathered.dtype, total_tokens, tail)
+    _need(v_gathered, "v_gathered", k_gathered.dtype, total_tokens, tail)
+    _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 2, ())
     if k_out is None:
         k_out = torch.empty_like(k_gathered)
     if v_out is None:
         v_out = torch.empty_like(v_gathered)
+    _need(k_out, "k_out", k_gathered.dtype, total_tokens, tail)
+    _need(v_out, "v_out", k_gathered.dtype, total_tokens, tail)
     row_bytes = k_gathered[0].numel() * k_gathered.element_size()
     cpthd_reorder_kv(k_gathered, v_gathered, k_out, v_out, row_bytes, cu_seqlens_padded,
                      cu_seqlens_padded.numel() - 1, total_tokens, k_gathered.shape[0], cp_size, strategy, dev_status)
@@ -248,6 +268,8 @@ class AttnPlan:
         self.built = None
 
     def build(self, cu_seqlens, cu_seqlens_padded, total_tokens, rank, strategy, dev_status=None):
+        _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 2, ())
+        _need(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens_padded.numel(), ())
         num_docs = cu_seqlens_padded.numel() - 1
         if num_docs > self.max_docs:
             raise ValueError("more documents than the workspace was sized for")
@@ -268,13 +290,20 @@ def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, ls
              events=None, kv_allgathered=False):
     """O and LSE of the rank's query rows.  ``kv_allgathered``: k and v are in rank-major all-gathered order
     (as an all-gather of the ranks' local K/V leaves them) instead of physical order."""
-    S = plan.built["total_tokens"] // plan.cp_size
+    T = plan.built["total_tokens"]
+    S = T // plan.cp_size
+    bf = torch.bfloat16
+    _need(q_local, "q_local", bf, S, (plan.Hq, plan.D))
+    _need(k, "k", bf, T, (plan.Hkv, plan.D))
+    _need(v, "v", bf, T, (plan.Hkv, plan.D))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
     if o_local is None:
         o_local = torch.empty((S, plan.Hq, plan.D), dtype=torch.bfloat16, device=q_local.device)
     if lse_local is None:
         lse_local = torch.empty((S, plan.Hq), dtype=torch.float32, device=q_local.device)
+    _need(o_local, "o_local", bf, S, (plan.Hq, plan.D))
+    _need(lse_local, "lse_local", torch.float32, S, (plan.Hq,))
     call = cpthd_attn_fwd_allgathered if kv_allgathered else cpthd_attn_fwd
     call(q_local, k, v, *plan._args(), softmax_scale, 1, -1, 0, o_local, lse_local, plan.workspace, dev_status,
          events=events)
@@ -285,6 +314,14 @@ def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softma
              dk=None, dv=None, dev_status=None, events=None, kv_allgathered=False):
     """dQ of the rank's rows and its partial dK, dV (fp32).  With ``kv_allgathered`` k, v and the returned
     dk, dv are in rank-major all-gathered order."""
+    T = plan.built["total_tokens"]
+    S = T // plan.cp_size
+    bf, f32 = torch.bfloat16, torch.float32
+    for t, name in ((q_local, "q_local"), (o_local, "o_local"), (do_local, "do_local")):
+        _need(t, name, bf, S, (plan.Hq, plan.D))
+    _need(k, "k", bf, T, (plan.Hkv, plan.D))
+    _need(v, "v", bf, T, (plan.Hkv, plan.D))
+    _need(lse_local, "lse_local", f32, S, (plan.Hq,))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
     if dq_local is None:
@@ -293,6 +330,9 @@ def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softma
         dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
     if dv is None:
         dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+    _need(dq_local, "dq_local", f32, S, (plan.Hq, plan.D))
+    _need(dk, "dk", f32, T, (plan.Hkv, plan.D))
+    _need(dv, "dv", f32, T, (plan.Hkv, plan.D))
     call = cpthd_attn_bwd_allgathered if kv_allgathered else cpthd_attn_bwd
     call(q_local, k, v, o_local, do_local, lse_local, *plan._args(), softmax_scale, 1, -1, 0, dq_local, dk, dv,
          plan.workspace, dev_status, events=events)
