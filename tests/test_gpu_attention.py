@@ -319,3 +319,27 @@ def test_plan_rejects_documents_of_2gib_kv():
         plan.build(cu, cu, T, 0, 1, st)
         torch.cuda.synchronize()
         assert int(st.item()) == bit, lengths
+
+
+@pytest.mark.parametrize("allgathered", [False, True])
+def test_autograd_wrapper_matches_entry_points(allgathered):
+    """cpthd.attention (autograd) gives the entry points' O bit for bit, and gradients equal to the fp32
+    dQ/dK/dV cast to the inputs' dtype; a plan rebuilt for another layout before backward is refused."""
+    wl = W.small_random(5, 2, 0, max_docs=4, max_len=300, Hq=8, Hkv=2, D=64, bf16=True, qkv_scale=0.5,
+                        do_scale=1.0)
+    S, T = wl.T // wl.cp, wl.T
+    sh = Share(wl, 0, 1, allgathered=allgathered)
+    q = sh.q[:S].clone().requires_grad_()
+    k = sh.k[:T].clone().requires_grad_()
+    v = sh.v[:T].clone().requires_grad_()
+    o = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
+    assert torch.equal(o.detach(), sh.o[:S])
+    o.backward(sh.do[:S])
+    torch.cuda.synchronize()
+    assert torch.equal(q.grad, sh.dq[:S].to(torch.bfloat16))
+    assert torch.equal(k.grad, sh.dk[:T].to(torch.bfloat16))
+    assert torch.equal(v.grad, sh.dv[:T].to(torch.bfloat16))
+    o2 = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
+    sh.plan.build(sh.cu_a, sh.cu_p, T, 0, 0, sh.st)          # another rank's layout
+    with pytest.raises(RuntimeError, match="rebuilt"):
+        o2.backward(sh.do[:S])
