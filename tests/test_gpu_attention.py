@@ -343,3 +343,22 @@ def test_autograd_wrapper_matches_entry_points(allgathered):
     sh.plan.build(sh.cu_a, sh.cu_p, T, 0, 0, sh.st)          # another rank's layout
     with pytest.raises(RuntimeError, match="rebuilt"):
         o2.backward(sh.do[:S])
+
+
+# dK/dV sum G heads of P * dO, so their magnitude (and the absolute rounding of the bf16 P operand) grows
+# like sqrt(G); dO is scaled by sqrt(4 / G) to keep dK/dV in the range of the measured workloads (G = 4),
+# where the absolute bound applies.  Unscaled, G = 64 stays at relative L2 ~1e-3.
+WIDE_GQA = [W.small_random(900 + i, cp, s, max_docs=4, max_len=200, Hq=hq, Hkv=hkv, D=d, bf16=True, qkv_scale=0.5,
+                           do_scale=(4.0 / (hq // hkv)) ** 0.5)
+            for i, (cp, s, hq, hkv, d) in enumerate([(2, 0, 64, 1, 64), (3, 1, 64, 1, 128), (2, 2, 32, 1, 32),
+                                                    (4, 0, 64, 2, 16), (1, 0, 32, 1, 128)])]
+
+
+@pytest.mark.parametrize("wl", WIDE_GQA, ids=lambda w: f"{w.name}-D{w.D}-h{w.Hq}x{w.Hkv}-cp{w.cp}-s{w.strategies[0]}")
+@pytest.mark.parametrize("allgathered", [False, True])
+def test_wide_gqa_groups(wl, allgathered):
+    """32 and 64 q heads per kv head: 8 or 4 tokens per query tile, one or two tokens per key-tile chunk."""
+    s = wl.strategies[0]
+    for r in range(wl.cp):
+        log(f"{wl.name} G={wl.Hq // wl.Hkv} allgathered={allgathered} r={r}")
+        Share(wl, s, r, allgathered=allgathered).compare()
