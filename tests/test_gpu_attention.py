@@ -362,3 +362,40 @@ def test_wide_gqa_groups(wl, allgathered):
     for r in range(wl.cp):
         log(f"{wl.name} G={wl.Hq // wl.Hkv} allgathered={allgathered} r={r}")
         Share(wl, s, r, allgathered=allgathered).compare()
+
+
+def test_strategies_agree_on_every_row_at_config3():
+    """Full-size property, every row: the three strategies compute the same function of the same tokens, so
+    all ranks' O, LSE, dQ scattered to physical rows, and dK, dV summed over ranks, agree between strategies
+    (to rounding: the tiles, and so the accumulation order, differ)."""
+    wl = W.config3()
+    T, cp = wl.T, wl.cp
+    res = {}
+    for s in (0, 1, 2):
+        o = torch.zeros((T, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
+        lse = torch.zeros((T, wl.Hq), dtype=torch.float32, device="cuda")
+        dq = torch.zeros((T, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
+        dk = torch.zeros((T, wl.Hkv, wl.D), dtype=torch.float32, device="cuda")
+        dv = torch.zeros((T, wl.Hkv, wl.D), dtype=torch.float32, device="cuda")
+        for r in range(cp):
+            log(f"config3 s={s} r={r}")
+            sh = Share(wl, s, r)
+            idx = torch.from_numpy(sh.idx.astype(np.int64)).to("cuda")
+            S = T // cp
+            o[idx] = sh.o[:S].float()
+            lse[idx] = sh.lse[:S]
+            dq[idx] = sh.dq[:S]
+            dk += sh.dk[:T]
+            dv += sh.dv[:T]
+            del sh
+        res[s] = (o, lse, dq, dk, dv)
+    _, _, valid_tok = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    vt = torch.from_numpy(valid_tok).to("cuda")
+    for s in (1, 2):
+        for name, a, b, tol in zip(("O", "LSE", "dQ", "dK", "dV"), res[0], res[s], (2e-2, 1e-4, 2e-2, 2e-2, 2e-2)):
+            same_pads = torch.equal(a[~vt], b[~vt])
+            err = float((a[vt] - b[vt]).abs().max())
+            rel = float((a[vt] - b[vt]).norm() / a[vt].norm())
+            log(f"    strategy 0 vs {s} {name}: max_abs={err:.3e} rel_l2={rel:.3e}")
+            assert same_pads, f"{name}: pad rows differ between strategies"
+            assert err <= tol and rel <= 5e-3, (name, s, err, rel)
