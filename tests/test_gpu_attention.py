@@ -22,7 +22,8 @@ cpthd = pytest.importorskip("context_causal_thd_amd")
 class Share:
     """One rank's share on the GPU: plan, forward and (optionally) backward."""
 
-    def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False, allgathered=False):
+    def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False, allgathered=False,
+                 kv=None):
         self.wl, self.s, self.r = wl, strategy, rank
         T, cp = wl.T, wl.cp
         S = T // cp
@@ -30,7 +31,7 @@ class Share:
         capS = cap // cp
         self.idx = oracle.partition_indices(wl.cu_padded, cp, rank, strategy)
         q = wl.q(self.idx)
-        k, v = wl.k(), wl.v()
+        k, v = kv if kv is not None else (wl.k(), wl.v())   # kv: the workload's K, V, generated once by the caller
         self.q_np, self.k_np, self.v_np = q, k, v
         # rank-major all-gathered K/V (the simulated all-gather of every rank's local rows)
         self.allgathered = allgathered
@@ -364,22 +365,25 @@ def test_wide_gqa_groups(wl, allgathered):
         Share(wl, s, r, allgathered=allgathered).compare()
 
 
-def test_strategies_agree_on_every_row_at_config3():
-    """Full-size property, every row: the three strategies compute the same function of the same tokens, so
-    all ranks' O, LSE, dQ scattered to physical rows, and dK, dV summed over ranks, agree between strategies
-    (to rounding: the tiles, and so the accumulation order, differ)."""
-    wl = W.config3()
+@pytest.mark.parametrize("name", ["config3", "config4"])
+def test_strategies_agree_on_every_row(name):
+    """Full-size property, every row: the strategies compute the same function of the same tokens, so all
+    ranks' O, LSE, dQ scattered to physical rows, and dK, dV summed over ranks, agree between strategies (to
+    rounding: the tiles, and so the accumulation order, differ).  Config 4's documents rule out DualChunkSwap."""
+    wl = W.config3() if name == "config3" else W.config4()
+    strategies = (0, 1, 2) if name == "config3" else (1, 2)
     T, cp = wl.T, wl.cp
+    kv = (wl.k(), wl.v())
     res = {}
-    for s in (0, 1, 2):
+    for s in strategies:
         o = torch.zeros((T, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
         lse = torch.zeros((T, wl.Hq), dtype=torch.float32, device="cuda")
         dq = torch.zeros((T, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
         dk = torch.zeros((T, wl.Hkv, wl.D), dtype=torch.float32, device="cuda")
         dv = torch.zeros((T, wl.Hkv, wl.D), dtype=torch.float32, device="cuda")
         for r in range(cp):
-            log(f"config3 s={s} r={r}")
-            sh = Share(wl, s, r)
+            log(f"{name} s={s} r={r}")
+            sh = Share(wl, s, r, kv=kv)
             idx = torch.from_numpy(sh.idx.astype(np.int64)).to("cuda")
             S = T // cp
             o[idx] = sh.o[:S].float()
@@ -391,11 +395,12 @@ def test_strategies_agree_on_every_row_at_config3():
         res[s] = (o, lse, dq, dk, dv)
     _, _, valid_tok = oracle.token_map(wl.cu_padded, wl.cu_actual)
     vt = torch.from_numpy(valid_tok).to("cuda")
-    for s in (1, 2):
-        for name, a, b, tol in zip(("O", "LSE", "dQ", "dK", "dV"), res[0], res[s], (2e-2, 1e-4, 2e-2, 2e-2, 2e-2)):
+    s0 = strategies[0]
+    for s in strategies[1:]:
+        for t, a, b, tol in zip(("O", "LSE", "dQ", "dK", "dV"), res[s0], res[s], (2e-2, 1e-4, 2e-2, 2e-2, 2e-2)):
             same_pads = torch.equal(a[~vt], b[~vt])
             err = float((a[vt] - b[vt]).abs().max())
             rel = float((a[vt] - b[vt]).norm() / a[vt].norm())
-            log(f"    strategy 0 vs {s} {name}: max_abs={err:.3e} rel_l2={rel:.3e}")
-            assert same_pads, f"{name}: pad rows differ between strategies"
-            assert err <= tol and rel <= 5e-3, (name, s, err, rel)
+            log(f"    strategy {s0} vs {s} {t}: max_abs={err:.3e} rel_l2={rel:.3e}")
+            assert same_pads, f"{t}: pad rows differ between strategies"
+            assert err <= tol and rel <= 5e-3, (t, s, err, rel)
