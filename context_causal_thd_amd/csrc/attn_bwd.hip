@@ -514,8 +514,9 @@ static int attn_bwd_entry(const void* q_local, const void* k, const void* v, con
   }
   prm.scale = softmax_scale;
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const unsigned gq = qtile_grid(prm);
-  const unsigned gkv = (unsigned)(((total_tokens + kKeysPerWG - 1) / kKeysPerWG + num_docs) * num_kv_heads);
+  const int64_t gq = qtile_grid(prm);
+  const int64_t gkv = ((total_tokens + kKeysPerWG - 1) / kKeysPerWG + num_docs) * (int64_t)num_kv_heads;
+  if (gq * kDqSplit > INT32_MAX || gkv > INT32_MAX) return CPTHD_ERR_TOKENS;   // more work-groups than one launch takes
   char* ws = (char*)workspace;
   return ag ? dispatch_bwd<true>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm,
                                  dev_status, gq, gkv, stream, events, n_events)

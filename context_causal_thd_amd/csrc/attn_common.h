@@ -260,6 +260,6 @@ __device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buff
 int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32_t strategy, int32_t num_docs,
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t wl, int32_t wr, const void* ws,
                     size_t ws_bytes, PlanLayout& lay, AttnParams& prm);
-unsigned qtile_grid(const AttnParams& prm);
+int64_t qtile_grid(const AttnParams& prm);
 
 }  // namespace cpthd

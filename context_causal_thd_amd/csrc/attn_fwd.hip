@@ -312,10 +312,10 @@ int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32
 
 // Work-groups for the query tiles: an upper bound from the active S (the plan
 // holds the exact count; surplus work-groups exit at once).
-unsigned qtile_grid(const AttnParams& prm) {
+int64_t qtile_grid(const AttnParams& prm) {
   const int64_t bm = tokens_per_qtile(prm.G);
   const int64_t seg = (prm.strategy == CPTHD_NO_LOAD_BALANCE ? 1 : 2) * (int64_t)prm.num_docs;
-  return (unsigned)(((prm.S + bm - 1) / bm + seg) * prm.Hkv);
+  return ((prm.S + bm - 1) / bm + seg) * prm.Hkv;
 }
 
 }  // namespace cpthd
@@ -342,7 +342,8 @@ static int attn_fwd_entry(const void* q_local, const void* k, const void* v, int
   }
   prm.scale = softmax_scale;
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const unsigned grid = qtile_grid(prm);
+  const int64_t grid = qtile_grid(prm);
+  if (grid > INT32_MAX) return CPTHD_ERR_TOKENS;   // more work-groups than one launch takes
   const char* ws = (const char*)workspace;
   return ag ? dispatch_fwd<true>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events,
                                  n_events)
