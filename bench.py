@@ -78,6 +78,49 @@ def measured_traffic(kernel):
     return None if v is None else v["fetch_bytes_per_launch"] + v["write_bytes_per_launch"]
 
 
+class ClockSampler:
+    """Samples the GPU shader clock (the starred level of the driver's pp_dpm_sclk file) every 2 ms from a
+    background thread while the timed steps run; reads a file, starts nothing."""
+
+    def __init__(self):
+        import glob
+        import threading
+        self.paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        import re
+        while not self._stop.is_set():
+            for path in self.paths:
+                try:
+                    for line in open(path):
+                        if line.rstrip().endswith("*"):
+                            m = re.search(r"(\d+)\s*Mhz", line, flags=re.I)
+                            if m:
+                                self.samples.append(int(m.group(1)))
+                except OSError:
+                    return
+            time.sleep(0.002)
+
+    def __enter__(self):
+        if self.paths:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        return {"median_mhz": float(np.median(self.samples)), "min_mhz": int(min(self.samples)),
+                "samples": len(self.samples), "source": "pp_dpm_sclk current level, sampled every 2 ms"}
+
+
 def useful_pairs(idx, cu_p, cu_a):
     """Allowed (query, key) pairs for the rank's query rows: sum over actual rows of (position + 1)."""
     cu_p = cu_p.astype(np.int64)
@@ -215,11 +258,12 @@ def main():
 
     events = [make_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k_step in range(args.steps):
-        step(events[k_step])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    with ClockSampler() as clock:
+        t0 = time.perf_counter()
+        for k_step in range(args.steps):
+            step(events[k_step])
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     cpthd.check_dev_status(status)
     log(f"timed {args.steps} steps in {elapsed:.3f} s")
     acc = np.zeros((len(shares), n_kernels))
@@ -343,6 +387,7 @@ def main():
         "reorder_gbs_cold": reorder_cold,
         "device_copy_gbs_same_bytes": {"cold": copy_cold, "warm": copy_warm},
         "gpu_kernel_ms_per_step": gpu_step_ms,
+        "shader_clock_during_timed_steps": clock.summary(),
         # attention reading the all-gathered (rank-major) K/V through the inverse partition map: partition +
         # plan + fwd + bwd per share, no restoration pass; dK/dV come out in the gathered order
         "allgathered_path": None if ag is None else {
