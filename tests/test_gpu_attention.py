@@ -404,3 +404,38 @@ def test_strategies_agree_on_every_row(name):
             log(f"    strategy {s0} vs {s} {t}: max_abs={err:.3e} rel_l2={rel:.3e}")
             assert same_pads, f"{t}: pad rows differ between strategies"
             assert err <= tol and rel <= 5e-3, (t, s, err, rel)
+
+
+def test_graph_replays_match_eager():
+    """The plan, forward and backward launches captured in a HIP graph (torch.cuda.CUDAGraph) replay to the
+    eager results bit for bit, several times, with eager work between the replays."""
+    wl = W.small_random(77, 2, 0, max_docs=5, max_len=400, Hq=8, Hkv=2, D=128, bf16=True, qkv_scale=0.5,
+                        do_scale=1.0)
+    sh = Share(wl, 0, 1)                          # eager run: plan, forward, backward
+    S, T = wl.T // wl.cp, wl.T
+    outs = dict(o=torch.empty_like(sh.o), lse=torch.empty_like(sh.lse), dq=torch.empty_like(sh.dq),
+                dk=torch.empty_like(sh.dk), dv=torch.empty_like(sh.dv))
+    plan = cpthd.AttnPlan(T, wl.cp, wl.Hq, wl.Hkv, wl.D, max_docs=wl.num_docs)
+    st = status_dev()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                 # warm-up launch outside the capture
+        plan.build(sh.cu_a, sh.cu_p, T, 1, 0, st)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        plan.build(sh.cu_a, sh.cu_p, T, 1, 0, st)
+        cpthd.attn_fwd(sh.q, sh.k, sh.v, plan, wl.softmax_scale, outs["o"], outs["lse"], st)
+        cpthd.attn_bwd(sh.q, sh.k, sh.v, outs["o"], sh.do, outs["lse"], plan, wl.softmax_scale, outs["dq"],
+                       outs["dk"], outs["dv"], st)
+    for rep in range(3):
+        for t in outs.values():
+            t.fill_(float("nan"))                 # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        assert torch.equal(outs["o"][:S], sh.o[:S]) and torch.equal(outs["lse"][:S], sh.lse[:S]), rep
+        assert torch.equal(outs["dq"][:S], sh.dq[:S]), rep
+        assert torch.equal(outs["dk"][:T], sh.dk[:T]) and torch.equal(outs["dv"][:T], sh.dv[:T]), rep
