@@ -81,10 +81,10 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
     if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
     return;
   }
-  float* delta = reinterpret_cast<float*>(ws + lay.delta);
+  float* ndelta = reinterpret_cast<float*>(ws + lay.delta);   // -delta per row, for the key-tile pass
   float* lse2w = reinterpret_cast<float*>(ws + lay.lse2);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
 
@@ -145,16 +145,19 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
     dlt[qb] = sum_xor32(dpart);
     lse2[qb] = valid[qb] ? lse[qrow[qb]] * 1.4426950408889634f : INFINITY;
     if (row_in[qb] && h == 0) {
-      delta[qrow[qb]] = valid[qb] ? dlt[qb] : 0.f;
+      ndelta[qrow[qb]] = valid[qb] ? -dlt[qb] : 0.f;
       lse2w[qrow[qb]] = valid[qb] ? lse2[qb] : 0.f;
     }
   }
 
-  f32x16 acc[QB][DP / 32];
+  f32x16 acc[QB][DP / 32], ndl[QB];   // ndl: -delta in every entry, the start of each dP^T product
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < QB; ++qb) {
 #pragma unroll
     for (int db = 0; db < DP / 32; ++db) acc[qb][db] = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ndl[qb][r] = -dlt[qb];
+  }
 
   lds_loads_barrier();
 
@@ -170,7 +173,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         sc[qb] = f32x16{};
-        dp[qb] = f32x16{};
+        dp[qb] = ndl[qb];   // dP^T - delta accumulates in place
       }
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
@@ -185,18 +188,26 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
 #if CPTHD_DQ_PIPE
       if constexpr (QB == 1) pipeline_reads_mfma<2 * (DP / 16), 4>();
 #endif
+      // dS = P (dP - delta); the causal test only on steps that reach the diagonal (a uniform branch)
+      auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const int lim = p_q[qb] - kb - 32 * b - 4 * h;   // key offset 8(r/4) + r%4 allowed iff <= lim
+        for (int qb = 0; qb < QB; ++qb) {
+          const int lim = p_q[qb] - kb - 32 * b - 4 * h;   // key offset 8(r/4) + r%4 allowed iff <= lim
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pv = exp2_fast(fmaf(sc[qb][r], sl2, -lse2[qb]));
-          if (need_mask && 8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
-          sc[qb][r] = pv * (dp[qb][r] - dlt[qb]);
+          for (int r = 0; r < 16; ++r) {
+            float pv = exp2_fast(fmaf(sc[qb][r], sl2, -lse2[qb]));
+            if constexpr (decltype(masked)::value)
+              if (8 * (r >> 2) + (r & 3) > lim) pv = 0.f;
+            sc[qb][r] = pv * dp[qb][r];
+          }
+          dsb[qb][2 * b] = acc_to_bf16(sc[qb], 0);
+          dsb[qb][2 * b + 1] = acc_to_bf16(sc[qb], 8);
         }
-        dsb[qb][2 * b] = acc_to_bf16(sc[qb], 0);
-        dsb[qb][2 * b + 1] = acc_to_bf16(sc[qb], 8);
-      }
+      };
+      if (need_mask)
+        probs(std::true_type{});
+      else
+        probs(std::false_type{});
     }
 #pragma unroll
     for (int db = 0; db < DP / 32; ++db)
@@ -238,10 +249,10 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
 // pass 2: dK and dV over the key tiles
 // ---------------------------------------------------------------------------
 // Direct loads of one step's Q and dO rows (local rows from `base` / Hq, ntok
-// tokens) and of their LSE*log2(e) and delta values into the given buffers.
+// tokens) and of their LSE*log2(e) and -delta values into the given buffers.
 template <int DP, int NW>
 __device__ inline void issue_q_chunk(const TileLoader<DP, true, NW>& qld, const uint16_t* q, const uint16_t* dout,
-                                     const float* lse2w, const float* delta, int64_t base, int ntok,
+                                     const float* lse2w, const float* ndelta, int64_t base, int ntok,
                                      uint32_t tok_bytes, int Hq, int D, uint32_t ld_off, int wave, uint16_t* Qn,
                                      uint16_t* On, float* Ln, float* En) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource builtins: device pass only
@@ -249,7 +260,7 @@ __device__ inline void issue_q_chunk(const TileLoader<DP, true, NW>& qld, const 
   qld.issue(make_rsrc(q + base * D, nrec), Qn, 0, wave);
   qld.issue(make_rsrc(dout + base * D, nrec), On, 0, wave);
   if (wave == 0) lds_load_dword(make_rsrc(lse2w + base, (uint32_t)ntok * Hq * 4), Ln, ld_off);
-  if (wave == 1) lds_load_dword(make_rsrc(delta + base, (uint32_t)ntok * Hq * 4), En, ld_off);
+  if (wave == 1) lds_load_dword(make_rsrc(ndelta + base, (uint32_t)ntok * Hq * 4), En, ld_off);
 #endif
 }
 
@@ -267,7 +278,7 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
   using QT = LdsTile<DP, true>;   // Q and dO: read by rows (S, dP operands) and transposed (dK, dV operands)
   __shared__ __align__(16) uint16_t Q0[QT::ELEMS], Q1[QT::ELEMS];
   __shared__ __align__(16) uint16_t O0[QT::ELEMS], O1[QT::ELEMS];
-  __shared__ __align__(16) float L0[kQChunk], L1[kQChunk], E0[kQChunk], E1[kQChunk];   // LSE*log2(e), delta
+  __shared__ __align__(16) float L0[kQChunk], L1[kQChunk], E0[kQChunk], E1[kQChunk];   // LSE*log2(e), -delta
   __shared__ __align__(16) bf16x8 X[SD == 2 ? 4 * 2 * 4 * 64 : 1];   // [key group][query block][P0,P1,dS0,dS1][lane]
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
@@ -284,10 +295,10 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
     return;
   }
   const DocSeg ds = reinterpret_cast<const DocSeg*>(ws + lay.docs)[kt.doc];
-  const float* delta = reinterpret_cast<const float*>(ws + lay.delta);
+  const float* ndelta = reinterpret_cast<const float*>(ws + lay.delta);
   const float* lse2w = reinterpret_cast<const float*>(ws + lay.lse2);
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv, S = prm.S;
   const int kw = wave & 3, dh = wave >> 2;
   const int key = kt.k0 + kw * 32 + l32;            // this lane's key (B operand column)
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
     ntok = min(tpc, phi[si] - c0);
   };
 
-  // Q / dO rows of a chunk: tile row r = token r/G, head r%G; LSE / delta: one float per row
+  // Q / dO rows of a chunk: tile row r = token r/G, head r%G; LSE / -delta: one float per row
   const uint32_t tok_bytes = (uint32_t)Hq * D * 2;
   TileLoader<DP, true, NW> qld;
   auto qrowoff = [&](int r) __attribute__((always_inline)) -> int64_t {
@@ -341,7 +352,7 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
   auto issue = [&](int i, uint16_t* Qn, uint16_t* On, float* Ln, float* En) __attribute__((always_inline)) {
     int c0, l0, ntok;
     chunk_at(i, c0, l0, ntok);
-    issue_q_chunk<DP, NW>(qld, q, dout, lse2w, delta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn,
+    issue_q_chunk<DP, NW>(qld, q, dout, lse2w, ndelta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn,
                           On, Ln, En);
   };
   if (nchunks > 0) issue(0, Q0, O0, L0, E0);
@@ -378,29 +389,44 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
     const int thr = (key - c0) * G - 4 * h;
     // P and dS of one 32-row query block as bf16 operands (key as the lane index)
     auto scores = [&](int qb, bf16x8 (&pd)[4]) {
-      f32x16 sc = f32x16{}, dp = f32x16{};
+      // dP starts from the rows' -delta, so it accumulates dP - delta in place
+      f32x16 sc = f32x16{}, dp;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(Et + 32 * qb + 8 * g4 + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp[4 * g4 + j] = e4[j];
+      }
 #pragma unroll
       for (int s = 0; s < DP / 16; ++s) {
         sc = mfma32(lds_row8<DP, true>(Qt, 32 * qb + l32, 16 * s, h), kf[s], sc);
         dp = mfma32(lds_row8<DP, true>(Dt, 32 * qb + l32, 16 * s, h), vf[s], dp);
       }
 #if CPTHD_DKDV_PIPE
-      pipeline_reads_mfma<2 * (DP / 16), CPTHD_DKDV_PIPE>();
+      pipeline_reads_mfma<2 * (DP / 16), CPTHD_DKDV_PIPE, 1, 4>();   // + the four reads of -delta
 #endif
+      // P = exp2(S * scale * log2(e) - LSE * log2(e)), dS = P (dP - delta); the
+      // causal test only on steps that reach the tile's diagonal (a uniform branch)
+      auto probs = [&](auto masked) __attribute__((always_inline)) {
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int q4 = 32 * qb + 8 * g4 + 4 * h;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + q4);
-        const f32x4 e4 = *reinterpret_cast<const f32x4*>(Et + q4);
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int q4 = 32 * qb + 8 * g4 + 4 * h;
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + q4);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = 4 * g4 + j;
-          float pv = exp2_fast(fmaf(sc[r], sl2, -l4[j]));
-          if (need_mask && 32 * qb + 8 * g4 + j < thr) pv = 0.f;
-          sc[r] = pv;
-          dp[r] = pv * (dp[r] - e4[j]);
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * g4 + j;
+            float pv = exp2_fast(fmaf(sc[r], sl2, -l4[j]));
+            if constexpr (decltype(masked)::value)
+              if (32 * qb + 8 * g4 + j < thr) pv = 0.f;
+            sc[r] = pv;
+            dp[r] = pv * dp[r];
+          }
         }
-      }
+      };
+      if (need_mask)
+        probs(std::true_type{});
+      else
+        probs(std::false_type{});
       pd[0] = acc_to_bf16(sc, 0);
       pd[1] = acc_to_bf16(sc, 8);
       pd[2] = acc_to_bf16(dp, 0);

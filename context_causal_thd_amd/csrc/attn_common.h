@@ -206,10 +206,12 @@ __device__ inline bf16x8 lds_tr8(const uint16_t* tile, int q0, int q1, int c0) {
 // Scheduling hint for a run of N MFMAs that consume R LDS reads each, in
 // order: keep the reads of AHEAD products in flight ahead of the products, so
 // a product waits for reads issued AHEAD products earlier rather than for the
-// ones just issued.  Place it after the run's code.
-template <int N, int AHEAD, int R = 1>
+// ones just issued.  EXTRA further reads (operands read once, such as an
+// accumulator's start values) go with the first group.  Place it after the
+// run's code.
+template <int N, int AHEAD, int R = 1, int EXTRA = 0>
 __device__ inline void pipeline_reads_mfma() {
-  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R, 0);   // LDS reads
+  __builtin_amdgcn_sched_group_barrier(0x100, AHEAD * R + EXTRA, 0);   // LDS reads
 #pragma unroll
   for (int i = 0; i < N - AHEAD; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // MFMA

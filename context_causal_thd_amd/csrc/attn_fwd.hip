@@ -68,7 +68,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     return;
   }
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
 

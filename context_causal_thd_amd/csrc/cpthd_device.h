@@ -122,6 +122,11 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int 
 // ---------------------------------------------------------------------------
 // small device helpers
 // ---------------------------------------------------------------------------
+// The work-item's wave within its work-group, as a wave-uniform (scalar) value:
+// everything derived from it (LDS tile bases, M0 for direct loads, row blocks)
+// then lives in scalar registers instead of being kept per lane.
+__device__ inline int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
