@@ -44,6 +44,9 @@ constexpr int kDqSplit = CPTHD_DQ_SPLIT;
 #ifndef CPTHD_DQ_PIPE
 #define CPTHD_DQ_PIPE 1   // read-ahead scheduling hints in the dQ pass
 #endif
+#ifndef CPTHD_DKDV_ACC_PIPE
+#define CPTHD_DKDV_ACC_PIPE 2   // dK/dV products: transpose-read pairs kept this many ahead (0: no hint)
+#endif
 #ifndef CPTHD_DKDV_PIPE
 #define CPTHD_DKDV_PIPE 2   // dK/dV score products: row reads kept this many ahead (0: no hint)
 #endif
@@ -435,6 +438,9 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
     // dV += P^T dO, dK += dS^T Q for one query block over this wave's column blocks
     auto accumulate = [&](int qb, const bf16x8 (&pd)[4]) {
       const int r0 = 32 * qb + 4 * h;
+#if CPTHD_DKDV_ACC_PIPE
+      __builtin_amdgcn_sched_barrier(0);   // its own scheduling region, so the hint below applies to it alone
+#endif
 #pragma unroll
       for (int j = 0; j < NDB; ++j) {
         const int c0l = 32 * (dh * NDB + j);
@@ -443,6 +449,9 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
         dka[j] = mfma32(pd[2], lds_tr8<DP, true>(Qt, r0, r0 + 8, c0l), dka[j]);
         dka[j] = mfma32(pd[3], lds_tr8<DP, true>(Qt, r0 + 16, r0 + 24, c0l), dka[j]);
       }
+#if CPTHD_DKDV_ACC_PIPE
+      pipeline_reads_mfma<4 * NDB, CPTHD_DKDV_ACC_PIPE, 2>();
+#endif
     };
     if (SD == 1) {
 #pragma unroll
