@@ -166,7 +166,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-allgathered", action="store_true",
-                    help="skip timing the rank-major gathered K/V path (profiling runs: only the main step's launches)")
+                    help="skip the extra timing legs: the rank-major gathered K/V path and the HIP-graph replay of "
+                         "the step (profiling runs: only the main step's launches)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the timed region, run one plain copy of the K/V buffers (known bytes) through the "
                          "restoration kernel in contiguous mode, as the reference for HBM byte counters")
@@ -256,16 +257,24 @@ def main():
     cpthd.check_dev_status(status)
     log(f"warmup done ({args.warmup} steps)")
 
-    events = [make_events() for _ in range(args.steps)]
+    # the timed steps: plain launches, nothing recorded between them
     torch.cuda.synchronize()
     with ClockSampler() as clock:
         t0 = time.perf_counter()
-        for k_step in range(args.steps):
-            step(events[k_step])
+        for _ in range(args.steps):
+            step(None)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
     cpthd.check_dev_status(status)
     log(f"timed {args.steps} steps in {elapsed:.3f} s")
+
+    # per-kernel durations: as many steps again, with events recorded around every launch
+    events = [make_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for k_step in range(args.steps):
+        step(events[k_step])
+    torch.cuda.synchronize()
+    cpthd.check_dev_status(status)
     acc = np.zeros((len(shares), n_kernels))
     for evs, hevs in events:
         for i in range(len(shares)):
@@ -307,6 +316,31 @@ def main():
         ag_acc /= args.steps
         log(f"allgathered path: {args.steps} steps in {ag_elapsed:.3f} s")
         ag = {"ms_per_step": ag_elapsed * 1e3 / args.steps}
+
+    # the same step captured once in a HIP graph and replayed: the launch overhead a training loop that
+    # captures its step would not pay (the kernels and their work are unchanged)
+    graph_ms = None
+    if not args.no_allgathered:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step(None)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(None)
+        for _ in range(args.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        cpthd.check_dev_status(status)
+        del g
+        log(f"graph replay: {args.steps} steps, {graph_ms:.3f} ms each")
 
     # HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V), and the
     # restoration alone, each cold (a 512 MiB write before every rep evicts the 256 MiB last-level cache) and
@@ -396,6 +430,9 @@ def main():
             "kernel_ms_per_step": {n: float(ag_acc[:, jj].sum())
                                    for jj, n in enumerate(["attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"])},
         },
+        # the main step (restoration path) replayed from a HIP graph, same kernels and inputs
+        "graph_replayed_step": None if graph_ms is None else {
+            "ms_per_step": graph_ms, "tflops": step_flops / (graph_ms * 1e-3) / 1e12},
     }
 
     cpu = None
