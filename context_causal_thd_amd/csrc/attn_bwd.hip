@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
   for (int s = 0; s < DP / 16; ++s) {
     u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
     const int d = 16 * s + 8 * h;
-    if (key_in && d < D) {
+    if (key_in && d < D && nchunks > 0) {   // a tile no row of the rank sees only writes zeros
       a = *reinterpret_cast<const u32x4*>(k + krow * D + d);
       b = *reinterpret_cast<const u32x4*>(v + krow * D + d);
     }
