@@ -207,3 +207,17 @@ def test_batch_on_rank_keeps_global_positions(wl):
         cu = wl.cu_padded.astype(np.int64)
         doc = np.searchsorted(cu, parts[r], side="right") - 1
         assert np.array_equal(slices[r][2], parts[r] - cu[doc])
+
+
+@pytest.mark.parametrize("strategy", [oracle.NO_LOAD_BALANCE, oracle.PACKED_SUPER_SEQUENCE])
+def test_config4_pairs_sum_to_every_documents_causal_pairs(strategy):
+    # CP is exact: the ranks' useful pairs add up to every document's causal pairs over its actual tokens,
+    # sum of a(a+1)/2.  The per-rank split is what the config's "least and most work" ranks are checked on.
+    wl = W.config4()
+    a = np.diff(wl.cu_actual.astype(np.int64))
+    per_rank = [oracle.useful_pairs(oracle.partition_indices(wl.cu_padded, wl.cp, r, strategy), wl.cu_padded,
+                                    wl.cu_actual) for r in range(wl.cp)]
+    assert sum(per_rank) == int(np.sum(a * (a + 1) // 2))
+    if strategy == oracle.NO_LOAD_BALANCE:
+        # with packed documents rank 7 holds the least causal work and rank 4 the most (not ranks 0 and 7)
+        assert int(np.argmin(per_rank)) == 7 and int(np.argmax(per_rank)) == 4
