@@ -299,13 +299,17 @@ def main():
     if not args.no_allgathered:
         for _ in range(args.warmup):
             step_allgathered(None)
-        ag_events = [[[cpthd.HipEvents(2), cpthd.HipEvents(4)] for _ in shares] for _ in range(args.steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for k_step in range(args.steps):
-            step_allgathered(ag_events[k_step])
+        for _ in range(args.steps):
+            step_allgathered(None)
         torch.cuda.synchronize()
         ag_elapsed = time.perf_counter() - t0
+        cpthd.check_dev_status(status)
+        ag_events = [[[cpthd.HipEvents(2), cpthd.HipEvents(4)] for _ in shares] for _ in range(args.steps)]
+        for k_step in range(args.steps):   # per-kernel durations: a second pass with events
+            step_allgathered(ag_events[k_step])
+        torch.cuda.synchronize()
         cpthd.check_dev_status(status)
         ag_acc = np.zeros((len(shares), 3))
         for he in ag_events:

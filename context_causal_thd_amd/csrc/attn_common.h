@@ -54,6 +54,19 @@ struct AgMap {
     const bool first = j < cp;
     return (first ? j : 2 * cp - 1 - j) * S + lb + (first ? off : c + off);
   }
+  // chunk j holding p (p >= u0) and its first token
+  __device__ inline void chunk_of(int p, int& j, int& start) const {
+    const int pos = p - u0;
+    const int j0 = (int)((float)pos * rc);
+    const int o0 = pos - j0 * c;
+    j = o0 < 0 ? j0 - 1 : (o0 >= c ? j0 + 1 : j0);
+    start = u0 + j * c;
+  }
+};
+
+// The chunk the key steps of one tile have reached (keys only move forward).
+struct AgCursor {
+  int j, start;
 };
 
 // The map of a document's keys (contiguous strategy: the identity, c = S).
@@ -70,6 +83,10 @@ __device__ inline AgMap ag_map(const DocSeg& d, const AttnParams& p) {
     m.c = p.strategy == kPacked ? p.S / 2 : p.S;
     m.lb = 0;
   }
+  // the map is the same for every lane: keep it (and whatever is derived from it) in scalar registers
+  m.u0 = __builtin_amdgcn_readfirstlane(m.u0);
+  m.c = __builtin_amdgcn_readfirstlane(m.c);
+  m.lb = __builtin_amdgcn_readfirstlane(m.lb);
   m.rc = m.c > 0 ? 1.0f / (float)m.c : 0.f;
   return m;
 }
@@ -144,6 +161,25 @@ struct TileLoader {
       const int r = srow[i];
       const uint32_t o = off(r < 0 ? 0 : r) + scol[i];
       voff[i] = (r >= 0 && valid(r)) ? o : 0x80000000u;
+    }
+  }
+  // rows [0, nvalid) of a step whose rows follow each other from a scalar offset on: r * row_bytes + col;
+  // rows from nvalid on read as zero
+  __device__ inline void set_rows_linear(uint32_t row_bytes, uint32_t col, int nvalid) {
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int r = srow[i];
+      voff[i] = (r >= 0 && r < nvalid) ? (uint32_t)r * row_bytes + col + scol[i] : 0x80000000u;
+    }
+  }
+  // the same over two runs of consecutive rows: rows [0, split) from row a0 on, rows [split, nvalid) from
+  // row a1 on (absolute row offsets, used with a zero scalar offset)
+  __device__ inline void set_rows_two(uint32_t row_bytes, uint32_t col, int nvalid, int split, int a0, int a1) {
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int r = srow[i];
+      const int row = r < split ? a0 + r : a1 + (r - split);
+      voff[i] = (r >= 0 && r < nvalid) ? (uint32_t)row * row_bytes + col + scol[i] : 0x80000000u;
     }
   }
   __device__ inline void issue(__amdgpu_buffer_rsrc_t rsrc, uint16_t* tile, uint32_t soff, int wave) const {
@@ -235,21 +271,49 @@ __device__ inline bf16x8 acc_to_bf16(const f32x16& a, int r0) {
 // kend on read as zero.  Physical order: the descriptors start at the
 // document's first key ds and the lane offsets were set once, so a step only
 // moves the scalar offset.  Rank-major all-gathered order (AG): the
-// descriptors cover all T rows (T * row_bytes < 2^31) and every lane's row
-// offsets go through the map, per step.
+// descriptors cover all T rows (T * row_bytes < 2^31).  A step whose keys lie
+// in one chunk of the partition reads consecutive gathered rows, from a scalar
+// offset the cursor gives; a step over two chunks picks one of two scalar row
+// bases per lane; only a step over more chunks (chunks under 64 keys) maps
+// every lane's row through the map.
 template <bool AG, int DP, int NW>
 __device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buffer_rsrc_t krs,
-                                     __amdgpu_buffer_rsrc_t vrs, const AgMap& agm, int kb, int ds, int kend,
-                                     uint32_t row_bytes, int kvh, int D, int wave, int lane, uint16_t* Kn,
+                                     __amdgpu_buffer_rsrc_t vrs, const AgMap& agm, AgCursor& cur, int kb, int ds,
+                                     int kend, uint32_t row_bytes, int kvh, int D, int wave, int lane, uint16_t* Kn,
                                      uint16_t* Vn) {
 #if defined(__HIP_DEVICE_COMPILE__)   // buffer-resource builtins: device pass only
   if constexpr (AG) {
     const uint32_t col = (uint32_t)kvh * D * 2;
-    const int last = kend - 1;
-    ld.set_rows([&](int r) __attribute__((always_inline)) { return (uint32_t)agm.row(min(kb + r, last)) * row_bytes + col; },
-                [&](int r) __attribute__((always_inline)) { return kb + r < kend; });
-    ld.issue(krs, Kn, 0, wave);
-    ld.issue(vrs, Vn, 0, wave);
+    const int nvalid = min(kKvStep, kend - kb);
+    // move the cursor to the chunk holding kb (at most 2cp chunks in a unit)
+    for (int g = 0; g < 2 * agm.cp && kb >= cur.start + agm.c; ++g) {
+      cur.start += agm.c;
+      ++cur.j;
+    }
+    // gathered row of the first token of chunk j
+    auto chunk_row = [&](int j) __attribute__((always_inline)) {
+      const bool first = j < agm.cp;
+      return (first ? j : 2 * agm.cp - 1 - j) * agm.S + agm.lb + (first ? 0 : agm.c);
+    };
+    if (kb >= cur.start && kb + nvalid <= cur.start + agm.c) {
+      // the step's keys lie in one chunk, so they are consecutive rows of the gathered buffer
+      const int row0 = chunk_row(cur.j) + (kb - cur.start);
+      ld.set_rows_linear(row_bytes, col, nvalid);
+      ld.issue(krs, Kn, (uint32_t)row0 * row_bytes, wave);
+      ld.issue(vrs, Vn, (uint32_t)row0 * row_bytes, wave);
+    } else if (kb >= cur.start && kb + nvalid <= cur.start + 2 * agm.c && cur.j + 1 < 2 * agm.cp) {
+      // two chunks: two runs of consecutive gathered rows
+      const int split = cur.start + agm.c - kb;
+      ld.set_rows_two(row_bytes, col, nvalid, split, chunk_row(cur.j) + (kb - cur.start), chunk_row(cur.j + 1));
+      ld.issue(krs, Kn, 0, wave);
+      ld.issue(vrs, Vn, 0, wave);
+    } else {
+      const int last = kend - 1;
+      ld.set_rows([&](int r) __attribute__((always_inline)) { return (uint32_t)agm.row(min(kb + r, last)) * row_bytes + col; },
+                  [&](int r) __attribute__((always_inline)) { return kb + r < kend; });
+      ld.issue(krs, Kn, 0, wave);
+      ld.issue(vrs, Vn, 0, wave);
+    }
   } else {
     const uint32_t soff = (uint32_t)(kb - ds) * row_bytes;
     ld.issue(krs, Kn, soff, wave);

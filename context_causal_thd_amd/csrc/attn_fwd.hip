@@ -85,9 +85,13 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(v + kv0, kv_bytes);
   TileLoader<DP, true, NW> kvld;
   AgMap agm;
-  if constexpr (AG) agm = ag_map(reinterpret_cast<const DocSeg*>(ws + lay.docs)[t.doc], prm);
+  AgCursor cur{0, 0};
+  if constexpr (AG) {
+    agm = ag_map(reinterpret_cast<const DocSeg*>(ws + lay.docs)[t.doc], prm);
+    agm.chunk_of(t.ds, cur.j, cur.start);
+  }
   auto issue_kv = [&](int kb, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
-    issue_kv_step<AG>(kvld, krs, vrs, agm, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
+    issue_kv_step<AG>(kvld, krs, vrs, agm, cur, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
   };
   if constexpr (AG) {
     kvld.init_slots(wave, lane, D);
