@@ -30,12 +30,12 @@ namespace cpthd {
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 #ifndef CPTHD_FWD_ROW_BLOCKS
-#define CPTHD_FWD_ROW_BLOCKS 1
+#define CPTHD_FWD_ROW_BLOCKS 1   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
 #endif
 constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;
 #ifndef CPTHD_FWD_PREFETCH
-#define CPTHD_FWD_PREFETCH 1
-#endif   // 32-row blocks per wave (1: 8 waves, 2: 4 waves)
+#define CPTHD_FWD_PREFETCH 1     // K operands of a 32-key block read ahead of its products
+#endif
 
 template <int DP, int QB, bool AG>
 __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_EU(kQWaves / QB * kQMinBlocks / 4) void attn_fwd_kernel(const uint16_t* __restrict__ q,
