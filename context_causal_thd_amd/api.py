@@ -266,6 +266,7 @@ class AttnPlan:
             raise ValueError("unsupported attention configuration")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.built = None
+        self.generation = 0   # counts builds, so a user of the plan can tell that it was rebuilt
 
     def build(self, cu_seqlens, cu_seqlens_padded, total_tokens, rank, strategy, dev_status=None):
         _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 2, ())
@@ -276,6 +277,7 @@ class AttnPlan:
         cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, self.capacity, self.cp_size, rank,
                         strategy, self.Hq, self.Hkv, self.D, self.workspace, dev_status)
         self.built = dict(total_tokens=total_tokens, num_docs=num_docs, rank=rank, strategy=strategy)
+        self.generation += 1
         return self
 
     def _args(self):
@@ -346,7 +348,7 @@ class CPAttention(torch.autograd.Function):
     def forward(ctx, q_local, k, v, plan: AttnPlan, softmax_scale, kv_allgathered=False):
         o, lse = attn_fwd(q_local, k, v, plan, softmax_scale, kv_allgathered=kv_allgathered)
         ctx.plan = plan
-        ctx.layout = dict(plan.built)
+        ctx.generation = plan.generation
         ctx.scale = softmax_scale
         ctx.kv_allgathered = kv_allgathered
         ctx.save_for_backward(q_local, k, v, o, lse)
@@ -355,8 +357,9 @@ class CPAttention(torch.autograd.Function):
     @staticmethod
     def backward(ctx, do):
         q_local, k, v, o, lse = ctx.saved_tensors
-        if ctx.plan.built != ctx.layout:
-            raise RuntimeError("the plan was rebuilt for another layout between forward and backward")
+        if ctx.plan.generation != ctx.generation:
+            # even with the same sizes, other document boundaries would give other tiles: refuse any rebuild
+            raise RuntimeError("the plan was rebuilt between forward and backward")
         dq, dk, dv = attn_bwd(q_local, k, v, o, do.contiguous(), lse, ctx.plan, ctx.scale,
                               kv_allgathered=ctx.kv_allgathered)
         return dq.to(q_local.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None

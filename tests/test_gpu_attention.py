@@ -325,7 +325,7 @@ def test_plan_rejects_documents_of_2gib_kv():
 @pytest.mark.parametrize("allgathered", [False, True])
 def test_autograd_wrapper_matches_entry_points(allgathered):
     """cpthd.attention (autograd) gives the entry points' O bit for bit, and gradients equal to the fp32
-    dQ/dK/dV cast to the inputs' dtype; a plan rebuilt for another layout before backward is refused."""
+    dQ/dK/dV cast to the inputs' dtype; a plan rebuilt in any way before backward is refused."""
     wl = W.small_random(5, 2, 0, max_docs=4, max_len=300, Hq=8, Hkv=2, D=64, bf16=True, qkv_scale=0.5,
                         do_scale=1.0)
     S, T = wl.T // wl.cp, wl.T
@@ -344,6 +344,13 @@ def test_autograd_wrapper_matches_entry_points(allgathered):
     sh.plan.build(sh.cu_a, sh.cu_p, T, 0, 0, sh.st)          # another rank's layout
     with pytest.raises(RuntimeError, match="rebuilt"):
         o2.backward(sh.do[:S])
+    # a rebuild with the same sizes, rank and strategy (as for the next micro-batch of equal length) is
+    # refused as well: other document boundaries would give other tiles
+    sh.plan.build(sh.cu_a, sh.cu_p, T, 1, 0, sh.st)
+    o3 = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
+    sh.plan.build(sh.cu_a, sh.cu_p, T, 1, 0, sh.st)
+    with pytest.raises(RuntimeError, match="rebuilt"):
+        o3.backward(sh.do[:S])
 
 
 # dK/dV sum G heads of P * dO, so their magnitude (and the absolute rounding of the bf16 P operand) grows
