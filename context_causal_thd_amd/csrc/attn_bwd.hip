@@ -90,6 +90,11 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
   const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
   const int bm = kRowsPerWG / G;
+  // a work-group holding none of the tile's rows (the tile has at most
+  // part * kRowsPerWG / kDqSplit of them) has nothing to write: it leaves
+  // before issuing any load
+  const int m_first = part * (kRowsPerWG / kDqSplit);
+  if (m_first >= bm * G || m_first / G >= t.ntok) return;
 
   // K/V rows [ds, kv_end) as in the forward (physical or all-gathered order)
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
@@ -156,6 +161,14 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
       lse2w[qrow[qb]] = valid[qb] ? lse2[qb] : 0.f;
     }
   }
+
+  // a wave none of whose rows is an actual token (the tail of a segment's last
+  // tile, or pads) skips the products and only helps load the tiles: its SIMD
+  // then runs the other wave alone (its rows' dQ stays zero, as it must)
+  bool any_valid = false;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) any_valid = any_valid || valid[qb];
+  const bool wave_active = __any(any_valid);
 
   f32x16 acc[QB][DP / 32], ndl[QB];   // ndl: -delta in every entry, the start of each dP^T product
 #pragma unroll
@@ -229,9 +242,21 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
 #endif
     lds_loads_barrier();
   };
-  for (int it = 0; it < nsteps; it += 2) {
-    step(it, K0, V0, K1, V1);
-    if (it + 1 < nsteps) step(it + 1, K1, V1, K0, V0);
+  if (wave_active) {
+    for (int it = 0; it < nsteps; it += 2) {
+      step(it, K0, V0, K1, V1);
+      if (it + 1 < nsteps) step(it + 1, K1, V1, K0, V0);
+    }
+  } else {
+    // the same loads and barriers, no products
+    for (int it = 0; it < nsteps; it += 2) {
+      if (it + 1 < nsteps) issue_kv(t.ds + (it + 1) * kKvStep, K1, V1);
+      lds_loads_barrier();
+      if (it + 1 < nsteps) {
+        if (it + 2 < nsteps) issue_kv(t.ds + (it + 2) * kKvStep, K0, V0);
+        lds_loads_barrier();
+      }
+    }
   }
 
 #pragma unroll

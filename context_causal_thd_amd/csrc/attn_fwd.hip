@@ -123,6 +123,20 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     }
   }
 
+  // Steps this wave computes: up to the one holding the key of its last actual
+  // token.  Later steps of the tile are masked for every row of the wave (and
+  // a wave without an actual row, the tail of a segment's last tile, has none):
+  // it only loads its share of those tiles and meets the barriers, so its SIMD
+  // runs the other wave alone.  The outputs do not change.
+  int nsteps_w = 0;
+  {
+    const int m_lo = wave * 32 * QB, m_hi = min(m_lo + 32 * QB, bm * G) - 1;
+    if (m_lo <= m_hi && m_lo / G < t.ntok && t.p0 + m_lo / G < t.ve) {
+      const int p_hi = min(t.p0 + min(m_hi / G, t.ntok - 1), t.ve - 1);
+      nsteps_w = (p_hi + 1 - t.ds + kKvStep - 1) / kKvStep;
+    }
+  }
+
   float m_i[QB], l_i[QB];
   f32x16 acc[QB][DP / 32];
 #pragma unroll
@@ -242,9 +256,14 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     pv_products(Vt, pb);
     lds_loads_barrier();
   };
-  for (int it = 0; it < nsteps; it += 2) {
+  for (int it = 0; it < nsteps_w; it += 2) {
     step(it, K0, V0, K1, V1);
-    if (it + 1 < nsteps) step(it + 1, K1, V1, K0, V0);
+    if (it + 1 < nsteps_w) step(it + 1, K1, V1, K0, V0);
+  }
+  // the rest of the tile's steps: the same loads and barriers, no products
+  for (int it = nsteps_w; it < nsteps; ++it) {
+    if (it + 1 < nsteps) issue_kv(t.ds + (it + 1) * kKvStep, (it & 1) ? K0 : K1, (it & 1) ? V0 : V1);
+    lds_loads_barrier();
   }
 
 #pragma unroll
