@@ -346,6 +346,34 @@ def main():
         del g
         log(f"graph replay: {args.steps} steps, {graph_ms:.3f} ms each")
 
+    # the partition kernel alone at the million-token layout (T = 1,048,576 in 10,000 documents, cp_size 4),
+    # every rank under both strategies: 50 back-to-back calls per (strategy, rank), mean time per call
+    part_big = None
+    if not args.no_allgathered:
+        cu_big_np, _ = W.config5b()
+        T_big, cp_big = int(cu_big_np[-1]), 4
+        cu_big = torch.from_numpy(cu_big_np).to(dev)
+        idx_big = torch.empty(T_big // cp_big, dtype=torch.int32, device=dev)
+        us = []
+        for s_b in (0, 1):
+            for r_b in range(cp_big):
+                for _ in range(3):
+                    cpthd.partition_indices(cu_big, T_big, cp_big, r_b, s_b, out=idx_big, dev_status=status)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for _ in range(50):
+                    cpthd.partition_indices(cu_big, T_big, cp_big, r_b, s_b, out=idx_big, dev_status=status)
+                e1.record()
+                torch.cuda.synchronize()
+                us.append(e0.elapsed_time(e1) * 1e3 / 50)
+        cpthd.check_dev_status(status)
+        out_bytes = 4.0 * (T_big // cp_big)
+        part_big = {"T": T_big, "num_docs": int(len(cu_big_np) - 1), "cp_size": cp_big,
+                    "us_per_call_mean": float(np.mean(us)), "us_per_call_max": float(np.max(us)),
+                    "out_bytes_per_call": out_bytes, "gbs": float(out_bytes / (np.mean(us) * 1e-6) / 1e9),
+                    "note": "back-to-back launches on one stream; 1 MiB of indices per call is latency-bound"}
+        log(f"partition at T={T_big}: {np.mean(us):.2f} us per call")
+
     # HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V), and the
     # restoration alone, each cold (a 512 MiB write before every rep evicts the 256 MiB last-level cache) and
     # the copy also warm (the source left in that cache, as inside the step)
@@ -420,6 +448,7 @@ def main():
         "attn_fwd_bwd_tflops": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12),
         "attn_frac_of_bf16_peak": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS),
         "partition_gbs": float(part_bytes / (per_kernel_ms[:, 0].mean() * 1e-3) / 1e9),
+        "partition_million_tokens": part_big,
         "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
         "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
         "reorder_gbs_cold": reorder_cold,

@@ -164,11 +164,13 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
 
   // a wave none of whose rows is an actual token (the tail of a segment's last
   // tile, or pads) skips the products and only helps load the tiles: its SIMD
-  // then runs the other wave alone (its rows' dQ stays zero, as it must)
+  // then runs the other wave alone (its rows' dQ stays zero, as it must).  The
+  // all-gathered instantiation keeps every wave computing: it sits at the
+  // register limit, and the second loop made it spill.
   bool any_valid = false;
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) any_valid = any_valid || valid[qb];
-  const bool wave_active = __any(any_valid);
+  const bool wave_active = AG || __any(any_valid);
 
   f32x16 acc[QB][DP / 32], ndl[QB];   // ndl: -delta in every entry, the start of each dP^T product
 #pragma unroll
