@@ -9,8 +9,7 @@
 // Both kernels are pure data movement (HBM bound).  Under DualChunkSwap the
 // rank's local rows of document i start at local row cu_padded[i] / cp_size
 // (every earlier document contributed L/cp_size rows), so an output position
-// finds its document with one binary search over cu_seqlens_padded, without a
-// prefix sum.
+// finds its document by a search over cu_seqlens_padded, without a prefix sum.
 #include <algorithm>
 
 #include "cpthd_device.h"
@@ -37,6 +36,25 @@ __device__ inline void validate_cu_padded(const int32_t* cu, int B, int64_t T, i
   if (bits) atomicOr(status, bits);
 }
 
+// Document of the wave's first output under DualChunkSwap: the largest i in
+// [0, B-1] with cu[i] <= x0, found by all 64 lanes together.  Each round the
+// lanes probe 64 evenly spaced offsets and one ballot keeps the piece holding
+// x0, so 10,000 documents take 3 dependent loads instead of 14.
+__device__ inline int wave_upper_index(const int32_t* cu, int B, int64_t x0, int lane) {
+  int lo = 0, hi = B - 1;   // cu[lo] <= x0 for a valid layout
+  while (hi - lo >= 64) {
+    const int64_t span = hi - lo;
+    const int m = lo + (int)((span * (lane + 1)) >> 6);   // lane 63 probes hi
+    const int k = __popcll(__ballot((int64_t)cu[m] <= x0));   // probes are non-decreasing: lanes 0..k-1 hold
+    const int m_next = lo + (int)((span * (k + 1)) >> 6);     // first probe above x0 (when k < 64)
+    if (k > 0) lo = lo + (int)((span * k) >> 6);
+    if (k < 64) hi = m_next - 1;
+  }
+  const int cand = lo + lane;
+  const int k = __popcll(__ballot(cand <= hi && (int64_t)cu[cand] <= x0));
+  return max(lo + k - 1, 0);   // k >= 1 unless the layout is rejected
+}
+
 // One thread writes 4 consecutive outputs j = 4*gid .. 4*gid+3 of [0, S).
 __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restrict__ cu, int B, int T, int cp,
                                                         int rank, int strategy, int32_t* __restrict__ out,
@@ -44,28 +62,55 @@ __global__ __launch_bounds__(256) void partition_kernel(const int32_t* __restric
   validate_cu_padded(cu, B, T, cp, strategy, status);
   const int S = T / cp;
   const int64_t j0 = 4 * ((int64_t)blockIdx.x * blockDim.x + threadIdx.x);
-  if (j0 >= S) return;
   int32_t res[4];
   if (strategy == kContig) {
+    if (j0 >= S) return;
     for (int u = 0; u < 4; ++u) res[u] = rank * S + (int)j0 + u;
   } else if (strategy == kPacked) {
+    if (j0 >= S) return;
     const int c = T / (2 * cp);   // whole-buffer chunks r and 2cp-1-r
     for (int u = 0; u < 4; ++u) {
       const int j = (int)j0 + u;
       res[u] = j < c ? rank * c + j : (2 * cp - 1 - rank) * c + (j - c);
     }
   } else {
-    // document of output j: cu[i] <= j*cp < cu[i+1]
-    int i = upper_index(cu, B - 1, j0 * cp);
+    // document of output j: cu[i] <= j*cp < cu[i+1].  The wave's 256 outputs
+    // span a short run of documents: find the first with a wave search, hold
+    // the next 64 offsets one per lane, and look each output up among them
+    // with register shuffles.  Every lane of a live wave takes part.
+    const int lane = threadIdx.x & 63;
+    const int64_t jw = j0 - 4 * lane;   // the wave's first output
+    if (jw >= S) return;                // the whole wave is past the end
+    const int64_t x_last = (min(jw + 255, (int64_t)S - 1)) * cp;
+    const int i0 = wave_upper_index(cu, B, jw * cp, lane);
+    const int w = cu[min(i0 + lane, B)];   // offsets of documents i0 .. i0+63 (cu[B] = T past the end)
+    // the run is held whole when the document after the wave's last output starts inside it
+    const bool held = (int64_t)__shfl(w, 63) > x_last;
     for (int u = 0; u < 4; ++u) {
-      const int64_t j = j0 + u;
-      while (i < B - 1 && (int64_t)cu[i + 1] <= j * cp) ++i;
-      const int start = cu[i];
-      const int c = (cu[i + 1] - start) / (2 * cp);
+      const int64_t j = min(j0 + u, (int64_t)S - 1);
+      const int64_t x = j * cp;
+      int start, next;
+      if (held) {
+        int k = 0;   // largest k with w_k <= x, one bit at a time (w_0 <= x; k <= 62 when held)
+#pragma unroll
+        for (int b = 32; b >= 1; b >>= 1) {
+          const int t = k + b;
+          if ((int64_t)__shfl(w, t) <= x) k = t;
+        }
+        k = min(k, 62);
+        start = __shfl(w, k);
+        next = __shfl(w, k + 1);
+      } else {
+        const int i = i0 + upper_index(cu + i0, B - 1 - i0, x);
+        start = cu[i];
+        next = cu[i + 1];
+      }
+      const int c = (next - start) / (2 * cp);
       const int jj = (int)(j - start / cp);
-      int p = jj < c ? start + rank * c + jj : start + (2 * cp - 1 - rank) * c + (jj - c);
+      const int p = jj < c ? start + rank * c + jj : start + (2 * cp - 1 - rank) * c + (jj - c);
       res[u] = min(max(p, 0), T - 1);   // stays in range even for a rejected layout
     }
+    if (j0 >= S) return;
   }
   if (j0 + 3 < S && (S & 3) == 0) {
     *reinterpret_cast<int4*>(out + j0) = make_int4(res[0], res[1], res[2], res[3]);

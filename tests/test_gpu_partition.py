@@ -50,6 +50,32 @@ def test_partition_bit_exact(name, wl):
             np.testing.assert_array_equal(got, ref)
 
 
+def _short_document_layouts():
+    """3000 documents: 1000 of 2*cp or 4*cp tokens, a run of 100 long ones, then 1900 of 2*cp to 8*cp tokens.
+    A wave's 256 outputs then span more than 63 documents (the kernel's per-lane search) or fewer (its register
+    lookup), and some waves straddle the two."""
+    out = []
+    for seed, cp in enumerate((1, 2, 4, 8)):
+        rng = np.random.default_rng([77, seed])
+        units = rng.integers(1, 5, size=3000)
+        units[:1000] = rng.integers(1, 3, size=1000)
+        units[1000:1100] = rng.integers(50, 400, size=100)
+        out.append((f"short_docs.cp{cp}", np.concatenate([[0], np.cumsum(2 * cp * units)]).astype(np.int32), cp))
+    return out
+
+
+SHORT_DOCS = _short_document_layouts()
+
+
+@pytest.mark.parametrize("name,cu_p,cp", SHORT_DOCS, ids=[n for n, _, _ in SHORT_DOCS])
+def test_partition_many_short_documents(name, cu_p, cp):
+    T = int(cu_p[-1])
+    for s in (0, 1, 2):
+        for r in range(cp):
+            log(f"partition {name} s={s} r={r}")
+            np.testing.assert_array_equal(_gpu_indices(cu_p, T, cp, r, s), oracle.partition_indices(cu_p, cp, r, s))
+
+
 def test_partition_million_tokens_ten_thousand_docs():
     cu_p, _ = W.config5b()
     T = int(cu_p[-1])
