@@ -43,7 +43,7 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_config3_hbm_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_t32768_gqa32x8_hbm_traffic.json")
 KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
 # the physical-order kernels the main step launches at head_dim 128 (rocprofv3 kernel names)
 KERNEL_SYMBOL = {"attn_fwd": "cpthd::attn_fwd_kernel<128, 1, false>",
@@ -182,7 +182,7 @@ def main():
     import context_causal_thd_amd as cpthd
 
     dev = "cuda"
-    wl = W.config3()
+    wl = W.t32768_gqa32x8()
     T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
     S = T // cp
     log(f"workload: T={T} docs={wl.num_docs} Hq={Hq} Hkv={Hkv} D={D} cp={cp}")
@@ -351,7 +351,7 @@ def main():
     # the host's launch rate does not enter the time
     part_big = None
     if not args.no_allgathered:
-        cu_big_np, _ = W.config5b()
+        cu_big_np, _ = W.t1m_10k_docs()
         T_big, cp_big = int(cu_big_np[-1]), 4
         cu_big = torch.from_numpy(cu_big_np).to(dev)
         idx_big = torch.empty(T_big // cp_big, dtype=torch.int32, device=dev)
@@ -494,7 +494,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "config3: T=32768 packed bf16 tokens, 32 q / 8 kv heads, head_dim 128, log-normal "
+        "config": {"workload": "t32768_gqa32x8: T=32768 packed bf16 tokens, 32 q / 8 kv heads, head_dim 128, log-normal "
                                "doc lengths (median 1024, sigma 1) clipped to [64,8192] padded to x8, cp_size=4; "
                                "shares dcs r0, dcs r3, contiguous r0, contiguous r3; partition + reorder + plan + "
                                "attention fwd + bwd per share",

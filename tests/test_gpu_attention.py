@@ -129,11 +129,11 @@ def _small_cases():
 SMALL = _small_cases()
 
 
-def test_config1_all_shares():
-    wl = W.config1(bf16=True)
+def test_tiny_t28_all_shares():
+    wl = W.tiny_t28(bf16=True)
     for s in wl.strategies:
         for r in wl.ranks:
-            log(f"config1 s={s} r={r}")
+            log(f"tiny_t28 s={s} r={r}")
             sh = Share(wl, s, r)
             sh.compare()
 
@@ -147,11 +147,11 @@ def test_small_full_parity(wl):
         sh.compare()
 
 
-def test_config2_forward_both_strategies():
-    wl = W.config2()
+def test_t8192_mha16_forward_both_strategies():
+    wl = W.t8192_mha16()
     for s in wl.strategies:
         for r in wl.ranks:
-            log(f"config2 s={s} r={r}")
+            log(f"t8192_mha16 s={s} r={r}")
             sh = Share(wl, s, r, backward=False)
             sh.compare(backward=False)
 
@@ -167,9 +167,9 @@ def _sample_docs(wl, idx, n=3):
 
 @pytest.mark.parametrize("s", [0, 1, 2])
 @pytest.mark.parametrize("r", [0, 3])
-def test_config3_sampled(s, r):
-    wl = W.config3()
-    log(f"config3 s={s} r={r}")
+def test_t32768_gqa32x8_sampled(s, r):
+    wl = W.t32768_gqa32x8()
+    log(f"t32768_gqa32x8 s={s} r={r}")
     sh = Share(wl, s, r)
     docs = _sample_docs(wl, sh.idx)
     log(f"  docs {docs}")
@@ -178,9 +178,9 @@ def test_config3_sampled(s, r):
 
 @pytest.mark.parametrize("s", [1, 2])
 @pytest.mark.parametrize("r", [0, 7])
-def test_config4_sampled(s, r):
-    wl = W.config4()
-    log(f"config4 s={s} r={r}")
+def test_t131072_gqa64x8_sampled(s, r):
+    wl = W.t131072_gqa64x8()
+    log(f"t131072_gqa64x8 s={s} r={r}")
     sh = Share(wl, s, r)
     doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
     touched = np.unique(doc[sh.idx])
@@ -190,14 +190,14 @@ def test_config4_sampled(s, r):
     sh.compare(docs=docs, kv_heads=[5])
 
 
-def test_config5_capacity_microbatches():
+def test_dynamic_t_capacity_microbatches():
     """Fixed-capacity buffers, NaN-poisoned beyond the active T, canaries on output tails."""
     for m in (0, 5, 11):
-        wl = W.config5(m)
+        wl = W.dynamic_t(m)
         for s in wl.strategies + (2,):
             for r in (0, 3):
-                log(f"config5 mb={m} T={wl.T} s={s} r={r}")
-                sh = Share(wl, s, r, capacity=W.CONFIG5_CAPACITY, poison=True)
+                log(f"dynamic_t mb={m} T={wl.T} s={s} r={r}")
+                sh = Share(wl, s, r, capacity=W.DYNAMIC_T_CAPACITY, poison=True)
                 sh.check_tails()
                 docs = _sample_docs(wl, sh.idx, n=2)
                 sh.compare(docs=docs, kv_heads=[3])
@@ -206,11 +206,11 @@ def test_config5_capacity_microbatches():
 # ---------------------------------------------------------------------------
 # K/V read straight from the rank-major all-gathered buffer (no restoration pass)
 # ---------------------------------------------------------------------------
-def test_config1_allgathered_all_shares():
-    wl = W.config1(bf16=True)
+def test_tiny_t28_allgathered_all_shares():
+    wl = W.tiny_t28(bf16=True)
     for s in wl.strategies + (2,):
         for r in wl.ranks:
-            log(f"config1 allgathered s={s} r={r}")
+            log(f"tiny_t28 allgathered s={s} r={r}")
             Share(wl, s, r, allgathered=True).compare()
 
 
@@ -229,16 +229,16 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
 
 
-@pytest.mark.parametrize("case", ["config3-s0-r0", "config3-s0-r3", "config3-s2-r1", "config5.mb5-s0-r2"])
+@pytest.mark.parametrize("case", ["t32768_gqa32x8-s0-r0", "t32768_gqa32x8-s0-r3", "t32768_gqa32x8-s2-r1", "dynamic_t.mb5-s0-r2"])
 def test_allgathered_bitwise_equals_physical(case):
     """Same arithmetic, other addresses: O, LSE, dQ bit-identical; dK/dV are the physical ones permuted
     into rank-major order."""
     name, s, r = case.split("-")
     s, r = int(s[1:]), int(r[1:])
-    if name == "config3":
-        wl, kw = W.config3(), {}
+    if name == "t32768_gqa32x8":
+        wl, kw = W.t32768_gqa32x8(), {}
     else:
-        wl, kw = W.config5(int(name.split("mb")[1])), dict(capacity=W.CONFIG5_CAPACITY, poison=True)
+        wl, kw = W.dynamic_t(int(name.split("mb")[1])), dict(capacity=W.DYNAMIC_T_CAPACITY, poison=True)
     log(f"{case} physical")
     a = Share(wl, s, r, **kw)
     log(f"{case} allgathered")
@@ -282,7 +282,7 @@ def test_degenerate_layouts(wl, allgathered):
 
 
 def test_plan_mismatch_sets_status_and_writes_nothing():
-    wl = W.config1(bf16=True)
+    wl = W.tiny_t28(bf16=True)
     sh = Share(wl, 0, 0)
     st = status_dev()
     o = torch.full_like(sh.o, 3.0)
@@ -296,7 +296,7 @@ def test_plan_mismatch_sets_status_and_writes_nothing():
 
 
 def test_plan_rejects_bad_layouts():
-    wl = W.config1(bf16=True)
+    wl = W.tiny_t28(bf16=True)
     plan = cpthd.AttnPlan(64, 2, 2, 2, 16, max_docs=4)
     st = status_dev()
     cu_bad = i32_dev([0, 6, 20, 28])                          # 6 % 4 != 0 under DCS
@@ -372,13 +372,13 @@ def test_wide_gqa_groups(wl, allgathered):
         Share(wl, s, r, allgathered=allgathered).compare()
 
 
-@pytest.mark.parametrize("name", ["config3", "config4"])
+@pytest.mark.parametrize("name", ["t32768_gqa32x8", "t131072_gqa64x8"])
 def test_strategies_agree_on_every_row(name):
     """Full-size property, every row: the strategies compute the same function of the same tokens, so all
     ranks' O, LSE, dQ scattered to physical rows, and dK, dV summed over ranks, agree between strategies (to
     rounding: the tiles, and so the accumulation order, differ).  Config 4's documents rule out DualChunkSwap."""
-    wl = W.config3() if name == "config3" else W.config4()
-    strategies = (0, 1, 2) if name == "config3" else (1, 2)
+    wl = W.t32768_gqa32x8() if name == "t32768_gqa32x8" else W.t131072_gqa64x8()
+    strategies = (0, 1, 2) if name == "t32768_gqa32x8" else (1, 2)
     T, cp = wl.T, wl.cp
     kv = (wl.k(), wl.v())
     res = {}

@@ -13,8 +13,8 @@ cpthd = pytest.importorskip("context_causal_thd_amd")
 
 
 def _layouts():
-    out = [("config1", W.config1()), ("config2", W.config2()), ("config3", W.config3()), ("config4", W.config4())]
-    out += [(f"config5.mb{m}", W.config5(m)) for m in range(W.CONFIG5_MICROBATCHES)]
+    out = [("tiny_t28", W.tiny_t28()), ("t8192_mha16", W.t8192_mha16()), ("t32768_gqa32x8", W.t32768_gqa32x8()), ("t131072_gqa64x8", W.t131072_gqa64x8())]
+    out += [(f"dynamic_t.mb{m}", W.dynamic_t(m)) for m in range(W.DYNAMIC_T_MICROBATCHES)]
     for seed in range(12):
         for cp in (1, 2, 3, 4, 8):
             for s in (0, 1, 2):
@@ -77,7 +77,7 @@ def test_partition_many_short_documents(name, cu_p, cp):
 
 
 def test_partition_million_tokens_ten_thousand_docs():
-    cu_p, _ = W.config5b()
+    cu_p, _ = W.t1m_10k_docs()
     T = int(cu_p[-1])
     for s in (0, 1, 2):
         for r in range(4):
@@ -113,7 +113,7 @@ def _rand_rows(T, row_elems, seed):
     return torch.from_numpy(bits.view(np.int16)).to("cuda")
 
 
-REORDER = [(n, wl) for n, wl in LAYOUTS if not n.startswith("config4")][::2] + [("config3", W.config3())]
+REORDER = [(n, wl) for n, wl in LAYOUTS if not n.startswith("t131072_gqa64x8")][::2] + [("t32768_gqa32x8", W.t32768_gqa32x8())]
 
 
 @pytest.mark.parametrize("name,wl", REORDER, ids=[n for n, _ in REORDER])
@@ -150,7 +150,7 @@ def test_reorder_bit_exact(name, wl):
     torch.cuda.synchronize()
 
 
-SLICE = [(n, wl) for n, wl in LAYOUTS if n.startswith(("config1", "config3", "config5.mb3")) or n.endswith(".cp3.s2")]
+SLICE = [(n, wl) for n, wl in LAYOUTS if n.startswith(("tiny_t28", "t32768_gqa32x8", "dynamic_t.mb3")) or n.endswith(".cp3.s2")]
 
 
 @pytest.mark.parametrize("name,wl", SLICE, ids=[n for n, _ in SLICE])

@@ -68,8 +68,8 @@ def test_fwd_matches_brute_force(wl):
         np.testing.assert_allclose(lse[fin], blse[fin], rtol=1e-12, atol=1e-12)
 
 
-def test_config1_fwd_brute_force_both_strategies():
-    wl = W.config1()
+def test_tiny_t28_fwd_brute_force_both_strategies():
+    wl = W.tiny_t28()
     for s in wl.strategies:
         for r in wl.ranks:
             idx, q, k, v, _ = _inputs(wl, r, s)
@@ -83,7 +83,7 @@ def test_config1_fwd_brute_force_both_strategies():
 def test_first_token_closed_form_and_pads():
     # At a document's first actual token the softmax has one key: O = V[start], LSE = scale*q.k;
     # pads give O = 0 and LSE = -inf exactly.
-    wl = W.config1()
+    wl = W.tiny_t28()
     for s in wl.strategies:
         for r in wl.ranks:
             idx, q, k, v, _ = _inputs(wl, r, s)
@@ -146,7 +146,7 @@ def _packed_autograd(q, k, v, do, cu_p, cu_a, scale):
     return o, dq, kt.grad.numpy(), vt.grad.numpy()
 
 
-@pytest.mark.parametrize("wl", [W.config1()] + SMALL[:4] + SMALL[-2:], ids=lambda w: w.name)
+@pytest.mark.parametrize("wl", [W.tiny_t28()] + SMALL[:4] + SMALL[-2:], ids=lambda w: w.name)
 def test_union_of_ranks_equals_unpartitioned_and_autograd(wl):
     T = wl.T
     q, k, v, do = wl.q(), wl.k(), wl.v(), wl.do()
@@ -170,8 +170,8 @@ def test_union_of_ranks_equals_unpartitioned_and_autograd(wl):
         np.testing.assert_allclose(dv_sum, ref_dv, rtol=1e-10, atol=1e-10)
 
 
-def test_bwd_central_finite_differences_config1():
-    wl = W.config1()
+def test_bwd_central_finite_differences_tiny_t28():
+    wl = W.tiny_t28()
     q, k, v, do = wl.q(), wl.k(), wl.v(), wl.do()
     rng = np.random.default_rng(5)
     h = 1e-6
@@ -197,7 +197,7 @@ def test_bwd_central_finite_differences_config1():
 
 
 def test_bwd_pads_and_first_token_exact():
-    wl = W.config1()
+    wl = W.tiny_t28()
     q, k, v, do = wl.q(), wl.k(), wl.v(), wl.do()
     _, pos, valid = oracle.token_map(wl.cu_padded, wl.cu_actual)
     for s in wl.strategies:

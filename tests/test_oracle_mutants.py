@@ -47,17 +47,17 @@ def _load_mutant(src):
 
 
 PINS = [
-    TP.test_config1_golden_indices_and_pairs,
-    TP.test_config1_golden_gather_restore_maps,
+    TP.test_tiny_t28_golden_indices_and_pairs,
+    TP.test_tiny_t28_golden_gather_restore_maps,
     lambda: [TP.test_partition_invariants(w) for w in TP._random_layouts()[::7]],
     lambda: [TP.test_packed_super_sequence_on_one_document_is_dual_chunk_swap(cp) for cp in (2, 3)],
     lambda: [TP.test_restore_inverts_all_gather(w) for w in TP._random_layouts()[1::9]],
     lambda: [TP.test_dcs_balances_causal_work_on_unpadded_documents(cp) for cp in (2, 3)],
     lambda: [TA.test_fwd_matches_brute_force(w) for w in TA.SMALL[:3]],
-    TA.test_config1_fwd_brute_force_both_strategies,
+    TA.test_tiny_t28_fwd_brute_force_both_strategies,
     TA.test_first_token_closed_form_and_pads,
     TA.test_fwd_single_unpadded_document_matches_sdpa,
-    lambda: [TA.test_union_of_ranks_equals_unpartitioned_and_autograd(w) for w in [TA.W.config1()]],
+    lambda: [TA.test_union_of_ranks_equals_unpartitioned_and_autograd(w) for w in [TA.W.tiny_t28()]],
     TA.test_bwd_pads_and_first_token_exact,
 ]
 

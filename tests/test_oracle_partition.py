@@ -14,7 +14,7 @@ import pytest
 import oracle
 import workloads as W
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "config1.txt")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "tiny_t28.txt")
 STRAT = {"dcs": oracle.DUAL_CHUNK_SWAP, "contiguous": oracle.NO_LOAD_BALANCE}
 PACKED = oracle.PACKED_SUPER_SEQUENCE
 
@@ -29,9 +29,9 @@ def _golden():
     return out
 
 
-def test_config1_golden_indices_and_pairs():
+def test_tiny_t28_golden_indices_and_pairs():
     g = _golden()
-    wl = W.config1()
+    wl = W.tiny_t28()
     for name, s in STRAT.items():
         for r in (0, 1):
             idx = oracle.partition_indices(wl.cu_padded, 2, r, s)
@@ -39,9 +39,9 @@ def test_config1_golden_indices_and_pairs():
             assert oracle.useful_pairs(idx, wl.cu_padded, wl.cu_actual) == g[f"pairs {name} {r}"][0]
 
 
-def test_config1_golden_gather_restore_maps():
+def test_tiny_t28_golden_gather_restore_maps():
     g = _golden()
-    wl = W.config1()
+    wl = W.tiny_t28()
     parts = [oracle.partition_indices(wl.cu_padded, 2, r, oracle.DUAL_CHUNK_SWAP) for r in (0, 1)]
     phys = np.arange(wl.T)
     assert oracle.all_gather(phys, parts).tolist() == g["gathered_source dcs"]
@@ -154,16 +154,16 @@ def test_check_layout_rejections():
 
 
 def test_workload_layouts_are_valid():
-    for wl in (W.config1(), W.config2(), W.config3(), W.config4()):
+    for wl in (W.tiny_t28(), W.t8192_mha16(), W.t32768_gqa32x8(), W.t131072_gqa64x8()):
         for s in wl.strategies:
             oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
         assert int(wl.cu_padded[-1]) == wl.T
-    for m in range(W.CONFIG5_MICROBATCHES):
-        wl = W.config5(m)
-        assert 4096 <= wl.T <= W.CONFIG5_CAPACITY and wl.T % 64 == 0
+    for m in range(W.DYNAMIC_T_MICROBATCHES):
+        wl = W.dynamic_t(m)
+        assert 4096 <= wl.T <= W.DYNAMIC_T_CAPACITY and wl.T % 64 == 0
         for s in wl.strategies:
             oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
-    cu_p, cu_a = W.config5b()
+    cu_p, cu_a = W.t1m_10k_docs()
     assert cu_p[-1] == 1 << 20 and cu_p.size == 10001
     oracle.check_layout(cu_p, cu_a, 4, oracle.DUAL_CHUNK_SWAP)
 
@@ -210,10 +210,10 @@ def test_batch_on_rank_keeps_global_positions(wl):
 
 
 @pytest.mark.parametrize("strategy", [oracle.NO_LOAD_BALANCE, oracle.PACKED_SUPER_SEQUENCE])
-def test_config4_pairs_sum_to_every_documents_causal_pairs(strategy):
+def test_t131072_gqa64x8_pairs_sum_to_every_documents_causal_pairs(strategy):
     # CP is exact: the ranks' useful pairs add up to every document's causal pairs over its actual tokens,
     # sum of a(a+1)/2.  The per-rank split is what the config's "least and most work" ranks are checked on.
-    wl = W.config4()
+    wl = W.t131072_gqa64x8()
     a = np.diff(wl.cu_actual.astype(np.int64))
     per_rank = [oracle.useful_pairs(oracle.partition_indices(wl.cu_padded, wl.cp, r, strategy), wl.cu_padded,
                                     wl.cu_actual) for r in range(wl.cp)]

@@ -8,18 +8,18 @@ here, and that is the only thing the two sides share.
 Recipes (the pages fix none of the seeds or distributions; these follow the
 workload descriptions of the five measured configurations):
 
-* ``config1``  tiny: three documents of actual lengths 5, 12, 7 in padded slots
+* ``tiny_t28``  tiny: three documents of actual lengths 5, 12, 7 in padded slots
   ``[0, 8, 20, 28]`` (pads between documents), 2 q / 2 kv heads, head dim 16,
   all tensors N(0, 1).
-* ``config2``  T = 8192, lengths ``4 * round(U/4)`` with U uniform on
+* ``t8192_mha16``  T = 8192, lengths ``4 * round(U/4)`` with U uniform on
   [256, 2048], no pads, 16 q / 16 kv heads, head dim 128, Q/K/V ~ 0.5 N(0, 1).
-* ``config3``  T = 32768, actual lengths log-normal (median 1024, sigma 1)
+* ``t32768_gqa32x8``  T = 32768, actual lengths log-normal (median 1024, sigma 1)
   clipped to [64, 8192], slots padded up to a multiple of 8, 32 q / 8 kv heads.
-* ``config4``  T = 131072, lengths uniform integers on [1, 16384], no pads,
+* ``t131072_gqa64x8``  T = 131072, lengths uniform integers on [1, 16384], no pads,
   64 q / 8 kv heads.
-* ``config5``  16 micro-batches, active T = 64 * U with U uniform on [64, 1024],
-  lengths as config 3 but clipped to [32, 8192], on a 65536-token capacity.
-* ``config5b`` T = 1,048,576 in 10,000 documents: 8 times a uniformly random
+* ``dynamic_t``  16 micro-batches, active T = 64 * U with U uniform on [64, 1024],
+  lengths as t32768_gqa32x8 but clipped to [32, 8192], on a 65536-token capacity.
+* ``t1m_10k_docs`` T = 1,048,576 in 10,000 documents: 8 times a uniformly random
   composition of 131072 into 10,000 positive parts (partition indices only).
 
 In every recipe the last document is trimmed so the padded lengths sum to T
@@ -191,44 +191,44 @@ class Workload:
 DCS, CONTIG, PACKED = 0, 1, 2   # strategy codes as passed to both sides (enum values of the C ABI)
 
 
-def config1(bf16=False) -> Workload:
+def tiny_t28(bf16=False) -> Workload:
     cu_p = np.array([0, 8, 20, 28], dtype=np.int32)
     cu_a = np.array([0, 5, 17, 24], dtype=np.int32)
-    return Workload("config1", [0], 28, 2, 2, 16, cu_p, cu_a, 2, (DCS, CONTIG), (0, 1), True,
+    return Workload("tiny_t28", [0], 28, 2, 2, 16, cu_p, cu_a, 2, (DCS, CONTIG), (0, 1), True,
                     qkv_scale=1.0, do_scale=1.0, bf16=bf16)
 
 
-def config2() -> Workload:
+def t8192_mha16() -> Workload:
     rng = np.random.default_rng(2)
     p, a = docs_uniform_mult4(rng, 8192)
-    return Workload("config2", [2], 8192, 16, 16, 128, _cu(p), _cu(a), 2, (DCS, CONTIG), (0, 1), False)
+    return Workload("t8192_mha16", [2], 8192, 16, 16, 128, _cu(p), _cu(a), 2, (DCS, CONTIG), (0, 1), False)
 
 
-def config3() -> Workload:
+def t32768_gqa32x8() -> Workload:
     rng = np.random.default_rng(3)
     p, a = docs_lognormal(rng, 32768, 64, 8192)
-    return Workload("config3", [3], 32768, 32, 8, 128, _cu(p), _cu(a), 4, (DCS, CONTIG), (0, 3), True)
+    return Workload("t32768_gqa32x8", [3], 32768, 32, 8, 128, _cu(p), _cu(a), 4, (DCS, CONTIG), (0, 3), True)
 
 
-def config4() -> Workload:
+def t131072_gqa64x8() -> Workload:
     rng = np.random.default_rng(4)
     p, a = docs_uniform_any(rng, 131072)
-    return Workload("config4", [4], 131072, 64, 8, 128, _cu(p), _cu(a), 8, (CONTIG,), (0, 7), True)
+    return Workload("t131072_gqa64x8", [4], 131072, 64, 8, 128, _cu(p), _cu(a), 8, (CONTIG,), (0, 7), True)
 
 
-CONFIG5_CAPACITY = 65536
-CONFIG5_MICROBATCHES = 16
+DYNAMIC_T_CAPACITY = 65536
+DYNAMIC_T_MICROBATCHES = 16
 
 
-def config5(m: int) -> Workload:
+def dynamic_t(m: int) -> Workload:
     rng = np.random.default_rng([5, m])
     T = 64 * int(rng.integers(64, 1025))
     p, a = docs_lognormal(rng, T, 32, 8192)
-    return Workload(f"config5.mb{m}", [5, m], T, 32, 8, 128, _cu(p), _cu(a), 4, (DCS, CONTIG), (0, 1, 2, 3),
-                    True, capacity=CONFIG5_CAPACITY)
+    return Workload(f"dynamic_t.mb{m}", [5, m], T, 32, 8, 128, _cu(p), _cu(a), 4, (DCS, CONTIG), (0, 1, 2, 3),
+                    True, capacity=DYNAMIC_T_CAPACITY)
 
 
-def config5b():
+def t1m_10k_docs():
     """Partition-only layout: 1,048,576 tokens in 10,000 documents (multiples of 8)."""
     rng = np.random.default_rng(55)
     p, a = docs_composition(rng, 131072, 10000, 8)
