@@ -11,10 +11,16 @@ cp_size = 4, ranks 0 and 3, both strategies).  For every share:
 Inputs are resident in HBM before the timed region.  The metric is useful
 causal attention FLOP/s: forward 4*D*Hq*N, backward 10*D*Hq*N, with N the
 number of (query, key) pairs the causal document mask allows for the share's
-actual query rows.  The same shares are then timed once more with attention
-reading the rank-major gathered K/V directly (no restoration pass), reported
-under breakdown.allgathered_path.  Prints one JSON line; progress goes to
-stderr.
+actual query rows.  Extra legs (skipped with --no-allgathered, as in profiling
+runs), reported under breakdown:
+  allgathered_path          the same shares with attention reading the
+                            rank-major gathered K/V directly (no restoration);
+  graph_replayed_step       the main step replayed from a HIP graph;
+  partition_million_tokens  the partition kernel alone at T = 1,048,576 in
+                            10,000 documents, every rank and strategy;
+  dynamic_t_sweep           every share of 16 micro-batches of varying active T
+                            on buffers allocated once for 65,536 tokens.
+Prints one JSON line; progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -156,6 +162,87 @@ def cpu_baseline(wl, budget_s=15.0):
             "sample": f"fwd+bwd of {heads} of {wl.Hkv} kv heads ({heads * G} of {wl.Hq} q heads) of the "
                       f"DualChunkSwap rank-0 share, all {wl.num_docs} documents ({pairs} causal pairs per head), "
                       f"float64 numpy, {dt:.1f} s"}
+
+
+def dynamic_t_sweep(cpthd, torch, dev, status, reps=3):
+    """The dynamic-T micro-batch sweep on buffers allocated once for 65,536 tokens: 16 micro-batches whose active
+    T varies (multiples of 64 in [4096, 65536]), cp_size 4, both strategies, every rank; each share runs the
+    full step (partition, restoration under DualChunkSwap, plan, forward, backward) on the active prefix.  Per
+    micro-batch the eight shares' inputs are staged first, then the eight steps run back-to-back between two
+    events (reps times, after one untimed pass).  Tensor values are drawn on the GPU (timing only)."""
+    cap, cp = W.DYNAMIC_T_CAPACITY, 4
+    Hq, Hkv, D = 32, 8, 128
+    scale = 1.0 / math.sqrt(D)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+
+    def randn(shape, sd):
+        return (torch.randn(shape, generator=gen, device=dev) * sd).to(torch.bfloat16)
+
+    k_phys, v_phys = randn((cap, Hkv, D), 0.5), randn((cap, Hkv, D), 0.5)
+    q_full, do_full = randn((cap, Hq, D), 0.5), randn((cap, Hq, D), 1.0)
+    capS = cap // cp
+    kg, vg = torch.empty_like(k_phys), torch.empty_like(v_phys)
+    k_buf, v_buf = torch.empty_like(k_phys), torch.empty_like(v_phys)
+    o = torch.empty((capS, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((capS, Hq), dtype=torch.float32, device=dev)
+    dq = torch.empty((capS, Hq, D), dtype=torch.float32, device=dev)
+    dk = torch.empty((cap, Hkv, D), dtype=torch.float32, device=dev)
+    dv = torch.empty((cap, Hkv, D), dtype=torch.float32, device=dev)
+    idx_out = torch.empty(capS, dtype=torch.int32, device=dev)
+    layouts = [W.dynamic_t(m) for m in range(W.DYNAMIC_T_MICROBATCHES)]
+    plan = cpthd.AttnPlan(cap, cp, Hq, Hkv, D, max_docs=max(wl.num_docs for wl in layouts))
+    q_loc = [torch.empty((capS, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(cp)]
+    do_loc = [torch.empty((capS, Hq, D), dtype=torch.bfloat16, device=dev) for _ in range(cp)]
+    total_ms, flops = 0.0, {0: 0.0, 1: 0.0}
+    ms_by_strategy = {0: 0.0, 1: 0.0}
+    for wl in layouts:
+        T, S = wl.T, wl.T // cp
+        cu_a = torch.from_numpy(wl.cu_actual).to(dev)
+        cu_p = torch.from_numpy(wl.cu_padded).to(dev)
+        for s in (0, 1):
+            # staging (untimed): the ranks' local Q / dO rows and, under DualChunkSwap, the rank-major gathered K/V
+            parts = [cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status) for r in range(cp)]
+            for r in range(cp):
+                q_loc[r][:S] = q_full[parts[r].long()]
+                do_loc[r][:S] = do_full[parts[r].long()]
+                flops[s] += 14.0 * D * Hq * useful_pairs(parts[r].cpu().numpy().astype(np.int64), wl.cu_padded,
+                                                          wl.cu_actual)
+            if s == 0:
+                order = torch.cat(parts).long()
+                kg[:T], vg[:T] = k_phys[:T][order], v_phys[:T][order]
+                k_in, v_in = k_buf, v_buf
+            else:
+                k_in, v_in = k_phys, v_phys
+
+            def shares():
+                for r in range(cp):
+                    cpthd.partition_indices(cu_p, T, cp, r, s, out=idx_out, dev_status=status)
+                    if s == 0:
+                        cpthd.reorder_kv(kg, vg, cu_p, T, cp, 0, k_out=k_buf, v_out=v_buf, dev_status=status)
+                    plan.build(cu_a, cu_p, T, r, s, status)
+                    cpthd.attn_fwd(q_loc[r], k_in, v_in, plan, scale, o, lse, status)
+                    cpthd.attn_bwd(q_loc[r], k_in, v_in, o, do_loc[r], lse, plan, scale, dq, dk, dv, status)
+
+            shares()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                shares()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            total_ms += ms
+            ms_by_strategy[s] += ms
+    cpthd.check_dev_status(status)
+    all_flops = flops[0] + flops[1]
+    return {"microbatches": len(layouts), "shares": 2 * cp * len(layouts),
+            "active_T": [int(min(wl.T for wl in layouts)), int(max(wl.T for wl in layouts))],
+            "capacity_tokens": cap, "ms_per_sweep": total_ms,
+            "tflops": all_flops / (total_ms * 1e-3) / 1e12,
+            "tflops_by_strategy": {STRAT_NAME[s]: flops[s] / (ms_by_strategy[s] * 1e-3) / 1e12 for s in (0, 1)},
+            "note": "every (micro-batch, strategy, rank) share's full step; useful fwd+bwd flops over GPU time"}
 
 
 def main():
@@ -382,6 +469,11 @@ def main():
                             "latency-bound"}
         log(f"partition at T={T_big}: {np.mean(us):.2f} us per call")
 
+    dyn = None
+    if not args.no_allgathered:
+        dyn = dynamic_t_sweep(cpthd, torch, dev, status)
+        log(f"dynamic-T sweep: {dyn['tflops']:.1f} TFLOP/s over {dyn['shares']} shares")
+
     # HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V), and the
     # restoration alone, each cold (a 512 MiB write before every rep evicts the 256 MiB last-level cache) and
     # the copy also warm (the source left in that cache, as inside the step)
@@ -457,6 +549,8 @@ def main():
         "attn_frac_of_bf16_peak": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS),
         "partition_gbs": float(part_bytes / (per_kernel_ms[:, 0].mean() * 1e-3) / 1e9),
         "partition_million_tokens": part_big,
+        # the dynamic-T micro-batch sweep on capacity buffers (65,536 tokens): every share of 16 micro-batches
+        "dynamic_t_sweep": dyn,
         "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
         "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
         "reorder_gbs_cold": reorder_cold,
