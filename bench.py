@@ -19,7 +19,9 @@ runs), reported under breakdown:
   partition_million_tokens  the partition kernel alone at T = 1,048,576 in
                             10,000 documents, every rank and strategy;
   dynamic_t_sweep           every share of 16 micro-batches of varying active T
-                            on buffers allocated once for 65,536 tokens.
+                            on buffers allocated once for 65,536 tokens;
+  long_context_shares       contiguous ranks 0 and 7 of the 70B-shaped
+                            T = 131,072 workload (64 q / 8 kv heads, cp_size 8).
 Prints one JSON line; progress goes to stderr.
 """
 from __future__ import annotations
@@ -243,6 +245,60 @@ def dynamic_t_sweep(cpthd, torch, dev, status, reps=3):
             "tflops": all_flops / (total_ms * 1e-3) / 1e12,
             "tflops_by_strategy": {STRAT_NAME[s]: flops[s] / (ms_by_strategy[s] * 1e-3) / 1e12 for s in (0, 1)},
             "note": "every (micro-batch, strategy, rank) share's full step; useful fwd+bwd flops over GPU time"}
+
+
+def long_context_shares(cpthd, torch, dev, status, reps=3):
+    """The 70B-shaped long-context workload (T = 131,072 packed tokens, documents of 1 to 16,384 tokens, 64 q /
+    8 kv heads, head dim 128, cp_size 8, contiguous strategy): ranks 0 and 7, each share's full step (partition,
+    plan, forward, backward; contiguous ownership needs no restoration), timed between two events over reps
+    repetitions after one untimed pass.  Tensor values are drawn on the GPU (timing only)."""
+    wl = W.t131072_gqa64x8()
+    T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
+    S = T // cp
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+
+    def randn(shape, sd):
+        return (torch.randn(shape, generator=gen, device=dev) * sd).to(torch.bfloat16)
+
+    k, v = randn((T, Hkv, D), 0.5), randn((T, Hkv, D), 0.5)
+    cu_a = torch.from_numpy(wl.cu_actual).to(dev)
+    cu_p = torch.from_numpy(wl.cu_padded).to(dev)
+    plan = cpthd.AttnPlan(T, cp, Hq, Hkv, D, max_docs=wl.num_docs)
+    idx = torch.empty(S, dtype=torch.int32, device=dev)
+    o = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+    dq = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+    dk = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+    dv = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+    scale = 1.0 / math.sqrt(D)
+    out = []
+    for r in (0, cp - 1):
+        q, do = randn((S, Hq, D), 0.5), randn((S, Hq, D), 1.0)
+        pairs = useful_pairs(cpthd.partition_indices(cu_p, T, cp, r, 1, dev_status=status).cpu().numpy()
+                             .astype(np.int64), wl.cu_padded, wl.cu_actual)
+
+        def share():
+            cpthd.partition_indices(cu_p, T, cp, r, 1, out=idx, dev_status=status)
+            plan.build(cu_a, cu_p, T, r, 1, status)
+            cpthd.attn_fwd(q, k, v, plan, scale, o, lse, status)
+            cpthd.attn_bwd(q, k, v, o, do, lse, plan, scale, dq, dk, dv, status)
+
+        share()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            share()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out.append({"rank": r, "causal_pairs_per_head": int(pairs), "ms": ms,
+                    "tflops": 14.0 * D * Hq * pairs / (ms * 1e-3) / 1e12})
+        del q, do
+    cpthd.check_dev_status(status)
+    return {"T": T, "cp_size": cp, "num_q_heads": Hq, "num_kv_heads": Hkv, "num_docs": wl.num_docs,
+            "strategy": "contiguous", "shares": out}
 
 
 def main():
@@ -473,6 +529,10 @@ def main():
     if not args.no_allgathered:
         dyn = dynamic_t_sweep(cpthd, torch, dev, status)
         log(f"dynamic-T sweep: {dyn['tflops']:.1f} TFLOP/s over {dyn['shares']} shares")
+    longc = None
+    if not args.no_allgathered:
+        longc = long_context_shares(cpthd, torch, dev, status)
+        log("long context: " + ", ".join(f"rank {x['rank']} {x['tflops']:.1f} TFLOP/s" for x in longc["shares"]))
 
     # HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V), and the
     # restoration alone, each cold (a 512 MiB write before every rep evicts the 256 MiB last-level cache) and
@@ -551,6 +611,8 @@ def main():
         "partition_million_tokens": part_big,
         # the dynamic-T micro-batch sweep on capacity buffers (65,536 tokens): every share of 16 micro-batches
         "dynamic_t_sweep": dyn,
+        # the 70B-shaped long-context workload (T = 131,072, 64 q / 8 kv heads, cp_size 8): contiguous ranks 0, 7
+        "long_context_shares": longc,
         "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
         "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
         "reorder_gbs_cold": reorder_cold,
