@@ -21,7 +21,9 @@ runs), reported under breakdown:
   dynamic_t_sweep           every share of 16 micro-batches of varying active T
                             on buffers allocated once for 65,536 tokens;
   long_context_shares       contiguous ranks 0 and 7 of the 70B-shaped
-                            T = 131,072 workload (64 q / 8 kv heads, cp_size 8).
+                            T = 131,072 workload (64 q / 8 kv heads, cp_size 8);
+  short_mha_forward         the forward-only T = 8,192 workload (16 q / 16 kv
+                            heads, cp_size 2), both strategies, ranks 0 and 1.
 Prints one JSON line; progress goes to stderr.
 """
 from __future__ import annotations
@@ -301,6 +303,65 @@ def long_context_shares(cpthd, torch, dev, status, reps=3):
             "strategy": "contiguous", "shares": out}
 
 
+def short_mha_forward(cpthd, torch, dev, status, reps=10):
+    """The forward-only workload of T = 8,192 packed tokens (documents of 256 to 2,048 tokens, 16 q / 16 kv
+    heads, head dim 128, cp_size 2): ranks 0 and 1 under both strategies, each share's partition, restoration
+    (DualChunkSwap), plan and forward, timed between two events over reps repetitions after one untimed pass.
+    Tensor values are drawn on the GPU (timing only)."""
+    wl = W.t8192_mha16()
+    T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
+    S = T // cp
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(2)
+
+    def randn(shape, sd):
+        return (torch.randn(shape, generator=gen, device=dev) * sd).to(torch.bfloat16)
+
+    k_phys, v_phys = randn((T, Hkv, D), 0.5), randn((T, Hkv, D), 0.5)
+    cu_a = torch.from_numpy(wl.cu_actual).to(dev)
+    cu_p = torch.from_numpy(wl.cu_padded).to(dev)
+    plan = cpthd.AttnPlan(T, cp, Hq, Hkv, D, max_docs=wl.num_docs)
+    idx = torch.empty(S, dtype=torch.int32, device=dev)
+    o = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+    k_buf, v_buf = torch.empty_like(k_phys), torch.empty_like(v_phys)
+    scale = 1.0 / math.sqrt(D)
+    out, flops_all, ms_all = [], 0.0, 0.0
+    for s in (0, 1):
+        parts = [cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status) for r in range(cp)]
+        order = torch.cat(parts).long()
+        kg, vg = (k_phys[order].contiguous(), v_phys[order].contiguous()) if s == 0 else (k_phys, v_phys)
+        k_in, v_in = (k_buf, v_buf) if s == 0 else (k_phys, v_phys)
+        for r in range(cp):
+            q = randn((S, Hq, D), 0.5)
+            pairs = useful_pairs(parts[r].cpu().numpy().astype(np.int64), wl.cu_padded, wl.cu_actual)
+
+            def share():
+                cpthd.partition_indices(cu_p, T, cp, r, s, out=idx, dev_status=status)
+                if s == 0:
+                    cpthd.reorder_kv(kg, vg, cu_p, T, cp, 0, k_out=k_buf, v_out=v_buf, dev_status=status)
+                plan.build(cu_a, cu_p, T, r, s, status)
+                cpthd.attn_fwd(q, k_in, v_in, plan, scale, o, lse, status)
+
+            share()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                share()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            fl = 4.0 * D * Hq * pairs
+            flops_all += fl
+            ms_all += ms
+            out.append({"strategy": STRAT_NAME[s], "rank": r, "causal_pairs_per_head": int(pairs), "us": ms * 1e3,
+                        "tflops": fl / (ms * 1e-3) / 1e12})
+    cpthd.check_dev_status(status)
+    return {"T": T, "cp_size": cp, "num_q_heads": Hq, "num_kv_heads": Hkv, "num_docs": wl.num_docs,
+            "pass": "forward", "tflops": flops_all / (ms_all * 1e-3) / 1e12, "shares": out}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -529,6 +590,10 @@ def main():
     if not args.no_allgathered:
         dyn = dynamic_t_sweep(cpthd, torch, dev, status)
         log(f"dynamic-T sweep: {dyn['tflops']:.1f} TFLOP/s over {dyn['shares']} shares")
+    shortf = None
+    if not args.no_allgathered:
+        shortf = short_mha_forward(cpthd, torch, dev, status)
+        log(f"short MHA forward: {shortf['tflops']:.1f} TFLOP/s over {len(shortf['shares'])} shares")
     longc = None
     if not args.no_allgathered:
         longc = long_context_shares(cpthd, torch, dev, status)
@@ -613,6 +678,8 @@ def main():
         "dynamic_t_sweep": dyn,
         # the 70B-shaped long-context workload (T = 131,072, 64 q / 8 kv heads, cp_size 8): contiguous ranks 0, 7
         "long_context_shares": longc,
+        # the forward-only T = 8,192 workload (16 q / 16 kv heads, cp_size 2): both strategies, ranks 0 and 1
+        "short_mha_forward": shortf,
         "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
         "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
         "reorder_gbs_cold": reorder_cold,
