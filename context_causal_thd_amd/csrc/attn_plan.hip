@@ -105,12 +105,10 @@ __device__ inline int kv_tile_cost(const DocSeg& d, int k0, int G) {
   return cost;
 }
 
+// Counting sort of n tiles by cost, longest first; s_hist holds the count of
+// tiles per cost bin (filled while the tiles were emitted).
 template <typename Tile>
 __device__ void sort_by_cost_desc(const Tile* tmp, Tile* out, int n, int* s_hist, int* s_wave) {
-  for (int b = threadIdx.x; b < kCostBins; b += kPlanThreads) s_hist[b] = 0;
-  __syncthreads();
-  for (int t = threadIdx.x; t < n; t += kPlanThreads) atomicAdd(&s_hist[min(tmp[t].cost, kCostBins - 1)], 1);
-  __syncthreads();
   // position of bin b = number of tiles in bins above b
   const int hi = kCostBins - 1 - 2 * threadIdx.x;
   const int v0 = s_hist[hi], v1 = s_hist[hi - 1];
@@ -134,7 +132,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   __shared__ int s_bits;
   __shared__ int s_wave[40];
   __shared__ int s_qoff[kPlanThreads], s_kvoff[kPlanThreads];
-  __shared__ int s_hist[kCostBins];
+  __shared__ int s_hist_q[kCostBins], s_hist_kv[kCostBins];   // tiles per cost bin, counted at emission
+  __shared__ DocSeg s_docs[kPlanThreads];                       // this chunk's documents
+  __shared__ int s_len[kPlanThreads];                           // and their padded lengths
 
   PlanHeader* hdr = reinterpret_cast<PlanHeader*>(ws);
   QTile* qt = reinterpret_cast<QTile*>(ws + lay.qtiles);
@@ -177,6 +177,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
 
   // 2. documents in chunks of 1024: segments, tile counts, scan, emission
+  for (int b = tid; b < kCostBins; b += kPlanThreads) s_hist_q[b] = s_hist_kv[b] = 0;   // (the scans' barriers
+                                                                                          //  order this first)
   int carry_q = 0, carry_kv = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int i = base + tid;
@@ -185,8 +187,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     if (i < B) {
       const DocSeg d = doc_segments(cu_a, cu_p, i, S, cp, rank, strategy);
       docs[i] = d;
+      s_docs[tid] = d;
+      s_len[tid] = cu_p[i + 1] - d.ds;
       nq = cdiv(d.na, bm) + cdiv(d.nb, bm);
-      nkv = cdiv(cu_p[i + 1] - d.ds, kKeysPerWG);
+      nkv = cdiv(s_len[tid], kKeysPerWG);
     }
     int tq, tkv;
     const int oq = block_exclusive_scan(nq, s_wave, tq);
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         const int mid = (lo + hi + 1) >> 1;
         if (s_qoff[mid] <= t) lo = mid; else hi = mid - 1;
       }
-      const DocSeg d = docs[base + lo];
+      const DocSeg d = s_docs[lo];
       int k = t - s_qoff[lo];
       const int nA = cdiv(d.na, bm);
       QTile e;
@@ -221,6 +225,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       e.cost = cdiv(e.kv_end - d.ds, kKvStep);
       e.doc = base + lo;
       qtmp[carry_q + t] = e;
+      atomicAdd(&s_hist_q[min(e.cost, kCostBins - 1)], 1);
     }
     for (int t = tid; t < tkv; t += kPlanThreads) {
       int lo = 0, hi = cnt - 1;
@@ -228,15 +233,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
         const int mid = (lo + hi + 1) >> 1;
         if (s_kvoff[mid] <= t) lo = mid; else hi = mid - 1;
       }
-      const DocSeg d = docs[base + lo];
+      const DocSeg d = s_docs[lo];
       const int k = t - s_kvoff[lo];
-      const int L = cu_p[base + lo + 1] - d.ds;
+      const int L = s_len[lo];
       KVTile e;
       e.k0 = d.ds + k * kKeysPerWG;
       e.nkeys = min(kKeysPerWG, L - k * kKeysPerWG);
       e.doc = base + lo;
       e.cost = kv_tile_cost(d, e.k0, G);
       kvtmp[carry_kv + t] = e;
+      atomicAdd(&s_hist_kv[min(e.cost, kCostBins - 1)], 1);
     }
     carry_q += tq;
     carry_kv += tkv;
@@ -245,8 +251,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   }
 
   // 3. longest first
-  sort_by_cost_desc(qtmp, qt, carry_q, s_hist, s_wave);
-  sort_by_cost_desc(kvtmp, kvt, carry_kv, s_hist, s_wave);
+  __threadfence_block();
+  __syncthreads();
+  sort_by_cost_desc(qtmp, qt, carry_q, s_hist_q, s_wave);
+  sort_by_cost_desc(kvtmp, kvt, carry_kv, s_hist_kv, s_wave);
 
   // 4. header last
   if (tid == 0) {
