@@ -138,13 +138,14 @@ constexpr int kReorderRowsPerWave = CPTHD_REORDER_ROWS;
 #endif
 constexpr int kReorderChunks = CPTHD_REORDER_CHUNKS;
 
-__device__ inline int64_t gathered_row_of(const int32_t* cu, int B, int S, int cp, int strategy, int p) {
+// Gathered row of physical row p; under DualChunkSwap `doc` is the document
+// holding p (unused otherwise).
+__device__ inline int64_t gathered_row_of(const int32_t* cu, int doc, int S, int cp, int strategy, int p) {
   if (strategy == kContig) return p;
   int start = 0, L = cp * S;                      // whole buffer as one sequence (packed strategy)
   if (strategy == kDCS) {
-    const int i = upper_index(cu, B - 1, p);     // document holding physical row p
-    start = cu[i];
-    L = cu[i + 1] - start;
+    start = cu[doc];
+    L = cu[doc + 1] - start;
   }
   const int c = L / (2 * cp);
   if (c <= 0) return p;                           // only for a rejected layout
@@ -169,11 +170,16 @@ __global__ __launch_bounds__(256) void reorder_kernel(const char* __restrict__ k
   const int64_t row0 = ((int64_t)blockIdx.x * 4 + wave) * R;
   const int nrows = (int)min((int64_t)R, (int64_t)T - row0);
   if (nrows <= 0) return;
+  // the document of the wave's first row, found by all lanes together; the
+  // wave's other rows are at most R - 1 rows further on
+  int doc = strategy == kDCS ? wave_upper_index(cu, B, row0, lane) : 0;
   int64_t g[R];
 #pragma unroll
   for (int rr = 0; rr < R; ++rr) {
     const int64_t p = min(row0 + rr, (int64_t)T - 1);
-    const int64_t gr = gathered_row_of(cu, B, S, cp, strategy, (int)p);
+    if (strategy == kDCS)
+      while (doc < B - 1 && (int64_t)cu[doc + 1] <= p) ++doc;
+    const int64_t gr = gathered_row_of(cu, doc, S, cp, strategy, (int)p);
     g[rr] = __builtin_amdgcn_readfirstlane((int)min(max(gr, (int64_t)0), (int64_t)T - 1));
   }
   const int64_t n16 = row_bytes / 16;
