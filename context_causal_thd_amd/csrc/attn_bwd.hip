@@ -70,20 +70,14 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
   __shared__ __align__(16) uint16_t V0[VT::ELEMS], V1[VT::ELEMS];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
-  if (!plan_matches(hdr, prm)) {
-    if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
-    return;
-  }
   // kDqSplit work-groups per query tile, each with kRowsPerWG / kDqSplit of its rows; the kv head stays
   // blockIdx mod Hkv
   const int kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
   const int tile = blockIdx.x / (prm.Hkv * kDqSplit), part = (blockIdx.x / prm.Hkv) % kDqSplit;
-  if (tile >= hdr->n_qtiles) return;
-  QTile t;
-  if (!load_qtile(ws, lay, tile, prm, t)) {
-    if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
-    return;
-  }
+  // the tile is read beside the header (the workspace holds a tile slot for
+  // every query tile the launch can have); it is used only once both check out
+  const QTile t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[tile];
+  if (!tile_usable(plan_matches(hdr, prm), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
   float* ndelta = reinterpret_cast<float*>(ws + lay.delta);   // -delta per row, for the key-tile pass
   float* lse2w = reinterpret_cast<float*>(ws + lay.lse2);
 
@@ -316,18 +310,13 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
   __shared__ __align__(16) bf16x8 X[SD == 2 ? 4 * 2 * 4 * 64 : 1];   // [key group][query block][P0,P1,dS0,dS1][lane]
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
-  if (!plan_matches(hdr, prm)) {
-    if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
-    return;
-  }
   const int tile = blockIdx.x / prm.Hkv, kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
-  if (tile >= hdr->n_kvtiles) return;
+  // the tile is read beside the header (the workspace holds a tile slot for
+  // every work-group the launch can have); it is used only once both check out
   const KVTile kt = reinterpret_cast<const KVTile*>(ws + lay.kvtiles)[tile];
-  if (kt.doc < 0 || kt.doc >= prm.num_docs || kt.k0 < 0 || kt.nkeys < 0 || kt.nkeys > kKeysPerWG ||
-      kt.k0 > prm.T - kt.nkeys) {
-    if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
-    return;
-  }
+  const bool kt_ok = (kt.doc >= 0) & (kt.doc < prm.num_docs) & (kt.k0 >= 0) & (kt.nkeys >= 0) &
+                     (kt.nkeys <= kKeysPerWG) & (kt.k0 <= prm.T - kt.nkeys);
+  if (!tile_usable(plan_matches(hdr, prm), tile < hdr->n_kvtiles, kt_ok, status)) return;
   const DocSeg ds = reinterpret_cast<const DocSeg*>(ws + lay.docs)[kt.doc];
   const float* ndelta = reinterpret_cast<const float*>(ws + lay.delta);
   const float* lse2w = reinterpret_cast<const float*>(ws + lay.lse2);

@@ -19,19 +19,32 @@ struct AttnParams {
 };
 
 // A plan is usable iff it was built for exactly these arguments.
-__device__ inline bool plan_matches(const PlanHeader* h, const AttnParams& p) {
-  return h->valid == 1 && h->magic == kPlanMagic && h->version == kPlanVersion && h->T == p.T && h->S == p.S &&
-         h->cp == p.cp && h->rank == p.rank && h->strategy == p.strategy && h->Hq == p.Hq && h->Hkv == p.Hkv &&
-         h->D == p.D && h->num_docs == p.num_docs;
+// Every field is compared (bitwise &, no short circuit), so the header is read
+// in a few wide loads instead of a chain of dependent ones.
+__device__ inline bool plan_matches(const PlanHeader* hp, const AttnParams& p) {
+  const PlanHeader h = *hp;
+  return (h.valid == 1) & (h.magic == kPlanMagic) & (h.version == kPlanVersion) & (h.T == p.T) & (h.S == p.S) &
+         (h.cp == p.cp) & (h.rank == p.rank) & (h.strategy == p.strategy) & (h.Hq == p.Hq) & (h.Hkv == p.Hkv) &
+         (h.D == p.D) & (h.num_docs == p.num_docs);
 }
 
-// Load a query tile descriptor and clamp it to the tensors' extents.
-__device__ inline bool load_qtile(const char* ws, const PlanLayout& lay, int idx, const AttnParams& p, QTile& t) {
-  t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[idx];
-  if (t.lrow0 < 0 || t.ntok < 0 || t.lrow0 > p.S - t.ntok) return false;
-  if (t.ds < 0 || t.ds > p.T || t.kv_end < t.ds || t.kv_end > p.T || t.p0 < 0 || t.p0 > p.T - t.ntok) return false;
-  if (t.doc < 0 || t.doc >= p.num_docs) return false;
-  return true;
+// Check a query tile descriptor against the tensors' extents (bitwise, so
+// its fields load together).
+__device__ inline bool check_qtile(const QTile& t, const AttnParams& p) {
+  return (t.lrow0 >= 0) & (t.ntok >= 0) & (t.lrow0 <= p.S - t.ntok) & (t.ds >= 0) & (t.ds <= p.T) &
+         (t.kv_end >= t.ds) & (t.kv_end <= p.T) & (t.p0 >= 0) & (t.p0 <= p.T - t.ntok) & (t.doc >= 0) &
+         (t.doc < p.num_docs);
+}
+
+// The start of every attention work-group: is the plan the one built for these
+// arguments, is the work-group's tile in it, and is the tile sound?  Evaluated
+// without short circuits and decided by one branch, so the header and the tile
+// are read in one round of loads.  A mismatched plan or an unsound tile sets the
+// plan bit of the device status; a tile past the plan's count is only surplus.
+__device__ inline bool tile_usable(bool plan_ok, bool in_range, bool tile_ok, int32_t* status) {
+  if (plan_ok & in_range & tile_ok) return true;
+  if (threadIdx.x == 0 && status && (!plan_ok || (in_range && !tile_ok))) atomicOr(status, kDevPlan);
+  return false;
 }
 
 // Row of the rank-major all-gathered K/V buffer (rank 0's local rows, then

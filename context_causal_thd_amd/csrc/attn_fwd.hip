@@ -56,17 +56,11 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   __shared__ __align__(16) uint16_t V0[VT::ELEMS], V1[VT::ELEMS];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
-  if (!plan_matches(hdr, prm)) {
-    if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
-    return;
-  }
   const int tile = blockIdx.x / prm.Hkv, kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
-  if (tile >= hdr->n_qtiles) return;
-  QTile t;
-  if (!load_qtile(ws, lay, tile, prm, t)) {
-    if (threadIdx.x == 0 && status) atomicOr(status, kDevPlan);
-    return;
-  }
+  // the tile is read beside the header (the workspace holds a tile slot for
+  // every work-group the launch can have); it is used only once both check out
+  const QTile t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[tile];
+  if (!tile_usable(plan_matches(hdr, prm), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
 
   const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
