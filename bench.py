@@ -89,7 +89,7 @@ def measured_traffic(kernel):
 
 
 class ClockSampler:
-    """Samples the GPU shader clock (the starred level of the driver's pp_dpm_sclk file) every 2 ms from a
+    """Samples the GPU shader clock (the starred level of the amdgpu kernel driver's pp_dpm_sclk file) every 2 ms from a
     background thread while the timed steps run; reads a file, starts nothing."""
 
     def __init__(self):
@@ -377,8 +377,8 @@ def main():
                          "restoration kernel in contiguous mode, as the reference for HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU's rank share only; run it with --gpus 1 (the multi-GPU all-gather / "
-              "reduce-scatter path is not part of this build)", file=sys.stderr)
+        print("bench.py measures one GPU's rank share only; run it with --gpus 1 (the library holds the per-rank "
+              "kernels; the multi-GPU all-gather and reduce-scatter around them are not implemented)", file=sys.stderr)
         sys.exit(2)
 
     import torch

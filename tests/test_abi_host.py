@@ -182,3 +182,15 @@ def test_allgathered_attention_host_errors(lib):
             == d["CPTHD_ERR_TOKENS"]
         assert bwd(P, P, P, P, P, P, T, T, 16, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, P, wsb, None, None,
                    None, 0) == d["CPTHD_ERR_TOKENS"]
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU's rank share: asked for more GPUs it exits with status 2 and says why, before
+    touching the GPU."""
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "--gpus 1" in r.stderr
