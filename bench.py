@@ -1,27 +1,31 @@
 """Throughput of one CP rank's share of causal THD attention on one MI355X.
 
 A step is one pass of the whole hot path over the configured rank shares of
-the Llama-3-8B-shaped packed workload (T = 32768 bf16 tokens, 32 q / 8 kv
-heads, head dim 128, log-normal document lengths padded to multiples of 8,
-cp_size = 4, ranks 0 and 3, both strategies).  For every share:
+the 70B-shaped long-context workload (T = 131,072 packed bf16 tokens,
+documents of 1 to 16,384 tokens, 64 q / 8 kv heads, head dim 128, cp_size 8,
+contiguous strategy, ranks 0 and 7; the largest workload that fits one GPU).
+For every share:
 
-  partition indices -> (DualChunkSwap: K/V restoration from the rank-major
-  gathered buffer) -> attention plan -> forward (O, LSE) -> backward (dQ, dK, dV)
+  partition indices -> K/V restoration (the contiguous strategy's gathered
+  buffer is already in physical order: the call has nothing to do) ->
+  attention plan -> forward (O, LSE) -> backward (dQ, dK, dV)
 
-Inputs are resident in HBM before the timed region.  The metric is useful
-causal attention FLOP/s: forward 4*D*Hq*N, backward 10*D*Hq*N, with N the
-number of (query, key) pairs the causal document mask allows for the share's
-actual query rows.  Extra legs (skipped with --no-allgathered, as in profiling
-runs), reported under breakdown:
-  allgathered_path          the same shares with attention reading the
-                            rank-major gathered K/V directly (no restoration);
+Inputs are the workload's seeded values, resident in HBM before the timed
+region.  The metric is useful causal attention FLOP/s: forward 4*D*Hq*N,
+backward 10*D*Hq*N, with N the number of (query, key) pairs the causal
+document mask allows for the share's actual query rows.
+
+Further legs (skipped with --main-only, as in profiling runs), reported under
+breakdown:
+  t32768_gqa32x8            the Llama-3-8B-shaped workload (T = 32,768, 32 q /
+                            8 kv heads, cp_size 4), DualChunkSwap and contiguous
+                            ranks 0 and 3, with per-kernel times, the rank-major
+                            gathered K/V path and the restoration measured cold;
   graph_replayed_step       the main step replayed from a HIP graph;
   partition_million_tokens  the partition kernel alone at T = 1,048,576 in
                             10,000 documents, every rank and strategy;
   dynamic_t_sweep           every share of 16 micro-batches of varying active T
                             on buffers allocated once for 65,536 tokens;
-  long_context_shares       contiguous ranks 0 and 7 of the 70B-shaped
-                            T = 131,072 workload (64 q / 8 kv heads, cp_size 8);
   short_mha_forward         the forward-only T = 8,192 workload (16 q / 16 kv
                             heads, cp_size 2), both strategies, ranks 0 and 1.
 Prints one JSON line; progress goes to stderr.
@@ -45,20 +49,22 @@ import workloads as W  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-SHARES = [(0, 0), (0, 3), (1, 0), (1, 3)]   # (strategy, rank)
-STRAT_NAME = {0: "dcs", 1: "contiguous"}
+STRAT_NAME = {0: "dcs", 1: "contiguous", 2: "packed"}
+KERNELS = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"]
+
+KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
+# the physical-order kernels a step launches at head_dim 128 (rocprofv3 kernel names)
+KERNEL_SYMBOL = {"attn_fwd": "cpthd::attn_fwd_kernel<128, 1, false>",
+                 "attn_bwd_dq": "cpthd::attn_bwd_dq_kernel<128, 1, false>",
+                 "attn_bwd_dkdv": "cpthd::attn_bwd_dkdv_kernel<128, 2, false>"}
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_t32768_gqa32x8_hbm_traffic.json")
-KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
-# the physical-order kernels the main step launches at head_dim 128 (rocprofv3 kernel names)
-KERNEL_SYMBOL = {"attn_fwd": "cpthd::attn_fwd_kernel<128, 1, false>",
-                 "attn_bwd_dq": "cpthd::attn_bwd_dq_kernel<128, 1, false>",
-                 "attn_bwd_dkdv": "cpthd::attn_bwd_dkdv_kernel<128, 2, false>"}
+def traffic_file(workload):
+    return os.path.join(ROOT, "profiles", f"attn_{workload}_hbm_traffic.json")
 
 
 def kernel_source_hash(root=ROOT):
@@ -75,11 +81,12 @@ def kernel_source_hash(root=ROOT):
     return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE,
-    calibrated on a plain copy), or None when the kernel sources changed since the counters were taken."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` at `workload` from the committed rocprofv3 counter summary (FETCH_SIZE +
+    WRITE_SIZE, calibrated on a plain copy), or None when the kernel sources changed since the counters were
+    taken."""
     try:
-        rec = json.load(open(TRAFFIC_FILE))
+        rec = json.load(open(traffic_file(workload)))
     except (OSError, ValueError):
         return None
     if kernel_source_hash() != rec.get("source_sha256"):
@@ -135,6 +142,7 @@ def useful_pairs(idx, cu_p, cu_a):
     """Allowed (query, key) pairs for the rank's query rows: sum over actual rows of (position + 1)."""
     cu_p = cu_p.astype(np.int64)
     cu_a = cu_a.astype(np.int64)
+    idx = np.asarray(idx, dtype=np.int64)
     doc = np.searchsorted(cu_p, idx, side="right") - 1
     pos = idx - cu_p[doc]
     actual = cu_a[doc + 1] - cu_a[doc]
@@ -142,30 +150,345 @@ def useful_pairs(idx, cu_p, cu_a):
     return int(np.sum(pos[ok] + 1))
 
 
-def cpu_baseline(wl, budget_s=15.0):
-    """Time the CPU oracle (fwd + bwd) on a bounded sample: whole kv heads of the DualChunkSwap rank-0 share."""
-    import oracle
-    from threadpoolctl import threadpool_info
+def gpu_partition(cpthd, cu_p, T, cp, r, s, status):
+    """The rank's physical token indices from the partition kernel, as a host array (staging and flop counts)."""
+    return cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status).cpu().numpy().astype(np.int64)
 
-    idx = oracle.partition_indices(wl.cu_padded, wl.cp, 0, 0)
-    q, k, v, do = wl.q(idx), wl.k(), wl.v(), wl.do(idx)
-    pairs = useful_pairs(idx, wl.cu_padded, wl.cu_actual)
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle, timed on the host's cores
+# ----------------------------------------------------------------------------
+def _host_info():
+    from threadpoolctl import threadpool_info
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    return {"affinity_cores": len(os.sched_getaffinity(0)), "blas_threads": int(blas), "cpu_model": model}
+
+
+def _oracle_sample(wl, strategy, rank, budget_s):
+    """The oracle's forward and backward (forward only for a forward-only workload) on units of the rank's share,
+    in order, until the time budget is spent: a unit is one q head on the rank's rows of one document, handed to
+    the oracle as a layout of its own (the document's slot of K/V rows of the head's kv head, the rank's rows in
+    it), which is the same arithmetic as a call over the whole buffer restricted to that document and head.
+    Returns (useful flops, seconds, units done)."""
+    import oracle
+    idx = oracle.partition_indices(wl.cu_padded, wl.cp, rank, strategy)
+    cu_p, cu_a = wl.cu_padded.astype(np.int64), wl.cu_actual.astype(np.int64)
     G = wl.Hq // wl.Hkv
+    flops = secs = 0.0
+    done = 0
+    for d in range(wl.num_docs):
+        lo, hi = int(cu_p[d]), int(cu_p[d + 1])
+        sel = idx[(idx >= lo) & (idx < hi)]
+        pairs = useful_pairs(sel, wl.cu_padded, wl.cu_actual)
+        if pairs == 0:
+            continue
+        cu1 = np.array([0, hi - lo], dtype=np.int64)
+        ca1 = np.array([0, int(cu_a[d + 1] - cu_a[d])], dtype=np.int64)
+        q_all, do_all = wl.q(sel), (wl.do(sel) if wl.backward else None)
+        k_all, v_all = wl.k(np.arange(lo, hi)), wl.v(np.arange(lo, hi))
+        for h in range(wl.Hq):
+            q, k, v = q_all[:, h:h + 1], k_all[:, h // G:h // G + 1], v_all[:, h // G:h // G + 1]
+            t0 = time.perf_counter()
+            oracle.attn_fwd(q, k, v, sel - lo, cu1, ca1, wl.softmax_scale)
+            if wl.backward:
+                oracle.attn_bwd(q, k, v, do_all[:, h:h + 1], sel - lo, cu1, ca1, wl.softmax_scale)
+            secs += time.perf_counter() - t0
+            flops += (14.0 if wl.backward else 4.0) * wl.D * pairs
+            done += 1
+            if secs > budget_s:
+                return flops, secs, done
+    return flops, secs, done
+
+
+def cpu_baseline(budget_s=15.0, per_config_s=2.0):
+    """The CPU oracle (plain float64 numpy, never tuned) on bounded samples: the headline share (contiguous rank 0
+    of t131072_gqa64x8: q heads of its documents in order until the budget is spent), and a shorter sample of
+    every other workload's first configured share."""
+    info = _host_info()
+    wl = W.t131072_gqa64x8()
+    flops, secs, done = _oracle_sample(wl, 1, 0, budget_s)
+    per_config = {}
+    samples = [("tiny_t28", W.tiny_t28(bf16=True), 0, 0), ("t8192_mha16", W.t8192_mha16(), 0, 0),
+               ("t32768_gqa32x8", W.t32768_gqa32x8(), 0, 0), ("t131072_gqa64x8", wl, 1, 7),
+               ("dynamic_t.mb0", W.dynamic_t(0), 0, 0)]
+    for name, w, s, r in samples:
+        f, t, n = _oracle_sample(w, s, r, per_config_s)
+        per_config[name] = {"strategy": STRAT_NAME[s], "rank": r, "passes": "fwd+bwd" if w.backward else "fwd",
+                            "units": n, "seconds": t, "tflops": f / t / 1e12 if t > 0 else None}
+    return {"value": flops / secs / 1e12, "unit": "TFLOP/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"fwd+bwd of the contiguous rank-0 share of t131072_gqa64x8: {done} (document, q head) units "
+                      f"in order, float64 numpy, {secs:.1f} s, {flops:.3e} useful causal flops",
+            "affinity_cores": info["affinity_cores"], "blas_threads": info["blas_threads"],
+            "cpu_model": info["cpu_model"], "per_config": per_config}
+
+
+# ----------------------------------------------------------------------------
+# rank shares on the GPU
+# ----------------------------------------------------------------------------
+class ShareSet:
+    """Resident buffers and one step of the hot path for the given (strategy, rank) shares of a workload."""
+
+    def __init__(self, cpthd, torch, wl, shares, seeded=True, gen_seed=0):
+        self.cpthd, self.torch, self.wl, self.dev = cpthd, torch, wl, "cuda"
+        T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
+        S = T // cp
+        dev = self.dev
+        self.status = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.cu_a = torch.from_numpy(wl.cu_actual).to(dev)
+        self.cu_p = torch.from_numpy(wl.cu_padded).to(dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(gen_seed)
+
+        def bf16(x):
+            return torch.from_numpy(W.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+        def draw(fn, rows, heads, sd):
+            if seeded:
+                return bf16(fn(rows))
+            n = T if rows is None else len(rows)
+            return (torch.randn((n, heads, D), generator=g, device=dev) * sd).to(torch.bfloat16)
+
+        self.k_phys = draw(wl.k, None, Hkv, wl.qkv_scale)
+        self.v_phys = draw(wl.v, None, Hkv, wl.qkv_scale)
+        self.shares = []
+        for s, r in shares:
+            idx = gpu_partition(cpthd, self.cu_p, T, cp, r, s, self.status)
+            sh = dict(s=s, r=r, idx=torch.empty(S, dtype=torch.int32, device=dev),
+                      q=draw(wl.q, idx, Hq, wl.qkv_scale), do=draw(wl.do, idx, Hq, wl.do_scale))
+            if s != 1:   # simulated all-gather: rank-major concatenation of every rank's K/V rows
+                order = torch.from_numpy(np.concatenate([gpu_partition(cpthd, self.cu_p, T, cp, rr, s, self.status)
+                                                         for rr in range(cp)])).to(dev)
+                sh["kg"], sh["vg"] = self.k_phys[order].contiguous(), self.v_phys[order].contiguous()
+                sh["k"], sh["v"] = torch.empty_like(self.k_phys), torch.empty_like(self.v_phys)
+            else:        # rank-major contiguous ownership: the gathered buffer is already in physical order
+                sh["kg"], sh["vg"] = self.k_phys, self.v_phys
+                sh["k"], sh["v"] = self.k_phys, self.v_phys
+            sh["plan"] = cpthd.AttnPlan(T, cp, Hq, Hkv, D, max_docs=wl.num_docs)
+            sh["o"] = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
+            sh["lse"] = torch.empty((S, Hq), dtype=torch.float32, device=dev)
+            sh["dq"] = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
+            sh["dk"] = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+            sh["dv"] = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
+            sh["pairs"] = useful_pairs(idx, wl.cu_padded, wl.cu_actual)
+            self.shares.append(sh)
+        torch.cuda.synchronize()
+        self.pairs = np.array([sh["pairs"] for sh in self.shares], dtype=np.float64)
+        self.flops_fwd = 4.0 * D * Hq * self.pairs
+        self.flops_bwd = 10.0 * D * Hq * self.pairs
+
+    @property
+    def step_flops(self):
+        return float(np.sum(self.flops_fwd + self.flops_bwd))
+
+    def make_events(self):
+        t = self.torch
+        return [([[t.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)],
+                 [self.cpthd.HipEvents(4), self.cpthd.HipEvents(6)]) for _ in self.shares]
+
+    def step(self, evs=None, allgathered=False):
+        """partition -> restoration -> plan -> forward -> backward for every share; `evs` from make_events()
+        times every kernel; `allgathered` reads the rank-major gathered K/V without a restoration pass."""
+        c, wl, st = self.cpthd, self.wl, self.status
+        for i, sh in enumerate(self.shares):
+            e, he = evs[i] if evs else (None, None)
+            if e:
+                e[0][0].record()
+            c.partition_indices(self.cu_p, wl.T, wl.cp, sh["r"], sh["s"], out=sh["idx"], dev_status=st)
+            if e:
+                e[0][1].record()
+                e[1][0].record()
+            if not allgathered:
+                # contiguous: gathered == physical, nothing to restore (the call returns at once)
+                c.reorder_kv(sh["kg"], sh["vg"], self.cu_p, wl.T, wl.cp, sh["s"], k_out=sh["k"], v_out=sh["v"],
+                             dev_status=st)
+            if e:
+                e[1][1].record()
+                e[2][0].record()
+            sh["plan"].build(self.cu_a, self.cu_p, wl.T, sh["r"], sh["s"], st)
+            if e:
+                e[2][1].record()
+            k, v = (sh["kg"], sh["vg"]) if allgathered else (sh["k"], sh["v"])
+            c.attn_fwd(sh["q"], k, v, sh["plan"], wl.softmax_scale, sh["o"], sh["lse"], st,
+                       events=he[0] if he else None, kv_allgathered=allgathered)
+            c.attn_bwd(sh["q"], k, v, sh["o"], sh["do"], sh["lse"], sh["plan"], wl.softmax_scale, sh["dq"], sh["dk"],
+                       sh["dv"], st, events=he[1] if he else None, kv_allgathered=allgathered)
+
+    def per_kernel_ms(self, events):
+        """[share, kernel] mean ms over the event-timed steps; the plan's column adds the attention calls' plan
+        checks to the explicit build."""
+        acc = np.zeros((len(self.shares), len(KERNELS)))
+        for evs in events:
+            for i, (e, he) in enumerate(evs):
+                for j in range(3):
+                    acc[i, j] += e[j][0].elapsed_time(e[j][1])
+                acc[i, 2] += he[0].elapsed_ms(0, 1) + he[1].elapsed_ms(0, 1)
+                acc[i, 3] += he[0].elapsed_ms(2, 3)
+                acc[i, 4] += he[1].elapsed_ms(2, 3)
+                acc[i, 5] += he[1].elapsed_ms(4, 5)
+        return acc / max(len(events), 1)
+
+    def timed(self, steps, warmup, allgathered=False, clock=False):
+        """Wall time per step of `steps` plain steps (nothing recorded between launches), then the per-kernel
+        durations from as many event-timed steps."""
+        torch = self.torch
+        for _ in range(warmup):
+            self.step(allgathered=allgathered)
+        torch.cuda.synchronize()
+        self.cpthd.check_dev_status(self.status)
+        sampler = ClockSampler() if clock else None
+        if sampler:
+            sampler.__enter__()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            self.step(allgathered=allgathered)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3 / steps
+        if sampler:
+            sampler.__exit__(None, None, None)
+        self.cpthd.check_dev_status(self.status)
+        events = [self.make_events() for _ in range(steps)]
+        for k in range(steps):
+            self.step(events[k], allgathered=allgathered)
+        torch.cuda.synchronize()
+        self.cpthd.check_dev_status(self.status)
+        return wall_ms, self.per_kernel_ms(events), (sampler.summary() if sampler else None)
+
+    def report(self, wall_ms, pk):
+        per_share = []
+        for i, sh in enumerate(self.shares):
+            per_share.append({
+                "strategy": STRAT_NAME[sh["s"]], "rank": sh["r"], "causal_pairs_per_head": int(sh["pairs"]),
+                "fwd_tflops": float(self.flops_fwd[i] / (pk[i, 3] * 1e-3) / 1e12),
+                "bwd_tflops": float(self.flops_bwd[i] / ((pk[i, 4] + pk[i, 5]) * 1e-3) / 1e12),
+                "fwd_bwd_tflops": float((self.flops_fwd[i] + self.flops_bwd[i]) / (pk[i, 3:].sum() * 1e-3) / 1e12),
+                "ms": {n: float(pk[i, j]) for j, n in enumerate(KERNELS)}})
+        attn_ms = float(pk[:, 3:].sum())
+        return {"ms_per_step": wall_ms, "tflops": self.step_flops / (wall_ms * 1e-3) / 1e12,
+                "kernel_ms_per_step": {n: float(pk[:, j].sum()) for j, n in enumerate(KERNELS)},
+                "attn_fwd_bwd_tflops": self.step_flops / (attn_ms * 1e-3) / 1e12,
+                "attn_frac_of_bf16_peak": self.step_flops / (attn_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                "per_share": per_share}
+
+    def roofline(self, pk):
+        """The dominant attention kernel's algorithmic flops per launch over its mean launch duration: fwd
+        4*D*Hq*N; of the backward's 10*D*Hq*N the key-tile pass computes the score and dP recompute plus dK and
+        dV (8*D*Hq*N), the query-tile pass dQ (2*D*Hq*N; its recompute of S and dP is extra work)."""
+        algo = {"attn_fwd": self.flops_fwd, "attn_bwd_dkdv": 0.8 * self.flops_bwd, "attn_bwd_dq": 0.2 * self.flops_bwd}
+        kms = {n: float(pk[:, KERNELS.index(n)].sum()) for n in algo}
+        dom = max(algo, key=lambda n: kms[n])
+        achieved = float(np.sum(algo[dom]) / (kms[dom] * 1e-3) / 1e12)
+        return {"bound": "mfma", "kernel": dom, "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(self.wl.name, dom),
+                "traffic_unit": "bytes per launch (HBM, calibrated FETCH_SIZE + WRITE_SIZE)",
+                "avg_launch_us": float(pk[:, KERNELS.index(dom)].mean() * 1e3),
+                "algorithmic_flops_per_launch": float(np.mean(algo[dom])),
+                "per_kernel_frac": {n: float(np.sum(algo[n]) / (kms[n] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS)
+                                    for n in algo}}
+
+
+# ----------------------------------------------------------------------------
+# further legs
+# ----------------------------------------------------------------------------
+def graph_replay(torch, ss, steps, warmup):
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ss.step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ss.step()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    heads = 0
-    for g in range(wl.Hkv):
-        oracle.attn_fwd(q, k, v, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, kv_heads=[g])
-        oracle.attn_bwd(q, k, v, do, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, kv_heads=[g])
-        heads += 1
-        if time.perf_counter() - t0 > budget_s:
-            break
-    dt = time.perf_counter() - t0
-    flops = 14.0 * wl.D * G * heads * pairs
-    threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fwd+bwd of {heads} of {wl.Hkv} kv heads ({heads * G} of {wl.Hq} q heads) of the "
-                      f"DualChunkSwap rank-0 share, all {wl.num_docs} documents ({pairs} causal pairs per head), "
-                      f"float64 numpy, {dt:.1f} s"}
+    for _ in range(steps):
+        g.replay()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    ss.cpthd.check_dev_status(ss.status)
+    del g
+    return {"ms_per_step": ms, "tflops": ss.step_flops / (ms * 1e-3) / 1e12}
+
+
+def restoration_cold(torch, cpthd, ss, reps=7):
+    """The DualChunkSwap restoration and a plain device copy of the same bytes, each after a 512 MiB write that
+    evicts the 256 MiB last-level cache, and the copy also warm; median of reps - 1 event-timed launches."""
+    wl = ss.wl
+    sh0 = next(sh for sh in ss.shares if sh["s"] == 0)
+    copy_src = torch.cat([ss.k_phys.reshape(-1), ss.v_phys.reshape(-1)])
+    copy_dst = torch.empty_like(copy_src)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+
+    def median_ms(fn, cold):
+        ms = []
+        for rep in range(reps):
+            if cold:
+                flush.fill_(rep)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            if rep:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    moved = 2.0 * 2.0 * wl.T * wl.Hkv * wl.D * 2     # K and V, read + write
+    restore = lambda: cpthd.reorder_kv(sh0["kg"], sh0["vg"], ss.cu_p, wl.T, wl.cp, 0, k_out=sh0["k"],  # noqa: E731
+                                       v_out=sh0["v"], dev_status=ss.status)
+    out = {"bytes_moved": moved,
+           "restoration_gbs_cold_events": moved / (median_ms(restore, True) * 1e-3) / 1e9,
+           "device_copy_gbs_cold": moved / (median_ms(lambda: copy_dst.copy_(copy_src), True) * 1e-3) / 1e9,
+           "device_copy_gbs_warm": moved / (median_ms(lambda: copy_dst.copy_(copy_src), False) * 1e-3) / 1e9,
+           "note": "cold: a 512 MiB fill before every launch; event-timed, so each figure includes the launch gap"}
+    cpthd.check_dev_status(ss.status)
+    del flush, copy_dst, copy_src
+    return out
+
+
+def partition_million_tokens(torch, cpthd, status):
+    """The partition kernel alone at T = 1,048,576 in 10,000 documents, cp_size 4, every rank under both
+    strategies: 20 calls captured in a HIP graph per (strategy, rank) and replayed, so the host's launch rate does
+    not enter the time."""
+    dev = "cuda"
+    cu_big_np, _ = W.t1m_10k_docs()
+    T_big, cp_big = int(cu_big_np[-1]), 4
+    cu_big = torch.from_numpy(cu_big_np).to(dev)
+    idx_big = torch.empty(T_big // cp_big, dtype=torch.int32, device=dev)
+    us = []
+    for s_b in (0, 1):
+        for r_b in range(cp_big):
+            cpthd.partition_indices(cu_big, T_big, cp_big, r_b, s_b, out=idx_big, dev_status=status)
+            torch.cuda.synchronize()
+            g_b = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g_b):
+                for _ in range(20):
+                    cpthd.partition_indices(cu_big, T_big, cp_big, r_b, s_b, out=idx_big, dev_status=status)
+            g_b.replay()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(5):
+                g_b.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) * 1e3 / 100)
+            del g_b
+    cpthd.check_dev_status(status)
+    out_bytes = 4.0 * (T_big // cp_big)
+    return {"T": T_big, "num_docs": int(len(cu_big_np) - 1), "cp_size": cp_big,
+            "us_per_call_mean": float(np.mean(us)), "us_per_call_max": float(np.max(us)),
+            "out_bytes_per_call": out_bytes, "gbs": float(out_bytes / (np.mean(us) * 1e-6) / 1e9),
+            "note": "HIP-graph replay of 20 calls per (strategy, rank); 1 MiB of indices per call is latency-bound"}
 
 
 def dynamic_t_sweep(cpthd, torch, dev, status, reps=3):
@@ -206,14 +529,14 @@ def dynamic_t_sweep(cpthd, torch, dev, status, reps=3):
         cu_p = torch.from_numpy(wl.cu_padded).to(dev)
         for s in (0, 1):
             # staging (untimed): the ranks' local Q / dO rows and, under DualChunkSwap, the rank-major gathered K/V
-            parts = [cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status) for r in range(cp)]
+            parts = [gpu_partition(cpthd, cu_p, T, cp, r, s, status) for r in range(cp)]
             for r in range(cp):
-                q_loc[r][:S] = q_full[parts[r].long()]
-                do_loc[r][:S] = do_full[parts[r].long()]
-                flops[s] += 14.0 * D * Hq * useful_pairs(parts[r].cpu().numpy().astype(np.int64), wl.cu_padded,
-                                                          wl.cu_actual)
+                rows = torch.from_numpy(parts[r]).to(dev)
+                q_loc[r][:S] = q_full[rows]
+                do_loc[r][:S] = do_full[rows]
+                flops[s] += 14.0 * D * Hq * useful_pairs(parts[r], wl.cu_padded, wl.cu_actual)
             if s == 0:
-                order = torch.cat(parts).long()
+                order = torch.from_numpy(np.concatenate(parts)).to(dev)
                 kg[:T], vg[:T] = k_phys[:T][order], v_phys[:T][order]
                 k_in, v_in = k_buf, v_buf
             else:
@@ -249,60 +572,6 @@ def dynamic_t_sweep(cpthd, torch, dev, status, reps=3):
             "note": "every (micro-batch, strategy, rank) share's full step; useful fwd+bwd flops over GPU time"}
 
 
-def long_context_shares(cpthd, torch, dev, status, reps=3):
-    """The 70B-shaped long-context workload (T = 131,072 packed tokens, documents of 1 to 16,384 tokens, 64 q /
-    8 kv heads, head dim 128, cp_size 8, contiguous strategy): ranks 0 and 7, each share's full step (partition,
-    plan, forward, backward; contiguous ownership needs no restoration), timed between two events over reps
-    repetitions after one untimed pass.  Tensor values are drawn on the GPU (timing only)."""
-    wl = W.t131072_gqa64x8()
-    T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
-    S = T // cp
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(4)
-
-    def randn(shape, sd):
-        return (torch.randn(shape, generator=gen, device=dev) * sd).to(torch.bfloat16)
-
-    k, v = randn((T, Hkv, D), 0.5), randn((T, Hkv, D), 0.5)
-    cu_a = torch.from_numpy(wl.cu_actual).to(dev)
-    cu_p = torch.from_numpy(wl.cu_padded).to(dev)
-    plan = cpthd.AttnPlan(T, cp, Hq, Hkv, D, max_docs=wl.num_docs)
-    idx = torch.empty(S, dtype=torch.int32, device=dev)
-    o = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((S, Hq), dtype=torch.float32, device=dev)
-    dq = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
-    dk = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
-    dv = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
-    scale = 1.0 / math.sqrt(D)
-    out = []
-    for r in (0, cp - 1):
-        q, do = randn((S, Hq, D), 0.5), randn((S, Hq, D), 1.0)
-        pairs = useful_pairs(cpthd.partition_indices(cu_p, T, cp, r, 1, dev_status=status).cpu().numpy()
-                             .astype(np.int64), wl.cu_padded, wl.cu_actual)
-
-        def share():
-            cpthd.partition_indices(cu_p, T, cp, r, 1, out=idx, dev_status=status)
-            plan.build(cu_a, cu_p, T, r, 1, status)
-            cpthd.attn_fwd(q, k, v, plan, scale, o, lse, status)
-            cpthd.attn_bwd(q, k, v, o, do, lse, plan, scale, dq, dk, dv, status)
-
-        share()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            share()
-        e1.record()
-        torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / reps
-        out.append({"rank": r, "causal_pairs_per_head": int(pairs), "ms": ms,
-                    "tflops": 14.0 * D * Hq * pairs / (ms * 1e-3) / 1e12})
-        del q, do
-    cpthd.check_dev_status(status)
-    return {"T": T, "cp_size": cp, "num_q_heads": Hq, "num_kv_heads": Hkv, "num_docs": wl.num_docs,
-            "strategy": "contiguous", "shares": out}
-
-
 def short_mha_forward(cpthd, torch, dev, status, reps=10):
     """The forward-only workload of T = 8,192 packed tokens (documents of 256 to 2,048 tokens, 16 q / 16 kv
     heads, head dim 128, cp_size 2): ranks 0 and 1 under both strategies, each share's partition, restoration
@@ -328,13 +597,13 @@ def short_mha_forward(cpthd, torch, dev, status, reps=10):
     scale = 1.0 / math.sqrt(D)
     out, flops_all, ms_all = [], 0.0, 0.0
     for s in (0, 1):
-        parts = [cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status) for r in range(cp)]
-        order = torch.cat(parts).long()
+        parts = [gpu_partition(cpthd, cu_p, T, cp, r, s, status) for r in range(cp)]
+        order = torch.from_numpy(np.concatenate(parts)).to(dev)
         kg, vg = (k_phys[order].contiguous(), v_phys[order].contiguous()) if s == 0 else (k_phys, v_phys)
         k_in, v_in = (k_buf, v_buf) if s == 0 else (k_phys, v_phys)
         for r in range(cp):
             q = randn((S, Hq, D), 0.5)
-            pairs = useful_pairs(parts[r].cpu().numpy().astype(np.int64), wl.cu_padded, wl.cu_actual)
+            pairs = useful_pairs(parts[r], wl.cu_padded, wl.cu_actual)
 
             def share():
                 cpthd.partition_indices(cu_p, T, cp, r, s, out=idx, dev_status=status)
@@ -362,16 +631,30 @@ def short_mha_forward(cpthd, torch, dev, status, reps=10):
             "pass": "forward", "tflops": flops_all / (ms_all * 1e-3) / 1e12, "shares": out}
 
 
+WORKLOADS = {
+    "t131072_gqa64x8": (W.t131072_gqa64x8, [(1, 0), (1, 7)],
+                        "t131072_gqa64x8: T=131072 packed bf16 tokens, documents uniform on [1,16384] tokens (no "
+                        "pads), 64 q / 8 kv heads, head_dim 128, cp_size=8, contiguous strategy, ranks 0 and 7; "
+                        "partition + restoration (none needed) + plan + attention fwd + bwd per share"),
+    "t32768_gqa32x8": (W.t32768_gqa32x8, [(0, 0), (0, 3), (1, 0), (1, 3)],
+                       "t32768_gqa32x8: T=32768 packed bf16 tokens, 32 q / 8 kv heads, head_dim 128, log-normal doc "
+                       "lengths (median 1024, sigma 1) clipped to [64,8192] padded to x8, cp_size=4; shares dcs r0, "
+                       "dcs r3, contiguous r0, contiguous r3; partition + restoration + plan + attention fwd + bwd "
+                       "per share"),
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="t131072_gqa64x8",
+                    help="the workload of the main step (default: the largest that fits one GPU)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
-    ap.add_argument("--no-allgathered", action="store_true",
-                    help="skip the extra timing legs: the rank-major gathered K/V path and the HIP-graph replay of "
-                         "the step (profiling runs: only the main step's launches)")
+    ap.add_argument("--main-only", action="store_true",
+                    help="time the main step only (profiling runs: only the main step's launches)")
     ap.add_argument("--calibration-copy", action="store_true",
                     help="after the timed region, run one plain copy of the K/V buffers (known bytes) through the "
                          "restoration kernel in contiguous mode, as the reference for HBM byte counters")
@@ -386,324 +669,67 @@ def main():
     import context_causal_thd_amd as cpthd
 
     dev = "cuda"
-    wl = W.t32768_gqa32x8()
-    T, cp, Hq, Hkv, D = wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D
-    S = T // cp
-    log(f"workload: T={T} docs={wl.num_docs} Hq={Hq} Hkv={Hkv} D={D} cp={cp}")
+    make, shares, desc = WORKLOADS[args.workload]
+    wl = make()
+    log(f"workload: {wl.name} T={wl.T} docs={wl.num_docs} Hq={wl.Hq} Hkv={wl.Hkv} D={wl.D} cp={wl.cp}")
+    t0 = time.perf_counter()
+    ss = ShareSet(cpthd, torch, wl, shares, seeded=True)
+    log(f"seeded inputs staged in {time.perf_counter() - t0:.1f} s")
 
-    def bf16(x):
-        return torch.from_numpy(W.to_bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(dev)
+    wall_ms, pk, clock = ss.timed(args.steps, args.warmup, clock=True)
+    log(f"timed {args.steps} steps: {wall_ms:.3f} ms each")
+    main_report = ss.report(wall_ms, pk)
+    roofline = ss.roofline(pk)
 
-    q_full, k_phys, v_phys, do_full = bf16(wl.q()), bf16(wl.k()), bf16(wl.v()), bf16(wl.do())
-    cu_a = torch.from_numpy(wl.cu_actual).to(dev)
-    cu_p = torch.from_numpy(wl.cu_padded).to(dev)
-    status = torch.zeros(1, dtype=torch.int32, device=dev)
-
-    # per-share resident buffers (untimed set-up)
-    shares = []
-    for s, r in SHARES:
-        idx = cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=status)
-        idx_l = idx.long()
-        sh = dict(s=s, r=r, idx=torch.empty_like(idx), q=q_full[idx_l].contiguous(), do=do_full[idx_l].contiguous())
-        if s == 0:   # simulated all-gather: rank-major concatenation of every rank's K/V rows
-            parts = [cpthd.partition_indices(cu_p, T, cp, rr, s, dev_status=status).long() for rr in range(cp)]
-            order = torch.cat(parts)
-            sh["kg"], sh["vg"] = k_phys[order].contiguous(), v_phys[order].contiguous()
-            sh["k"], sh["v"] = torch.empty_like(k_phys), torch.empty_like(v_phys)
-        else:        # rank-major contiguous ownership: the gathered buffer is already physical order
-            sh["kg"], sh["vg"] = k_phys, v_phys
-            sh["k"], sh["v"] = k_phys, v_phys
-        sh["plan"] = cpthd.AttnPlan(T, cp, Hq, Hkv, D, max_docs=wl.num_docs)
-        sh["o"] = torch.empty((S, Hq, D), dtype=torch.bfloat16, device=dev)
-        sh["lse"] = torch.empty((S, Hq), dtype=torch.float32, device=dev)
-        sh["dq"] = torch.empty((S, Hq, D), dtype=torch.float32, device=dev)
-        sh["dk"] = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
-        sh["dv"] = torch.empty((T, Hkv, D), dtype=torch.float32, device=dev)
-        sh["pairs"] = useful_pairs(idx.cpu().numpy().astype(np.int64), wl.cu_padded, wl.cu_actual)
-        shares.append(sh)
-    del q_full, do_full
-    torch.cuda.synchronize()
-    cpthd.check_dev_status(status)
-
-    row_bytes = Hkv * D * 2
-    n_kernels = 6   # partition, reorder, plan, fwd, bwd-dq, bwd-dkdv
-
-    def make_events():
-        return ([[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)] for _ in shares],
-                [[cpthd.HipEvents(2), cpthd.HipEvents(4)] for _ in shares])
-
-    def step(evs):
-        for i, sh in enumerate(shares):
-            e, he = (evs[0][i], evs[1][i]) if evs else (None, None)
-            if e:
-                e[0][0].record()
-            cpthd.partition_indices(cu_p, T, cp, sh["r"], sh["s"], out=sh["idx"], dev_status=status)
-            if e:
-                e[0][1].record()
-                e[1][0].record()
-            if sh["s"] == 0:
-                cpthd.reorder_kv(sh["kg"], sh["vg"], cu_p, T, cp, 0, k_out=sh["k"], v_out=sh["v"],
-                                 dev_status=status)
-            if e:
-                e[1][1].record()
-                e[2][0].record()
-            sh["plan"].build(cu_a, cu_p, T, sh["r"], sh["s"], status)
-            if e:
-                e[2][1].record()
-            cpthd.attn_fwd(sh["q"], sh["k"], sh["v"], sh["plan"], wl.softmax_scale, sh["o"], sh["lse"], status,
-                           events=he[0] if he else None)
-            cpthd.attn_bwd(sh["q"], sh["k"], sh["v"], sh["o"], sh["do"], sh["lse"], sh["plan"], wl.softmax_scale,
-                           sh["dq"], sh["dk"], sh["dv"], status, events=he[1] if he else None)
-
-    for _ in range(args.warmup):
-        step(None)
-    torch.cuda.synchronize()
-    cpthd.check_dev_status(status)
-    log(f"warmup done ({args.warmup} steps)")
-
-    # the timed steps: plain launches, nothing recorded between them
-    torch.cuda.synchronize()
-    with ClockSampler() as clock:
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step(None)
-        torch.cuda.synchronize()
-        elapsed = time.perf_counter() - t0
-    cpthd.check_dev_status(status)
-    log(f"timed {args.steps} steps in {elapsed:.3f} s")
-
-    # per-kernel durations: as many steps again, with events recorded around every launch
-    events = [make_events() for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for k_step in range(args.steps):
-        step(events[k_step])
-    torch.cuda.synchronize()
-    cpthd.check_dev_status(status)
-    acc = np.zeros((len(shares), n_kernels))
-    for evs, hevs in events:
-        for i in range(len(shares)):
-            for j in range(3):
-                acc[i, j] += evs[i][j][0].elapsed_time(evs[i][j][1])
-            acc[i, 3] += hevs[i][0].elapsed_ms(0, 1)
-            acc[i, 4] += hevs[i][1].elapsed_ms(0, 1)
-            acc[i, 5] += hevs[i][1].elapsed_ms(2, 3)
-
-    # the same shares with attention reading the rank-major gathered K/V directly (no restoration pass)
-    def step_allgathered(he):
-        for i, sh in enumerate(shares):
-            cpthd.partition_indices(cu_p, T, cp, sh["r"], sh["s"], out=sh["idx"], dev_status=status)
-            sh["plan"].build(cu_a, cu_p, T, sh["r"], sh["s"], status)
-            cpthd.attn_fwd(sh["q"], sh["kg"], sh["vg"], sh["plan"], wl.softmax_scale, sh["o"], sh["lse"], status,
-                           events=he[i][0] if he else None, kv_allgathered=True)
-            cpthd.attn_bwd(sh["q"], sh["kg"], sh["vg"], sh["o"], sh["do"], sh["lse"], sh["plan"], wl.softmax_scale,
-                           sh["dq"], sh["dk"], sh["dv"], status, events=he[i][1] if he else None,
-                           kv_allgathered=True)
-
-    ag = None
-    if not args.no_allgathered:
-        for _ in range(args.warmup):
-            step_allgathered(None)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            step_allgathered(None)
-        torch.cuda.synchronize()
-        ag_elapsed = time.perf_counter() - t0
-        cpthd.check_dev_status(status)
-        ag_events = [[[cpthd.HipEvents(2), cpthd.HipEvents(4)] for _ in shares] for _ in range(args.steps)]
-        for k_step in range(args.steps):   # per-kernel durations: a second pass with events
-            step_allgathered(ag_events[k_step])
-        torch.cuda.synchronize()
-        cpthd.check_dev_status(status)
-        ag_acc = np.zeros((len(shares), 3))
-        for he in ag_events:
-            for i in range(len(shares)):
-                ag_acc[i, 0] += he[i][0].elapsed_ms(0, 1)
-                ag_acc[i, 1] += he[i][1].elapsed_ms(0, 1)
-                ag_acc[i, 2] += he[i][1].elapsed_ms(2, 3)
-        ag_acc /= args.steps
-        log(f"allgathered path: {args.steps} steps in {ag_elapsed:.3f} s")
-        ag = {"ms_per_step": ag_elapsed * 1e3 / args.steps}
-
-    # the same step captured once in a HIP graph and replayed: the launch overhead a training loop that
-    # captures its step would not pay (the kernels and their work are unchanged)
-    graph_ms = None
-    if not args.no_allgathered:
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step(None)
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(None)
-        for _ in range(args.warmup):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            g.replay()
-        torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-        cpthd.check_dev_status(status)
-        del g
-        log(f"graph replay: {args.steps} steps, {graph_ms:.3f} ms each")
-
-    # the partition kernel alone at the million-token layout (T = 1,048,576 in 10,000 documents, cp_size 4),
-    # every rank under both strategies: 20 calls captured in a HIP graph per (strategy, rank) and replayed, so
-    # the host's launch rate does not enter the time
-    part_big = None
-    if not args.no_allgathered:
-        cu_big_np, _ = W.t1m_10k_docs()
-        T_big, cp_big = int(cu_big_np[-1]), 4
-        cu_big = torch.from_numpy(cu_big_np).to(dev)
-        idx_big = torch.empty(T_big // cp_big, dtype=torch.int32, device=dev)
-        us = []
-        for s_b in (0, 1):
-            for r_b in range(cp_big):
-                cpthd.partition_indices(cu_big, T_big, cp_big, r_b, s_b, out=idx_big, dev_status=status)
-                torch.cuda.synchronize()
-                g_b = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(g_b):
-                    for _ in range(20):
-                        cpthd.partition_indices(cu_big, T_big, cp_big, r_b, s_b, out=idx_big, dev_status=status)
-                g_b.replay()
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record()
-                for _ in range(5):
-                    g_b.replay()
-                e1.record()
-                torch.cuda.synchronize()
-                us.append(e0.elapsed_time(e1) * 1e3 / 100)
-                del g_b
-        cpthd.check_dev_status(status)
-        out_bytes = 4.0 * (T_big // cp_big)
-        part_big = {"T": T_big, "num_docs": int(len(cu_big_np) - 1), "cp_size": cp_big,
-                    "us_per_call_mean": float(np.mean(us)), "us_per_call_max": float(np.max(us)),
-                    "out_bytes_per_call": out_bytes, "gbs": float(out_bytes / (np.mean(us) * 1e-6) / 1e9),
-                    "note": "HIP-graph replay of 20 calls per (strategy, rank); 1 MiB of indices per call is "
-                            "latency-bound"}
-        log(f"partition at T={T_big}: {np.mean(us):.2f} us per call")
-
-    dyn = None
-    if not args.no_allgathered:
-        dyn = dynamic_t_sweep(cpthd, torch, dev, status)
-        log(f"dynamic-T sweep: {dyn['tflops']:.1f} TFLOP/s over {dyn['shares']} shares")
-    shortf = None
-    if not args.no_allgathered:
-        shortf = short_mha_forward(cpthd, torch, dev, status)
-        log(f"short MHA forward: {shortf['tflops']:.1f} TFLOP/s over {len(shortf['shares'])} shares")
-    longc = None
-    if not args.no_allgathered:
-        longc = long_context_shares(cpthd, torch, dev, status)
-        log("long context: " + ", ".join(f"rank {x['rank']} {x['tflops']:.1f} TFLOP/s" for x in longc["shares"]))
-
-    # HBM ceiling for the restoration: a plain device-to-device copy of the same bytes (K and V), and the
-    # restoration alone, each cold (a 512 MiB write before every rep evicts the 256 MiB last-level cache) and
-    # the copy also warm (the source left in that cache, as inside the step)
-    copy_src = torch.cat([k_phys.reshape(-1), v_phys.reshape(-1)])
-    copy_dst = torch.empty_like(copy_src)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    sh0 = next(sh for sh in shares if sh["s"] == 0)
-
-    def median_ms(fn, cold):
-        ms = []
-        for rep in range(7):
-            if cold:
-                flush.fill_(rep)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            torch.cuda.synchronize()
-            if rep:
-                ms.append(e0.elapsed_time(e1))
-        return float(np.median(ms))
-
-    moved = 2.0 * 2.0 * T * Hkv * D * 2     # K and V, read + write
-    copy_cold = moved / (median_ms(lambda: copy_dst.copy_(copy_src), True) * 1e-3) / 1e9
-    copy_warm = moved / (median_ms(lambda: copy_dst.copy_(copy_src), False) * 1e-3) / 1e9
-    reorder_cold = moved / (median_ms(lambda: cpthd.reorder_kv(sh0["kg"], sh0["vg"], cu_p, T, cp, 0, k_out=sh0["k"],
-                                                              v_out=sh0["v"], dev_status=status), True) * 1e-3) / 1e9
-    cpthd.check_dev_status(status)
-    del flush, copy_dst, copy_src
+    breakdown = {"main_step": main_report, "shader_clock_during_timed_steps": clock}
+    if not args.main_only:
+        breakdown["graph_replayed_step"] = graph_replay(torch, ss, args.steps, args.warmup)
+        log(f"graph replay: {breakdown['graph_replayed_step']['ms_per_step']:.3f} ms per step")
 
     if args.calibration_copy:
-        k2, v2 = torch.empty_like(k_phys), torch.empty_like(v_phys)
-        cpthd.reorder_kv(k_phys, v_phys, cu_p, T, cp, 1, k_out=k2, v_out=v2, dev_status=status)
+        k2, v2 = torch.empty_like(ss.k_phys), torch.empty_like(ss.v_phys)
+        cpthd.reorder_kv(ss.k_phys, ss.v_phys, ss.cu_p, wl.T, wl.cp, 1, k_out=k2, v_out=v2, dev_status=ss.status)
         torch.cuda.synchronize()
-        log(f"calibration copy: {2 * k_phys.numel() * 2} bytes read and written")
+        log(f"calibration copy: {2 * ss.k_phys.numel() * 2} bytes read and written")
+        del k2, v2
 
-    # pure-GPU step time: the per-kernel event durations of one step
-    per_kernel_ms = acc / args.steps
-    gpu_step_ms = float(per_kernel_ms.sum())
-    wall_step_ms = elapsed * 1e3 / args.steps
-    pairs = np.array([sh["pairs"] for sh in shares], dtype=np.float64)
-    flops_fwd = 4.0 * D * Hq * pairs
-    flops_bwd = 10.0 * D * Hq * pairs
-    step_flops = float(np.sum(flops_fwd + flops_bwd))
-    value = step_flops / (wall_step_ms * 1e-3) / 1e12
-
-    names = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"]
-    kernel_ms = {n: float(per_kernel_ms[:, j].sum()) for j, n in enumerate(names)}
-    # algorithmic flops per kernel: fwd = 4DHqN; of the backward's 10DHqN, the key-tile pass computes the
-    # score and dP recompute plus dK and dV (8DHqN), the query-tile pass dQ (2DHqN; its recompute is extra)
-    algo = {"attn_fwd": flops_fwd, "attn_bwd_dkdv": 0.8 * flops_bwd, "attn_bwd_dq": 0.2 * flops_bwd}
-    dominant = max(algo, key=lambda n: kernel_ms[n])
-    j = names.index(dominant)
-    achieved = float(np.sum(algo[dominant]) / (kernel_ms[dominant] * 1e-3) / 1e12)
-    roofline = {"bound": "mfma", "kernel": dominant, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(dominant),
-                "traffic_unit": "bytes per launch (HBM, calibrated FETCH_SIZE + WRITE_SIZE)",
-                "avg_launch_us": float(per_kernel_ms[:, j].mean() * 1e3)}
-
-    dcs = [i for i, sh in enumerate(shares) if sh["s"] == 0]
-    part_bytes = 4.0 * S
-    reorder_bytes = 2.0 * 2.0 * T * row_bytes      # read + write of K and V
-    breakdown = {
-        "per_share": [
-            {"strategy": STRAT_NAME[sh["s"]], "rank": sh["r"], "causal_pairs_per_head": int(sh["pairs"]),
-             "fwd_tflops": float(flops_fwd[i] / (per_kernel_ms[i, 3] * 1e-3) / 1e12),
-             "bwd_tflops": float(flops_bwd[i] / ((per_kernel_ms[i, 4] + per_kernel_ms[i, 5]) * 1e-3) / 1e12),
-             "fwd_bwd_tflops": float((flops_fwd[i] + flops_bwd[i]) / (per_kernel_ms[i, 3:].sum() * 1e-3) / 1e12),
-             "ms": {n: float(per_kernel_ms[i, jj]) for jj, n in enumerate(names)}}
-            for i, sh in enumerate(shares)],
-        "kernel_ms_per_step": kernel_ms,
-        "attn_fwd_bwd_tflops": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12),
-        "attn_frac_of_bf16_peak": float(step_flops / (per_kernel_ms[:, 3:].sum() * 1e-3) / 1e12 / PEAK_BF16_TFLOPS),
-        "partition_gbs": float(part_bytes / (per_kernel_ms[:, 0].mean() * 1e-3) / 1e9),
-        "partition_million_tokens": part_big,
-        # the dynamic-T micro-batch sweep on capacity buffers (65,536 tokens): every share of 16 micro-batches
-        "dynamic_t_sweep": dyn,
-        # the 70B-shaped long-context workload (T = 131,072, 64 q / 8 kv heads, cp_size 8): contiguous ranks 0, 7
-        "long_context_shares": longc,
-        # the forward-only T = 8,192 workload (16 q / 16 kv heads, cp_size 2): both strategies, ranks 0 and 1
-        "short_mha_forward": shortf,
-        "reorder_gbs": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9),
-        "reorder_frac_of_hbm_peak": float(reorder_bytes / (per_kernel_ms[dcs, 1].mean() * 1e-3) / 1e9 / PEAK_HBM_GBS),
-        "reorder_gbs_cold": reorder_cold,
-        "device_copy_gbs_same_bytes": {"cold": copy_cold, "warm": copy_warm},
-        "gpu_kernel_ms_per_step": gpu_step_ms,
-        "shader_clock_during_timed_steps": clock.summary(),
-        # attention reading the all-gathered (rank-major) K/V through the inverse partition map: partition +
-        # plan + fwd + bwd per share, no restoration pass; dK/dV come out in the gathered order
-        "allgathered_path": None if ag is None else {
-            "ms_per_step": ag["ms_per_step"],
-            "tflops": step_flops / (ag["ms_per_step"] * 1e-3) / 1e12,
-            "kernel_ms_per_step": {n: float(ag_acc[:, jj].sum())
-                                   for jj, n in enumerate(["attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"])},
-        },
-        # the main step (restoration path) replayed from a HIP graph, same kernels and inputs
-        "graph_replayed_step": None if graph_ms is None else {
-            "ms_per_step": graph_ms, "tflops": step_flops / (graph_ms * 1e-3) / 1e12},
-    }
+    if not args.main_only:
+        # the Llama-3-8B-shaped workload's four shares, each kernel timed, plus the rank-major gathered K/V path
+        # and the restoration measured cold
+        other = "t32768_gqa32x8" if args.workload != "t32768_gqa32x8" else "t131072_gqa64x8"
+        om, osh, _ = WORKLOADS[other]
+        del ss
+        torch.cuda.empty_cache()
+        ss3 = ShareSet(cpthd, torch, om(), osh, seeded=True)
+        w3, pk3, _ = ss3.timed(args.steps, args.warmup)
+        rep3 = ss3.report(w3, pk3)
+        rep3["roofline"] = ss3.roofline(pk3)
+        if any(s == 0 for s, _ in osh):
+            wa, pka, _ = ss3.timed(args.steps, args.warmup, allgathered=True)
+            rep3["allgathered_path"] = ss3.report(wa, pka)
+            rep3["allgathered_path"].pop("per_share")
+            rep3["restoration"] = restoration_cold(torch, cpthd, ss3)
+            dcs = [i for i, sh in enumerate(ss3.shares) if sh["s"] == 0]
+            moved = 2.0 * 2.0 * ss3.wl.T * ss3.wl.Hkv * ss3.wl.D * 2
+            rep3["restoration"]["restoration_gbs_in_step"] = moved / (pk3[dcs, 1].mean() * 1e-3) / 1e9
+        breakdown[other] = rep3
+        log(f"{other}: {rep3['tflops']:.1f} TFLOP/s ({rep3['ms_per_step']:.3f} ms per step)")
+        del ss3
+        torch.cuda.empty_cache()
+        status = torch.zeros(1, dtype=torch.int32, device=dev)
+        breakdown["partition_million_tokens"] = partition_million_tokens(torch, cpthd, status)
+        log(f"partition at 1M tokens: {breakdown['partition_million_tokens']['us_per_call_mean']:.2f} us per call")
+        breakdown["dynamic_t_sweep"] = dynamic_t_sweep(cpthd, torch, dev, status)
+        log(f"dynamic-T sweep: {breakdown['dynamic_t_sweep']['tflops']:.1f} TFLOP/s")
+        breakdown["short_mha_forward"] = short_mha_forward(cpthd, torch, dev, status)
+        log(f"short MHA forward: {breakdown['short_mha_forward']['tflops']:.1f} TFLOP/s")
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle) ...")
-        cpu = cpu_baseline(wl, args.cpu_budget)
+        cpu = cpu_baseline(args.cpu_budget)
 
+    value = main_report["tflops"]
     out = {
         "metric": "useful causal attn TFLOP/s per CP-rank share (fwd+bwd) + % bf16 MFMA peak",
         "value": value,
@@ -711,18 +737,16 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": wall_step_ms,
+        "ms_per_step": wall_ms,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "t32768_gqa32x8: T=32768 packed bf16 tokens, 32 q / 8 kv heads, head_dim 128, log-normal "
-                               "doc lengths (median 1024, sigma 1) clipped to [64,8192] padded to x8, cp_size=4; "
-                               "shares dcs r0, dcs r3, contiguous r0, contiguous r3; partition + reorder + plan + "
-                               "attention fwd + bwd per share",
-                   "T": T, "cp_size": cp, "num_q_heads": Hq, "num_kv_heads": Hkv, "head_dim": D,
-                   "num_docs": wl.num_docs, "parallelism": "one CP rank share per call, 1 GPU"},
+        "data": "synthetic (seeded)",
+        "config": {"workload": desc, "T": wl.T, "cp_size": wl.cp, "num_q_heads": wl.Hq, "num_kv_heads": wl.Hkv,
+                   "head_dim": wl.D, "num_docs": wl.num_docs,
+                   "shares": [f"{STRAT_NAME[s]} r{r}" for s, r in shares],
+                   "parallelism": "one CP rank share per call, 1 GPU"},
         "frac_of_bf16_peak": value / PEAK_BF16_TFLOPS,
         "roofline": roofline,
         "cpu_baseline": cpu,

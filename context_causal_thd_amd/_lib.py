@@ -12,7 +12,7 @@ LIB_PATH = os.path.join(_HERE, "libcpthd.so")
 
 c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
-# name -> (restype, argtypes); mirrors include/cpthd.h
+# name -> (restype, argtypes); mirrors include/cpthd.h and include/cpthd_timing.h
 SIGNATURES = {
     "cpthd_partition_indices": (c_i32, [c_vp, c_i32, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp]),
     "cpthd_reorder_kv": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp]),
@@ -20,16 +20,19 @@ SIGNATURES = {
     "cpthd_attn_workspace_bytes": (c_sz, [c_i64, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "cpthd_attn_plan": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                 c_vp, c_sz, c_vp, c_vp]),
-    "cpthd_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
-                               c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp, c_vp, c_i32]),
-    "cpthd_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
-                               c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp,
-                               c_vp, c_i32]),
+    "cpthd_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,
+                               c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]),
+    "cpthd_attn_bwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32,
+                               c_i32, c_i32, c_i32, c_i32, c_f32, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz,
+                               c_vp, c_vp]),
     "cpthd_status_string": (ctypes.c_char_p, [ctypes.c_int]),
 }
 # K/V in rank-major all-gathered order: same arguments as the physical-order calls
 SIGNATURES["cpthd_attn_fwd_allgathered"] = SIGNATURES["cpthd_attn_fwd"]
 SIGNATURES["cpthd_attn_bwd_allgathered"] = SIGNATURES["cpthd_attn_bwd"]
+# instrumentation variants (include/cpthd_timing.h): + kv_allgathered, events, n_events
+SIGNATURES["cpthd_attn_fwd_timed"] = (c_i32, SIGNATURES["cpthd_attn_fwd"][1] + [c_i32, c_vp, c_i32])
+SIGNATURES["cpthd_attn_bwd_timed"] = (c_i32, SIGNATURES["cpthd_attn_bwd"][1] + [c_i32, c_vp, c_i32])
 
 _lib = None
 

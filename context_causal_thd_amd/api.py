@@ -103,62 +103,87 @@ def cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capac
                      workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream))
 
 
-def _attn_fwd_call(name, q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy,
-                   num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local,
-                   lse_local, workspace, dev_status, stream, events):
-    ev, nev = _ev(events)
-    return _lib.call(name, _p(q_local), _p(k), _p(v), total_tokens, capacity_tokens, num_docs, cp_size,
-                     rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                     window_right, _p(o_local), _p(lse_local), _p(workspace),
-                     workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream), ev, nev)
+_FWD_NAMES = {False: "cpthd_attn_fwd", True: "cpthd_attn_fwd_allgathered"}
+_BWD_NAMES = {False: "cpthd_attn_bwd", True: "cpthd_attn_bwd_allgathered"}
 
 
-def _attn_bwd_call(name, q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs,
-                   cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                   window_right, dq_local, dk, dv, workspace, dev_status, stream, events):
-    ev, nev = _ev(events)
-    return _lib.call(name, _p(q_local), _p(k), _p(v), _p(o_local), _p(do_local), _p(lse_local),
-                     total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads,
-                     head_dim, softmax_scale, causal, window_left, window_right, _p(dq_local), _p(dk), _p(dv),
-                     _p(workspace), workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream),
-                     ev, nev)
+def _fwd_args(q_local, k, v, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank,
+              strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local,
+              lse_local, workspace, dev_status, stream):
+    return (_p(q_local), _p(k), _p(v), _p(cu_seqlens), _p(cu_seqlens_padded), num_docs, total_tokens,
+            capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
+            window_left, window_right, _p(o_local), _p(lse_local), _p(workspace),
+            workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream))
 
 
-def cpthd_attn_fwd(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
-                   num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
-                   workspace, dev_status=None, stream=None, events=None):
-    return _attn_fwd_call("cpthd_attn_fwd", q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank,
-                          strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                          window_right, o_local, lse_local, workspace, dev_status, stream, events)
+def _bwd_args(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens,
+              capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
+              window_left, window_right, dq_local, dk, dv, workspace, dev_status, stream):
+    return (_p(q_local), _p(k), _p(v), _p(o_local), _p(do_local), _p(lse_local), _p(cu_seqlens),
+            _p(cu_seqlens_padded), num_docs, total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads,
+            num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, _p(dq_local), _p(dk), _p(dv),
+            _p(workspace), workspace.numel() * workspace.element_size(), _p(dev_status), _s(stream))
 
 
-def cpthd_attn_fwd_allgathered(q_local, k_gathered, v_gathered, total_tokens, capacity_tokens, num_docs, cp_size,
-                               rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
-                               window_left, window_right, o_local, lse_local, workspace, dev_status=None,
-                               stream=None, events=None):
-    return _attn_fwd_call("cpthd_attn_fwd_allgathered", q_local, k_gathered, v_gathered, total_tokens,
-                          capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
-                          softmax_scale, causal, window_left, window_right, o_local, lse_local, workspace,
-                          dev_status, stream, events)
-
-
-def cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
+def cpthd_attn_fwd(q_local, k, v, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size,
                    rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                   window_right, dq_local, dk, dv, workspace, dev_status=None, stream=None, events=None):
-    return _attn_bwd_call("cpthd_attn_bwd", q_local, k, v, o_local, do_local, lse_local, total_tokens,
-                          capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
-                          softmax_scale, causal, window_left, window_right, dq_local, dk, dv, workspace, dev_status,
-                          stream, events)
+                   window_right, o_local, lse_local, workspace, dev_status=None, stream=None):
+    return _lib.call("cpthd_attn_fwd", *_fwd_args(
+        q_local, k, v, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank,
+        strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local,
+        lse_local, workspace, dev_status, stream))
 
 
-def cpthd_attn_bwd_allgathered(q_local, k_gathered, v_gathered, o_local, do_local, lse_local, total_tokens,
-                               capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads, num_kv_heads,
-                               head_dim, softmax_scale, causal, window_left, window_right, dq_local, dk_gathered,
-                               dv_gathered, workspace, dev_status=None, stream=None, events=None):
-    return _attn_bwd_call("cpthd_attn_bwd_allgathered", q_local, k_gathered, v_gathered, o_local, do_local,
-                          lse_local, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
-                          num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, dq_local,
-                          dk_gathered, dv_gathered, workspace, dev_status, stream, events)
+def cpthd_attn_fwd_allgathered(q_local, k_gathered, v_gathered, cu_seqlens, cu_seqlens_padded, num_docs,
+                               total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads,
+                               head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
+                               workspace, dev_status=None, stream=None):
+    return _lib.call("cpthd_attn_fwd_allgathered", *_fwd_args(
+        q_local, k_gathered, v_gathered, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens,
+        cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+        window_right, o_local, lse_local, workspace, dev_status, stream))
+
+
+def cpthd_attn_fwd_timed(q_local, k, v, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens,
+                         cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
+                         window_left, window_right, o_local, lse_local, workspace, dev_status, stream, kv_allgathered,
+                         events):
+    ev, nev = _ev(events)
+    return _lib.call("cpthd_attn_fwd_timed", *_fwd_args(
+        q_local, k, v, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank,
+        strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local,
+        lse_local, workspace, dev_status, stream), int(bool(kv_allgathered)), ev, nev)
+
+
+def cpthd_attn_bwd(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens,
+                   capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale,
+                   causal, window_left, window_right, dq_local, dk, dv, workspace, dev_status=None, stream=None):
+    return _lib.call("cpthd_attn_bwd", *_bwd_args(
+        q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens,
+        capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
+        window_left, window_right, dq_local, dk, dv, workspace, dev_status, stream))
+
+
+def cpthd_attn_bwd_allgathered(q_local, k_gathered, v_gathered, o_local, do_local, lse_local, cu_seqlens,
+                               cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank, strategy,
+                               num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right,
+                               dq_local, dk_gathered, dv_gathered, workspace, dev_status=None, stream=None):
+    return _lib.call("cpthd_attn_bwd_allgathered", *_bwd_args(
+        q_local, k_gathered, v_gathered, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs,
+        total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale,
+        causal, window_left, window_right, dq_local, dk_gathered, dv_gathered, workspace, dev_status, stream))
+
+
+def cpthd_attn_bwd_timed(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs,
+                         total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
+                         softmax_scale, causal, window_left, window_right, dq_local, dk, dv, workspace, dev_status,
+                         stream, kv_allgathered, events):
+    ev, nev = _ev(events)
+    return _lib.call("cpthd_attn_bwd_timed", *_bwd_args(
+        q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens,
+        capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,
+        window_left, window_right, dq_local, dk, dv, workspace, dev_status, stream), int(bool(kv_allgathered)),
+        ev, nev)
 
 
 # ----------------------------------------------------------------------------
@@ -253,8 +278,30 @@ def reorder_kv(k_gathered, v_gathered, cu_seqlens_padded, total_tokens, cp_size,
     return k_out, v_out
 
 
+class Layout:
+    """The document layout of one micro-batch as one rank sees it: the device cu arrays, T, rank and strategy."""
+
+    def __init__(self, cu_seqlens, cu_seqlens_padded, total_tokens, rank, strategy):
+        _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 2, ())
+        _need(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens_padded.numel(), ())
+        if cu_seqlens.numel() != cu_seqlens_padded.numel():
+            raise ValueError("cu_seqlens and cu_seqlens_padded must have the same length")
+        self.cu_seqlens, self.cu_seqlens_padded = cu_seqlens, cu_seqlens_padded
+        self.num_docs = cu_seqlens_padded.numel() - 1
+        self.total_tokens, self.rank, self.strategy = int(total_tokens), int(rank), int(strategy)
+
+    def frozen(self):
+        """A copy whose cu arrays later writes to the caller's tensors cannot change."""
+        return Layout(self.cu_seqlens.clone(), self.cu_seqlens_padded.clone(), self.total_tokens, self.rank,
+                      self.strategy)
+
+
 class AttnPlan:
-    """Workspace holding one rank's attention plan; sized once for a capacity, rebuilt per micro-batch."""
+    """Workspace of one rank's attention calls, sized once for a token capacity and a document count, plus the
+    layout of the current micro-batch (set by ``build``) and a device status word.
+
+    The C entry points check the plan held in the workspace against the cu arrays of every call and rebuild it
+    when it was built from others, so a call always computes with its own layout."""
 
     def __init__(self, capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, device="cuda"):
         self.capacity = capacity_tokens
@@ -265,34 +312,44 @@ class AttnPlan:
         if nbytes == 0:
             raise ValueError("unsupported attention configuration")
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
-        self.built = None
-        self.generation = 0   # counts builds, so a user of the plan can tell that it was rebuilt
+        self.status = torch.zeros(1, dtype=torch.int32, device=device)
+        self.layout = None
 
     def build(self, cu_seqlens, cu_seqlens_padded, total_tokens, rank, strategy, dev_status=None):
-        _need(cu_seqlens_padded, "cu_seqlens_padded", torch.int32, 2, ())
-        _need(cu_seqlens, "cu_seqlens", torch.int32, cu_seqlens_padded.numel(), ())
-        num_docs = cu_seqlens_padded.numel() - 1
-        if num_docs > self.max_docs:
+        """Set the micro-batch's layout and build its plan now (a fresh status word unless ``dev_status``)."""
+        lay = Layout(cu_seqlens, cu_seqlens_padded, total_tokens, rank, strategy)
+        if lay.num_docs > self.max_docs:
             raise ValueError("more documents than the workspace was sized for")
-        cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, self.capacity, self.cp_size, rank,
-                        strategy, self.Hq, self.Hkv, self.D, self.workspace, dev_status)
-        self.built = dict(total_tokens=total_tokens, num_docs=num_docs, rank=rank, strategy=strategy)
-        self.generation += 1
+        if dev_status is None:
+            self.status.zero_()
+            dev_status = self.status
+        cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, lay.num_docs, lay.total_tokens, self.capacity, self.cp_size,
+                        lay.rank, lay.strategy, self.Hq, self.Hkv, self.D, self.workspace, dev_status)
+        self.layout = lay
         return self
 
-    def _args(self):
-        if self.built is None:
-            raise RuntimeError("plan not built")
-        b = self.built
-        return (b["total_tokens"], self.capacity, b["num_docs"], self.cp_size, b["rank"], b["strategy"],
-                self.Hq, self.Hkv, self.D)
+    def check(self):
+        """Raise if a call using this plan's status word reported a device-side error (synchronises)."""
+        check_dev_status(self.status)
+
+    def _args(self, lay=None):
+        lay = lay or self.layout
+        if lay is None:
+            raise RuntimeError("plan not built: no layout set")
+        if lay.num_docs > self.max_docs:
+            raise ValueError("more documents than the workspace was sized for")
+        return (lay.cu_seqlens, lay.cu_seqlens_padded, lay.num_docs, lay.total_tokens, self.capacity, self.cp_size,
+                lay.rank, lay.strategy, self.Hq, self.Hkv, self.D)
 
 
 def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, lse_local=None, dev_status=None,
-             events=None, kv_allgathered=False):
-    """O and LSE of the rank's query rows.  ``kv_allgathered``: k and v are in rank-major all-gathered order
-    (as an all-gather of the ranks' local K/V leaves them) instead of physical order."""
-    T = plan.built["total_tokens"]
+             events=None, kv_allgathered=False, layout=None):
+    """O and LSE of the rank's query rows for ``layout`` (default: the plan's current one).  ``kv_allgathered``:
+    k and v are in rank-major all-gathered order (as an all-gather of the ranks' local K/V leaves them) instead
+    of physical order.  ``events`` (HipEvents of 4) times the call's two kernels."""
+    lay = layout or plan.layout
+    args = plan._args(lay)
+    T = lay.total_tokens
     S = T // plan.cp_size
     bf = torch.bfloat16
     _need(q_local, "q_local", bf, S, (plan.Hq, plan.D))
@@ -306,17 +363,25 @@ def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, ls
         lse_local = torch.empty((S, plan.Hq), dtype=torch.float32, device=q_local.device)
     _need(o_local, "o_local", bf, S, (plan.Hq, plan.D))
     _need(lse_local, "lse_local", torch.float32, S, (plan.Hq,))
-    call = cpthd_attn_fwd_allgathered if kv_allgathered else cpthd_attn_fwd
-    call(q_local, k, v, *plan._args(), softmax_scale, 1, -1, 0, o_local, lse_local, plan.workspace, dev_status,
-         events=events)
+    if dev_status is None:
+        dev_status = plan.status
+    tail = (softmax_scale, 1, -1, 0, o_local, lse_local, plan.workspace, dev_status)
+    if events is not None:
+        cpthd_attn_fwd_timed(q_local, k, v, *args, *tail, None, kv_allgathered, events)
+    else:
+        (cpthd_attn_fwd_allgathered if kv_allgathered else cpthd_attn_fwd)(q_local, k, v, *args, *tail)
     return o_local, lse_local
 
 
 def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softmax_scale=None, dq_local=None,
-             dk=None, dv=None, dev_status=None, events=None, kv_allgathered=False):
-    """dQ of the rank's rows and its partial dK, dV (fp32).  With ``kv_allgathered`` k, v and the returned
-    dk, dv are in rank-major all-gathered order."""
-    T = plan.built["total_tokens"]
+             dk=None, dv=None, dev_status=None, events=None, kv_allgathered=False, layout=None):
+    """dQ of the rank's rows and its partial dK, dV (fp32) for ``layout`` (default: the plan's current one).
+    With ``kv_allgathered`` k, v and the returned dk, dv are in rank-major all-gathered order.  Gradients this
+    function allocates have the inputs' row counts; rows past the active S (dq) or T (dk, dv) are zero.
+    ``events`` (HipEvents of 6) times the call's three kernels."""
+    lay = layout or plan.layout
+    args = plan._args(lay)
+    T = lay.total_tokens
     S = T // plan.cp_size
     bf, f32 = torch.bfloat16, torch.float32
     for t, name in ((q_local, "q_local"), (o_local, "o_local"), (do_local, "do_local")):
@@ -326,48 +391,63 @@ def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softma
     _need(lse_local, "lse_local", f32, S, (plan.Hq,))
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
+
+    def grad_buf(x, rows):
+        g = torch.empty(x.shape, dtype=f32, device=x.device)
+        if x.shape[0] > rows:   # capacity-sized input: the inactive tail gets a zero gradient
+            g[rows:].zero_()
+        return g
+
     if dq_local is None:
-        dq_local = torch.empty(q_local.shape, dtype=torch.float32, device=q_local.device)
+        dq_local = grad_buf(q_local, S)
     if dk is None:
-        dk = torch.empty(k.shape, dtype=torch.float32, device=k.device)
+        dk = grad_buf(k, T)
     if dv is None:
-        dv = torch.empty(v.shape, dtype=torch.float32, device=v.device)
+        dv = grad_buf(v, T)
     _need(dq_local, "dq_local", f32, S, (plan.Hq, plan.D))
     _need(dk, "dk", f32, T, (plan.Hkv, plan.D))
     _need(dv, "dv", f32, T, (plan.Hkv, plan.D))
-    call = cpthd_attn_bwd_allgathered if kv_allgathered else cpthd_attn_bwd
-    call(q_local, k, v, o_local, do_local, lse_local, *plan._args(), softmax_scale, 1, -1, 0, dq_local, dk, dv,
-         plan.workspace, dev_status, events=events)
+    if dev_status is None:
+        dev_status = plan.status
+    tail = (softmax_scale, 1, -1, 0, dq_local, dk, dv, plan.workspace, dev_status)
+    if events is not None:
+        cpthd_attn_bwd_timed(q_local, k, v, o_local, do_local, lse_local, *args, *tail, None, kv_allgathered, events)
+    else:
+        (cpthd_attn_bwd_allgathered if kv_allgathered else cpthd_attn_bwd)(q_local, k, v, o_local, do_local,
+                                                                           lse_local, *args, *tail)
     return dq_local, dk, dv
 
 
 class CPAttention(torch.autograd.Function):
-    """Causal THD attention of one CP rank; backward reuses the plan (and strategy) captured in forward."""
+    """Causal THD attention of one CP rank; backward runs with the layout (cu arrays, rank, strategy) captured in
+    forward, whatever the plan was rebuilt for in between (PR #3221 "What changed": the strategy captured in
+    forward drives backward)."""
 
     @staticmethod
-    def forward(ctx, q_local, k, v, plan: AttnPlan, softmax_scale, kv_allgathered=False):
-        o, lse = attn_fwd(q_local, k, v, plan, softmax_scale, kv_allgathered=kv_allgathered)
-        ctx.plan = plan
-        ctx.generation = plan.generation
-        ctx.scale = softmax_scale
-        ctx.kv_allgathered = kv_allgathered
+    def forward(ctx, q_local, k, v, plan: AttnPlan, softmax_scale, kv_allgathered=False, check=True):
+        lay = plan.layout.frozen()
+        o, lse = attn_fwd(q_local, k, v, plan, softmax_scale, kv_allgathered=kv_allgathered, layout=lay)
+        if check:
+            plan.check()
+        ctx.plan, ctx.layout, ctx.scale, ctx.kv_allgathered, ctx.check = plan, lay, softmax_scale, kv_allgathered, check
         ctx.save_for_backward(q_local, k, v, o, lse)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q_local, k, v, o, lse = ctx.saved_tensors
-        if ctx.plan.generation != ctx.generation:
-            # even with the same sizes, other document boundaries would give other tiles: refuse any rebuild
-            raise RuntimeError("the plan was rebuilt between forward and backward")
         dq, dk, dv = attn_bwd(q_local, k, v, o, do.contiguous(), lse, ctx.plan, ctx.scale,
-                              kv_allgathered=ctx.kv_allgathered)
-        return dq.to(q_local.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None
+                              kv_allgathered=ctx.kv_allgathered, layout=ctx.layout)
+        if ctx.check:
+            ctx.plan.check()
+        return dq.to(q_local.dtype), dk.to(k.dtype), dv.to(v.dtype), None, None, None, None
 
 
-def attention(q_local, k, v, plan: AttnPlan, softmax_scale=None, kv_allgathered=False):
-    """Autograd attention of one CP rank; k and v in physical order, or in rank-major all-gathered order with
-    ``kv_allgathered`` (their gradients then come back in the same order)."""
+def attention(q_local, k, v, plan: AttnPlan, softmax_scale=None, kv_allgathered=False, check=True):
+    """Autograd attention of one CP rank for the plan's current layout; k and v in physical order, or in
+    rank-major all-gathered order with ``kv_allgathered`` (their gradients then come back in the same order).
+    ``check`` reads the plan's status word after forward and after backward (a synchronisation) and raises on a
+    device-side error; with ``check=False`` call ``plan.check()`` when convenient."""
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(plan.D)
-    return CPAttention.apply(q_local, k, v, plan, softmax_scale, kv_allgathered)
+    return CPAttention.apply(q_local, k, v, plan, softmax_scale, kv_allgathered, check)

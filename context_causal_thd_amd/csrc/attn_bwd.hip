@@ -1,8 +1,8 @@
 // Causal THD attention backward for one CP rank (gfx950).
 //
 // TransformerEngine PR #3221: forward captures the strategy so backward uses
-// the same token layout ("What changed"); backward restores it and "selects
-// the matching step layout and K/V ordering" (sequence diagram) to return
+// the same token layout ("What changed"); in the sequence diagram backward
+// restores that strategy and uses its step layout and K/V order to return
 // dQ/dK/dV.  With P = softmax of the scores, dP = dO V^T and
 // delta = rowsum(dO * O) = rowsum(P * dP):
 //   dS = P * (dP - delta),  dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO.
@@ -77,7 +77,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB / kDqSplit), kQMinBlocks * kDqSp
   // the tile is read beside the header (the workspace holds a tile slot for
   // every query tile the launch can have); it is used only once both check out
   const QTile t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[tile];
-  if (!tile_usable(plan_matches(hdr, prm), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
+  if (!tile_usable(plan_matches(hdr, prm, lay), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
   float* ndelta = reinterpret_cast<float*>(ws + lay.delta);   // -delta per row, for the key-tile pass
   float* lse2w = reinterpret_cast<float*>(ws + lay.lse2);
 
@@ -316,8 +316,14 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
   const KVTile kt = reinterpret_cast<const KVTile*>(ws + lay.kvtiles)[tile];
   const bool kt_ok = (kt.doc >= 0) & (kt.doc < prm.num_docs) & (kt.k0 >= 0) & (kt.nkeys >= 0) &
                      (kt.nkeys <= kKeysPerWG) & (kt.k0 <= prm.T - kt.nkeys);
-  if (!tile_usable(plan_matches(hdr, prm), tile < hdr->n_kvtiles, kt_ok, status)) return;
+  if (!tile_usable(plan_matches(hdr, prm, lay), tile < hdr->n_kvtiles, kt_ok, status)) return;
   const DocSeg ds = reinterpret_cast<const DocSeg*>(ws + lay.docs)[kt.doc];
+  // the document's segments and, for the all-gathered order, the tile's keys
+  // inside the document's chunks: every K/V/dK/dV row the map gives is then < T
+  const bool ds_ok = docseg_ok(ds, prm) &
+                     (!AG | (prm.strategy != kDCS) |
+                      ((kt.k0 >= ds.ds) & (kt.k0 - ds.ds <= 2 * prm.cp * ds.na - kt.nkeys)));
+  if (!tile_usable(true, true, ds_ok, status)) return;
   const float* ndelta = reinterpret_cast<const float*>(ws + lay.delta);
   const float* lse2w = reinterpret_cast<const float*>(ws + lay.lse2);
 
@@ -524,16 +530,13 @@ static int launch_bwd(const void* q, const void* k, const void* v, const void* o
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kDqRowBlocks;
   int e = launch(attn_bwd_dq_kernel<DP, QB, AG>, dim3(grid_q * kDqSplit), dim3(64 * (kQWaves / QB / kDqSplit)), 0,
-                 stream, ev, nev, 0,
-                 (const uint16_t*)q,
-                 (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o, (const uint16_t*)dout, lse, dq, ws,
-                 lay, prm, status);
+                 stream, ev, nev, 1, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,
+                 (const uint16_t*)dout, lse, dq, ws, lay, prm, status);
   if (e) return e;
   constexpr int SD = DP >= 64 ? kDkdvSplit : 1;
-  return launch(attn_bwd_dkdv_kernel<DP, SD, AG>, dim3(grid_kv), dim3(256 * SD), 0, stream, ev, nev, 1,
-                (const uint16_t*)q,
-                (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, dk, dv, (const char*)ws, lay,
-                prm, status);
+  return launch(attn_bwd_dkdv_kernel<DP, SD, AG>, dim3(grid_kv), dim3(256 * SD), 0, stream, ev, nev, 2,
+                (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, lse, dk, dv,
+                (const char*)ws, lay, prm, status);
 }
 
 template <bool AG>
@@ -550,13 +553,16 @@ static int dispatch_bwd(const void* q, const void* k, const void* v, const void*
 }
 
 static int attn_bwd_entry(const void* q_local, const void* k, const void* v, const void* o_local,
-                          const void* do_local, const float* lse_local, int64_t total_tokens, int64_t capacity_tokens,
-                          int32_t num_docs, int32_t cp_size, int32_t rank, int32_t strategy, int32_t num_q_heads,
-                          int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
-                          int32_t window_left, int32_t window_right, float* dq_local, float* dk, float* dv,
-                          void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
+                          const void* do_local, const float* lse_local, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                          int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy,
+                          int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                          int32_t causal, int32_t window_left, int32_t window_right, float* dq_local, float* dk,
+                          float* dv, void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
                           hipEvent_t* events, int32_t n_events, bool allgathered) {
-  if (!q_local || !k || !v || !o_local || !do_local || !lse_local || !dq_local || !dk || !dv) return CPTHD_ERR_NULL;
+  if (!q_local || !k || !v || !o_local || !do_local || !lse_local || !dq_local || !dk || !dv || !cu_seqlens ||
+      !cu_seqlens_padded)
+    return CPTHD_ERR_NULL;
   PlanLayout lay;
   AttnParams prm;
   if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
@@ -573,6 +579,8 @@ static int attn_bwd_entry(const void* q_local, const void* k, const void* v, con
   const int64_t gkv = ((total_tokens + kKeysPerWG - 1) / kKeysPerWG + num_docs) * (int64_t)num_kv_heads;
   if (gq * kDqSplit > INT32_MAX || gkv > INT32_MAX) return CPTHD_ERR_TOKENS;   // more work-groups than one launch takes
   char* ws = (char*)workspace;
+  if (int e = launch_plan(cu_seqlens, cu_seqlens_padded, prm, ws, lay, true, dev_status, stream, events, n_events, 0))
+    return e;
   return ag ? dispatch_bwd<true>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm,
                                  dev_status, gq, gkv, stream, events, n_events)
             : dispatch_bwd<false>(q_local, k, v, o_local, do_local, lse_local, dq_local, dk, dv, ws, lay, prm,
@@ -583,29 +591,26 @@ static int attn_bwd_entry(const void* q_local, const void* k, const void* v, con
 
 using namespace cpthd;
 
-extern "C" int cpthd_attn_bwd(const void* q_local, const void* k, const void* v, const void* o_local,
-                              const void* do_local, const float* lse_local, int64_t total_tokens,
-                              int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
-                              int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                              float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
-                              float* dq_local, float* dk, float* dv, void* workspace, size_t workspace_bytes,
-                              int32_t* dev_status, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
-  return attn_bwd_entry(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
-                        rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                        window_right, dq_local, dk, dv, workspace, workspace_bytes, dev_status, stream, events,
-                        n_events, false);
+#define CPTHD_BWD_ARGS                                                                                                \
+  const void *q_local, const void *k, const void *v, const void *o_local, const void *do_local,                     \
+      const float *lse_local, const int32_t *cu_seqlens, const int32_t *cu_seqlens_padded, int32_t num_docs,        \
+      int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy,              \
+      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,            \
+      int32_t window_left, int32_t window_right, float *dq_local, float *dk, float *dv, void *workspace,           \
+      size_t workspace_bytes, int32_t *dev_status, hipStream_t stream
+#define CPTHD_BWD_PASS                                                                                                \
+  q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens,               \
+      capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal,        \
+      window_left, window_right, dq_local, dk, dv, workspace, workspace_bytes, dev_status, stream
+
+extern "C" int cpthd_attn_bwd(CPTHD_BWD_ARGS) {
+  return attn_bwd_entry(CPTHD_BWD_PASS, nullptr, 0, false);
 }
 
-extern "C" int cpthd_attn_bwd_allgathered(const void* q_local, const void* k, const void* v, const void* o_local,
-                                          const void* do_local, const float* lse_local, int64_t total_tokens,
-                                          int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
-                                          int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
-                                          int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
-                                          int32_t window_right, float* dq_local, float* dk, float* dv,
-                                          void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                                          hipStream_t stream, hipEvent_t* events, int32_t n_events) {
-  return attn_bwd_entry(q_local, k, v, o_local, do_local, lse_local, total_tokens, capacity_tokens, num_docs, cp_size,
-                        rank, strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
-                        window_right, dq_local, dk, dv, workspace, workspace_bytes, dev_status, stream, events,
-                        n_events, true);
+extern "C" int cpthd_attn_bwd_allgathered(CPTHD_BWD_ARGS) {
+  return attn_bwd_entry(CPTHD_BWD_PASS, nullptr, 0, true);
+}
+
+extern "C" int cpthd_attn_bwd_timed(CPTHD_BWD_ARGS, int32_t kv_allgathered, hipEvent_t* events, int32_t n_events) {
+  return attn_bwd_entry(CPTHD_BWD_PASS, events, n_events, kv_allgathered != 0);
 }

@@ -18,14 +18,29 @@ struct AttnParams {
   float scale_log2;   // softmax scale * log2(e)
 };
 
-// A plan is usable iff it was built for exactly these arguments.
-// Every field is compared (bitwise &, no short circuit), so the header is read
-// in a few wide loads instead of a chain of dependent ones.
-__device__ inline bool plan_matches(const PlanHeader* hp, const AttnParams& p) {
+// A plan is usable iff it was built for exactly these arguments and this
+// workspace layout (the plan kernel that ran before the attention kernel in
+// the same call also checked the cu arrays it was built from).  Every field is
+// compared (bitwise &, no short circuit), so the header is read in a few wide
+// loads instead of a chain of dependent ones.
+__device__ inline bool plan_matches(const PlanHeader* hp, const AttnParams& p, const PlanLayout& lay) {
   const PlanHeader h = *hp;
   return (h.valid == 1) & (h.magic == kPlanMagic) & (h.version == kPlanVersion) & (h.T == p.T) & (h.S == p.S) &
          (h.cp == p.cp) & (h.rank == p.rank) & (h.strategy == p.strategy) & (h.Hq == p.Hq) & (h.Hkv == p.Hkv) &
-         (h.D == p.D) & (h.num_docs == p.num_docs);
+         (h.D == p.D) & (h.num_docs == p.num_docs) & (h.max_qtiles == (int)lay.max_qtiles) &
+         (h.max_kvtiles == (int)lay.max_kvtiles) & (h.max_docs == (int)lay.max_docs);
+}
+
+// A document's segments lie inside the rank's local rows and its slot inside
+// [0, T); under DualChunkSwap its two chunks are equal and adjacent in local
+// order, which keeps every row of the all-gathered map (AgMap) below T.
+__device__ inline bool docseg_ok(const DocSeg& d, const AttnParams& p) {
+  const bool base = (d.ds >= 0) & (d.ve >= d.ds) & (d.ve <= p.T) & (d.na >= 0) & (d.nb >= 0) &
+                    ((d.na == 0) | ((d.la >= 0) & (d.la <= p.S - d.na))) &
+                    ((d.nb == 0) | ((d.lb >= 0) & (d.lb <= p.S - d.nb)));
+  const bool dcs = (p.strategy != kDCS) | ((d.nb == d.na) & (d.lb == d.la + d.na) &
+                                            (d.ds <= p.T - 2 * p.cp * d.na));
+  return base & dcs;
 }
 
 // Check a query tile descriptor against the tensors' extents (bitwise, so
@@ -335,10 +350,15 @@ __device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buff
 #endif
 }
 
-// Host helpers shared by the forward and backward entry points.
+// Host helpers shared by the plan, forward and backward entry points.
 int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32_t strategy, int32_t num_docs,
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t wl, int32_t wr, const void* ws,
                     size_t ws_bytes, PlanLayout& lay, AttnParams& prm);
 int64_t qtile_grid(const AttnParams& prm);
+// Launch the plan kernel: build the plan (ensure = false), or make sure the
+// workspace holds the plan of these arguments and cu arrays, rebuilding it
+// only when it does not (ensure = true).  Event slot `slot` times it.
+int launch_plan(const int32_t* cu_a, const int32_t* cu_p, const AttnParams& prm, char* ws, const PlanLayout& lay,
+                bool ensure, int32_t* status, hipStream_t stream, hipEvent_t* ev, int nev, int slot);
 
 }  // namespace cpthd

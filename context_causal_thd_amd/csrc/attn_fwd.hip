@@ -1,10 +1,10 @@
 // Causal THD attention forward for one CP rank's query rows (gfx950).
 //
 // TransformerEngine PR #3221, "Scope and constraints": THD self-attention,
-// causal without a sliding window (window_size = (-1, 0)); documents stay
-// isolated through the sequence metadata ("Logical sequences remain isolated
-// by cu_seqlens", review thread).  A local row at physical token p of
-// document d attends to the actual keys of d at positions <= p's position.
+// causal without a sliding window (window_size = (-1, 0)); per the review
+// thread the packed documents are kept apart by the cu_seqlens metadata alone.
+// A local row at physical token p of document d attends to the actual keys of
+// d at positions <= p's position.
 //
 // One work-group = one query tile of the plan (<= 256/G tokens of one segment
 // times the G q heads of one kv head: 256 rows, 8 waves of one 32-row MFMA
@@ -60,7 +60,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   // the tile is read beside the header (the workspace holds a tile slot for
   // every work-group the launch can have); it is used only once both check out
   const QTile t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[tile];
-  if (!tile_usable(plan_matches(hdr, prm), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
+  if (!tile_usable(plan_matches(hdr, prm, lay), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
 
   const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
@@ -287,7 +287,7 @@ static int launch_fwd(const void* q, const void* k, const void* v, void* o, floa
                       const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kFwdRowBlocks;
-  return launch(attn_fwd_kernel<DP, QB, AG>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 0,
+  return launch(attn_fwd_kernel<DP, QB, AG>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 1,
                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
 }
 
@@ -339,13 +339,14 @@ int64_t qtile_grid(const AttnParams& prm) {
 
 using namespace cpthd;
 
-static int attn_fwd_entry(const void* q_local, const void* k, const void* v, int64_t total_tokens,
-                          int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank, int32_t strategy,
+static int attn_fwd_entry(const void* q_local, const void* k, const void* v, const int32_t* cu_seqlens,
+                          const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                          int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy,
                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
                           int32_t causal, int32_t window_left, int32_t window_right, void* o_local, float* lse_local,
                           void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
                           hipEvent_t* events, int32_t n_events, bool allgathered) {
-  if (!q_local || !k || !v || !o_local || !lse_local) return CPTHD_ERR_NULL;
+  if (!q_local || !k || !v || !o_local || !lse_local || !cu_seqlens || !cu_seqlens_padded) return CPTHD_ERR_NULL;
   PlanLayout lay;
   AttnParams prm;
   if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
@@ -361,32 +362,34 @@ static int attn_fwd_entry(const void* q_local, const void* k, const void* v, int
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
   const int64_t grid = qtile_grid(prm);
   if (grid > INT32_MAX) return CPTHD_ERR_TOKENS;   // more work-groups than one launch takes
-  const char* ws = (const char*)workspace;
+  char* ws = (char*)workspace;
+  if (int e = launch_plan(cu_seqlens, cu_seqlens_padded, prm, ws, lay, true, dev_status, stream, events, n_events, 0))
+    return e;
   return ag ? dispatch_fwd<true>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events,
                                  n_events)
             : dispatch_fwd<false>(q_local, k, v, o_local, lse_local, ws, lay, prm, dev_status, grid, stream, events,
                                   n_events);
 }
 
-extern "C" int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, int64_t total_tokens,
-                              int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
-                              int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
-                              float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
-                              void* o_local, float* lse_local, void* workspace, size_t workspace_bytes,
-                              int32_t* dev_status, hipStream_t stream, hipEvent_t* events, int32_t n_events) {
-  return attn_fwd_entry(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
-                        num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
-                        workspace, workspace_bytes, dev_status, stream, events, n_events, false);
+#define CPTHD_FWD_ARGS                                                                                              \
+  const void *q_local, const void *k, const void *v, const int32_t *cu_seqlens, const int32_t *cu_seqlens_padded, \
+      int32_t num_docs, int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,             \
+      int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,        \
+      int32_t causal, int32_t window_left, int32_t window_right, void *o_local, float *lse_local, void *workspace, \
+      size_t workspace_bytes, int32_t *dev_status, hipStream_t stream
+#define CPTHD_FWD_PASS                                                                                              \
+  q_local, k, v, cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank, strategy, \
+      num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,  \
+      workspace, workspace_bytes, dev_status, stream
+
+extern "C" int cpthd_attn_fwd(CPTHD_FWD_ARGS) {
+  return attn_fwd_entry(CPTHD_FWD_PASS, nullptr, 0, false);
 }
 
-extern "C" int cpthd_attn_fwd_allgathered(const void* q_local, const void* k, const void* v, int64_t total_tokens,
-                                          int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank,
-                                          int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
-                                          int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
-                                          int32_t window_right, void* o_local, float* lse_local, void* workspace,
-                                          size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
-                                          hipEvent_t* events, int32_t n_events) {
-  return attn_fwd_entry(q_local, k, v, total_tokens, capacity_tokens, num_docs, cp_size, rank, strategy, num_q_heads,
-                        num_kv_heads, head_dim, softmax_scale, causal, window_left, window_right, o_local, lse_local,
-                        workspace, workspace_bytes, dev_status, stream, events, n_events, true);
+extern "C" int cpthd_attn_fwd_allgathered(CPTHD_FWD_ARGS) {
+  return attn_fwd_entry(CPTHD_FWD_PASS, nullptr, 0, true);
+}
+
+extern "C" int cpthd_attn_fwd_timed(CPTHD_FWD_ARGS, int32_t kv_allgathered, hipEvent_t* events, int32_t n_events) {
+  return attn_fwd_entry(CPTHD_FWD_PASS, events, n_events, kv_allgathered != 0);
 }

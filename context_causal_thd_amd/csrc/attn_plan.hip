@@ -1,10 +1,11 @@
 // Strategy-specific attention metadata of one CP rank (gfx950).
 //
-// TransformerEngine PR #3221: the sequence diagram's "gather K/V and build
-// strategy-specific metadata" step; "Why": DualChunkSwap gives a rank two
-// attention steps per document (chunks r and 2*cp_size-1-r), NO_LOAD_BALANCE
-// one step over its contiguous chunk; commit messages: "simplify packed
-// metadata to one chunk and one attention step per rank".
+// TransformerEngine PR #3221: the sequence diagram has the CP layer gather
+// K/V and then build metadata specific to the strategy; "Why" gives
+// DualChunkSwap two attention steps per document (chunks r and 2*cp_size-1-r)
+// and NO_LOAD_BALANCE a single step over the rank's contiguous chunk; the
+// commit messages reduce the packed strategy's metadata to one chunk and one
+// step per rank.
 //
 // Here the two steps become *segments*: maximal runs of the rank's local rows
 // that are consecutive physical tokens of one document.  A query tile is up to
@@ -17,8 +18,13 @@
 //
 // One work-group of 1024 threads builds the whole plan: it validates the cu
 // arrays, scans per-document tile counts in chunks of 1024 documents, emits
-// the tiles in parallel, and counting-sorts them by cost.
-#include "cpthd_device.h"
+// the tiles in parallel, and counting-sorts them by cost.  The plan keeps a
+// copy of the cu arrays it was built from and the call's arguments in its
+// header.  Every attention call first runs this kernel in "ensure" mode: when
+// the workspace already holds a plan built from exactly the call's arguments
+// and cu arrays it returns at once, otherwise it rebuilds the plan, so an
+// attention kernel never reads tiles of another micro-batch.
+#include "attn_common.h"
 #include "cpthd_host.h"
 
 namespace cpthd {
@@ -125,11 +131,33 @@ __device__ void sort_by_cost_desc(const Tile* tmp, Tile* out, int n, int* s_hist
   __syncthreads();
 }
 
+// The header and stored cu arrays of a plan built from exactly these arguments?
+__device__ inline bool plan_current(const char* ws, const PlanLayout& lay, const int32_t* cu_a, const int32_t* cu_p,
+                                    int B, int T, int cp, int rank, int strategy, int Hq, int Hkv, int D,
+                                    int* s_flag) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const PlanHeader h = *reinterpret_cast<const PlanHeader*>(ws);
+    *s_flag = (h.valid == 1) & (h.magic == kPlanMagic) & (h.version == kPlanVersion) & (h.T == T) &
+              (h.S == T / cp) & (h.cp == cp) & (h.rank == rank) & (h.strategy == strategy) & (h.Hq == Hq) &
+              (h.Hkv == Hkv) & (h.D == D) & (h.num_docs == B) & (h.max_qtiles == (int)lay.max_qtiles) &
+              (h.max_kvtiles == (int)lay.max_kvtiles) & (h.max_docs == (int)lay.max_docs);
+  }
+  __syncthreads();
+  if (!*s_flag) return false;   // uniform: every thread read the same flag
+  const int32_t* cpy = reinterpret_cast<const int32_t*>(ws + lay.cu_copy);
+  int diff = 0;
+  for (int i = tid; i <= B; i += kPlanThreads) diff |= (cpy[i] != cu_p[i]) | (cpy[B + 1 + i] != cu_a[i]);
+  return !__syncthreads_or(diff);
+}
+
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu_a,
                                                             const int32_t* __restrict__ cu_p, int B, int T, int cp,
                                                             int rank, int strategy, int Hq, int Hkv, int D,
-                                                            char* __restrict__ ws, PlanLayout lay, int32_t* status) {
+                                                            char* __restrict__ ws, PlanLayout lay, int32_t* status,
+                                                            int ensure) {
   __shared__ int s_bits;
+  __shared__ int s_flag;
   __shared__ int s_wave[40];
   __shared__ int s_qoff[kPlanThreads], s_kvoff[kPlanThreads];
   __shared__ int s_hist_q[kCostBins], s_hist_kv[kCostBins];   // tiles per cost bin, counted at emission
@@ -145,6 +173,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
 
   const int tid = threadIdx.x;
   const int S = T / cp, G = Hq / Hkv, bm = tokens_per_qtile(G);
+  // ensure mode: nothing to do when the workspace holds this call's plan
+  if (ensure && plan_current(ws, lay, cu_a, cu_p, B, T, cp, rank, strategy, Hq, Hkv, D, &s_flag)) return;
   if (tid == 0) {
     s_bits = 0;
     hdr->valid = 0;
@@ -256,7 +286,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   sort_by_cost_desc(qtmp, qt, carry_q, s_hist_q, s_wave);
   sort_by_cost_desc(kvtmp, kvt, carry_kv, s_hist_kv, s_wave);
 
-  // 4. header last
+  // 4. the cu arrays the plan was built from, then the header
+  int32_t* cpy = reinterpret_cast<int32_t*>(ws + lay.cu_copy);
+  for (int i = tid; i <= B; i += kPlanThreads) {
+    cpy[i] = cu_p[i];
+    cpy[B + 1 + i] = cu_a[i];
+  }
+  __threadfence();
+  __syncthreads();
   if (tid == 0) {
     hdr->magic = kPlanMagic;
     hdr->version = kPlanVersion;
@@ -293,20 +330,27 @@ extern "C" size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp
   return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, max_docs).total;
 }
 
+namespace cpthd {
+
+int launch_plan(const int32_t* cu_a, const int32_t* cu_p, const AttnParams& prm, char* ws, const PlanLayout& lay,
+                bool ensure, int32_t* status, hipStream_t stream, hipEvent_t* ev, int nev, int slot) {
+  return launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, ev, nev, slot, cu_a, cu_p, prm.num_docs, prm.T,
+                prm.cp, prm.rank, prm.strategy, prm.Hq, prm.Hkv, prm.D, ws, lay, status, ensure ? 1 : 0);
+}
+
+}  // namespace cpthd
+
 extern "C" int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t num_docs,
                                int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,
                                int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
                                void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream) {
   if (!cu_seqlens || !cu_seqlens_padded) return CPTHD_ERR_NULL;
-  if (cp_size < 1 || rank < 0 || rank >= cp_size) return CPTHD_ERR_RANK;
-  if (int e = check_strategy(strategy)) return e;
-  if (int e = check_tokens(total_tokens, capacity_tokens, cp_size, num_docs)) return e;
-  if (int e = check_strategy_tokens(strategy, total_tokens, cp_size)) return e;
-  if (int e = check_heads(num_q_heads, num_kv_heads, head_dim)) return e;
-  const PlanLayout lay = plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, num_docs);
-  if (!workspace || workspace_bytes < lay.total || reinterpret_cast<uintptr_t>(workspace) % 256)
-    return CPTHD_ERR_WORKSPACE;
-  return launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, nullptr, 0, 0, cu_seqlens, cu_seqlens_padded,
-                num_docs, (int)total_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
-                (char*)workspace, lay, dev_status);
+  PlanLayout lay;
+  AttnParams prm;
+  // the mask arguments are those every attention call must pass
+  if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
+                              num_kv_heads, head_dim, 1, -1, 0, workspace, workspace_bytes, lay, prm))
+    return e;
+  return launch_plan(cu_seqlens, cu_seqlens_padded, prm, (char*)workspace, lay, false, dev_status, stream, nullptr,
+                     0, 0);
 }

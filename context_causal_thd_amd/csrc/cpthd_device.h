@@ -49,7 +49,7 @@ constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
 constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
 constexpr int kCostBins = 2048;   // counting-sort bins for longest-first ordering
 constexpr int kPlanMagic = 0x43505444;  // "CPTD"
-constexpr int kPlanVersion = 1;
+constexpr int kPlanVersion = 2;
 
 // Query tile: `ntok` consecutive local rows of one segment (a run of the rank's
 // rows inside one document), all q heads of one kv group.  Keys [ds, kv_end).
@@ -91,7 +91,7 @@ static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
 
 // Workspace layout (byte offsets), identical on host and device.
 struct PlanLayout {
-  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, delta, lse2, total;
+  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, cu_copy, delta, lse2, total;
   int64_t max_qtiles, max_kvtiles, max_docs;
 };
 
@@ -113,6 +113,7 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int 
   L.kvtiles = off;      off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
   L.kvtiles_tmp = off;  off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
   L.docs = off;         off = align_up(off + (size_t)max_docs * sizeof(DocSeg), 256);
+  L.cu_copy = off;      off = align_up(off + 2 * ((size_t)max_docs + 1) * sizeof(int32_t), 256);
   L.delta = off;        off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
   L.lse2 = off;         off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
   L.total = off;

@@ -8,6 +8,7 @@
 #include <utility>
 
 #include "../../include/cpthd.h"
+#include "../../include/cpthd_timing.h"
 
 namespace cpthd {
 

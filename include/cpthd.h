@@ -10,8 +10,8 @@
  *              strategy (DualChunkSwap or NO_LOAD_BALANCE);
  *   reorder    restoring the rank-major, all-gathered K/V buffer to physical
  *              token order ("K/V restoration"; contiguous ownership needs none);
- *   plan       the strategy-specific attention metadata of the rank ("gather
- *              K/V and build strategy-specific metadata");
+ *   plan       the strategy-specific attention metadata of the rank (the
+ *              sequence diagram builds it right after gathering K/V);
  *   fwd / bwd  causal attention with window (-1, 0), documents isolated by the
  *              sequence metadata, for the rank's query rows against the whole
  *              physical K/V buffer: O and LSE forward, dQ, dK, dV backward.
@@ -52,10 +52,11 @@
  *   device data (the contents of the cu arrays) are OR-ed as CPTHD_DEV_* bits
  *   into *dev_status (a device int32 the caller zeroes; NULL = unchecked).
  *   A call that raises a device bit leaves its outputs unspecified but never
- *   touches memory outside its arguments' ranges.
- * - Optional timing: `events` may point to n_events caller-created hipEvent_t
- *   handles, used in (start, stop) pairs around each kernel the call launches,
- *   in launch order (recorded by hipExtLaunchKernel).  NULL / 0 = none.
+ *   touches memory outside its arguments' ranges; an attention call whose cu
+ *   arrays are rejected writes none of its outputs.
+ * - A workspace serves one call at a time: calls that share a workspace must
+ *   be ordered on one stream (or synchronised), since each may rebuild the plan
+ *   in it.
  */
 #ifndef CPTHD_H
 #define CPTHD_H
@@ -168,19 +169,24 @@ size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp_size, int3
 
 /*
  * cpthd_attn_plan -- build the rank's attention metadata into `workspace`
- * (PR #3221 sequence diagram: "build strategy-specific metadata"; commit
- * messages: one chunk and one attention step per rank for NO_LOAD_BALANCE,
- * two steps for DualChunkSwap).  The plan lists the rank's query tiles (each
- * inside one document, with its causal key range) and the key tiles of every
- * document with the rank's query rows that see them, ordered longest first.
- * Build it once per micro-batch and pass the same workspace to fwd and bwd.
+ * (PR #3221 sequence diagram: the CP layer builds metadata specific to the
+ * strategy once K/V are gathered; commit messages: NO_LOAD_BALANCE has one
+ * chunk and one attention step per rank, DualChunkSwap two steps).  The plan
+ * lists the rank's query tiles (each inside one document, with its causal key
+ * range) and the key tiles of every document with the rank's query rows that
+ * see them, ordered longest first; it records the arguments and a copy of the
+ * cu arrays it was built from.  Every attention call checks the workspace's
+ * plan against its own arguments and cu arrays and rebuilds it when they
+ * differ, so calling this first is optional: it moves the build of a
+ * micro-batch's plan ahead of its first attention call.
  *
  *   cu_seqlens, cu_seqlens_padded  device int32 [num_docs + 1]
  *   workspace                      device, >= cpthd_attn_workspace_bytes(...)
  *                                  for capacity_tokens and num_docs, 256-byte aligned
  * Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, WORKSPACE, LAUNCH; device bits
  * CU_ORDER, CU_TOTAL, DCS_DIVISIBLE, ACTUAL, DOC_BYTES (the kernels address a
- * document's K/V rows through one 32-bit buffer range).
+ * document's K/V rows through one 32-bit buffer range).  A layout that raises
+ * a device bit leaves no plan in the workspace.
  */
 int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t num_docs,
                     int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,
@@ -190,29 +196,34 @@ int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded,
 /*
  * cpthd_attn_fwd -- causal attention forward for the rank's query rows
  * (PR #3221 "Scope and constraints": THD self-attention, causal without a
- * sliding window, window_size = (-1, 0), equal local Q/K/V lengths).
+ * sliding window, window_size = (-1, 0), equal local Q/K/V lengths; review
+ * thread: documents stay isolated through cu_seqlens).
  * For local row i at physical token p (document d, position pos) and q head
  * h (kv head h / (Hq/Hkv)): scores softmax_scale * q.k over the actual keys of
  * document d at positions <= pos;  lse = log(sum(exp(scores))) (natural log),
  * o = softmax(scores) @ v.  Pad rows: o = 0, lse = -inf.
  *
  *   q_local   device bf16 [S, Hq, D]          k, v  device bf16 [T, Hkv, D] (physical order)
+ *   cu_seqlens, cu_seqlens_padded             device int32 [num_docs + 1], the micro-batch's documents
  *   o_local   device bf16 [S, Hq, D] (out)    lse_local  device float [S, Hq] (out)
- *   num_docs  B, as given to cpthd_attn_plan (sizes the launch grid)
- *   workspace holding the plan from cpthd_attn_plan with the same arguments
- *             (T, capacity, B, cp_size, rank, strategy, heads, head_dim)
- * Launches one kernel.  Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, MASK,
- * WORKSPACE, LAUNCH; device bit PLAN.
+ *   workspace device, >= cpthd_attn_workspace_bytes(capacity_tokens, ..., num_docs), 256-byte aligned;
+ *             holds the plan (built or checked by this call, see cpthd_attn_plan)
+ * Launches two kernels: the plan check (a rebuild when the workspace holds
+ * another plan) and the attention kernel.
+ * Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, MASK, WORKSPACE, LAUNCH; device
+ * bits as cpthd_attn_plan (then nothing is written) and PLAN.
  */
-int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, int64_t total_tokens,
-                   int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank, int32_t strategy,
-                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
-                   int32_t causal, int32_t window_left, int32_t window_right, void* o_local,
-                   float* lse_local, void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                   hipStream_t stream, hipEvent_t* events, int32_t n_events);
+int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, const int32_t* cu_seqlens,
+                   const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                   int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                   int32_t window_left, int32_t window_right, void* o_local, float* lse_local, void* workspace,
+                   size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
 /*
- * cpthd_attn_bwd -- gradients of cpthd_attn_fwd for an upstream gradient dO.
+ * cpthd_attn_bwd -- gradients of cpthd_attn_fwd for an upstream gradient dO
+ * (PR #3221 "What changed": backward uses the strategy, and so the token
+ * layout, captured in forward; the caller passes the same layout arguments).
  * delta = rowsum(dO * O); dS = P * (dP - delta) with dP = dO @ v^T;
  * dq = scale * dS @ k for the rank's rows; dk = scale * dS^T @ q and
  * dv = P^T @ dO summed over the rank's query rows and the Hq/Hkv q heads of
@@ -222,52 +233,53 @@ int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, int64_t to
  *
  *   q_local, o_local, do_local  device bf16 [S, Hq, D]   lse_local device float [S, Hq]
  *   k, v                        device bf16 [T, Hkv, D]
+ *   cu_seqlens, cu_seqlens_padded, workspace  as cpthd_attn_fwd
  *   dq_local                    device float [S, Hq, D] (out)
  *   dk, dv                      device float [T, Hkv, D] (out)
- * Launches two kernels (query-tile pass: delta and dq; key-tile pass: dk, dv).
- * Errors as cpthd_attn_fwd.
+ * Launches three kernels (plan check; query-tile pass: delta and dq; key-tile
+ * pass: dk, dv).  Errors as cpthd_attn_fwd.
  */
 int cpthd_attn_bwd(const void* q_local, const void* k, const void* v, const void* o_local,
-                   const void* do_local, const float* lse_local, int64_t total_tokens,
-                   int64_t capacity_tokens, int32_t num_docs, int32_t cp_size, int32_t rank, int32_t strategy,
-                   int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
-                   int32_t causal, int32_t window_left, int32_t window_right, float* dq_local,
-                   float* dk, float* dv, void* workspace, size_t workspace_bytes, int32_t* dev_status,
-                   hipStream_t stream, hipEvent_t* events, int32_t n_events);
+                   const void* do_local, const float* lse_local, const int32_t* cu_seqlens,
+                   const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                   int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy, int32_t num_q_heads,
+                   int32_t num_kv_heads, int32_t head_dim, float softmax_scale, int32_t causal,
+                   int32_t window_left, int32_t window_right, float* dq_local, float* dk, float* dv,
+                   void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
 /*
  * cpthd_attn_fwd_allgathered / cpthd_attn_bwd_allgathered -- cpthd_attn_fwd and
  * cpthd_attn_bwd with k and v (and, backward, dk and dv) in the rank-major
  * all-gathered order instead of physical order: row s*S + j holds the token
  * at local row j of rank s, which is what an all-gather of the ranks' local
- * K/V produces (PR #3221 "Why": rank-major contiguous ownership needs no K/V
- * reorder; the other strategies pay a restoration).  The kernels read every
- * key through the inverse of the partition, so no restoration pass
- * (cpthd_reorder_kv) and no physical-order copy of K/V are needed.  dk/dv are
- * written in the same gathered order, which is the layout a reduce-scatter
- * over the ranks splits into per-rank slices.  Results are identical to
- * cpthd_reorder_kv + cpthd_attn_fwd / cpthd_attn_bwd with dk/dv permuted.
- * Under NO_LOAD_BALANCE the two orders coincide.
+ * K/V produces (PR #3221 "Why" and commit messages: contiguous, rank-major
+ * ownership needs no K/V reorder; the other strategies pay a restoration).
+ * The kernels read every key through the inverse of the partition, so no
+ * restoration pass (cpthd_reorder_kv) and no physical-order copy of K/V are
+ * needed.  dk/dv are written in the same gathered order, which is the layout
+ * a reduce-scatter over the ranks splits into per-rank slices.  Results are
+ * identical to cpthd_reorder_kv + cpthd_attn_fwd / cpthd_attn_bwd with dk/dv
+ * permuted.  Under NO_LOAD_BALANCE the two orders coincide.
  *
  * Arguments, plan and errors as cpthd_attn_fwd / cpthd_attn_bwd, plus:
  * under DUAL_CHUNK_SWAP and PACKED_SUPER_SEQUENCE, T * Hkv * D * 2 must be
  * below 2^31 bytes (CPTHD_ERR_TOKENS otherwise).
  */
 int cpthd_attn_fwd_allgathered(const void* q_local, const void* k_gathered, const void* v_gathered,
-                               int64_t total_tokens, int64_t capacity_tokens, int32_t num_docs, int32_t cp_size,
-                               int32_t rank, int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
-                               int32_t window_right, void* o_local, float* lse_local, void* workspace,
-                               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
-                               hipEvent_t* events, int32_t n_events);
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t num_docs,
+                               int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,
+                               int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+                               void* o_local, float* lse_local, void* workspace, size_t workspace_bytes,
+                               int32_t* dev_status, hipStream_t stream);
 int cpthd_attn_bwd_allgathered(const void* q_local, const void* k_gathered, const void* v_gathered,
                                const void* o_local, const void* do_local, const float* lse_local,
-                               int64_t total_tokens, int64_t capacity_tokens, int32_t num_docs, int32_t cp_size,
-                               int32_t rank, int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads,
-                               int32_t head_dim, float softmax_scale, int32_t causal, int32_t window_left,
-                               int32_t window_right, float* dq_local, float* dk_gathered, float* dv_gathered,
-                               void* workspace, size_t workspace_bytes, int32_t* dev_status, hipStream_t stream,
-                               hipEvent_t* events, int32_t n_events);
+                               const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded, int32_t num_docs,
+                               int64_t total_tokens, int64_t capacity_tokens, int32_t cp_size, int32_t rank,
+                               int32_t strategy, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+                               float* dq_local, float* dk_gathered, float* dv_gathered, void* workspace,
+                               size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* cpthd_status_string(int status);

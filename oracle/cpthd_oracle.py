@@ -187,12 +187,14 @@ def _doc_rows(idx, cu_padded, cu_actual, docs):
         yield d, rows, lpos[rows], cu_p[d], cu_a[d + 1] - cu_a[d]
 
 
-def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None, kv_heads=None):
+def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None, kv_heads=None, rows=None):
     """Forward for one rank: returns (O [S,Hq,D], LSE [S,Hq], computed [S]) in float64.
 
     ``docs`` restricts the work to those documents (rows of other documents are
     NaN and ``computed`` is False there); None means every document.
     ``kv_heads`` restricts it to the q heads of those kv heads (others NaN).
+    ``rows`` (local row indices) restricts it to those query rows (others NaN):
+    each row's result depends on that row's query and the keys alone.
     """
     q_local = np.asarray(q_local, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -207,13 +209,19 @@ def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None, kv_head
     computed = np.zeros(S, dtype=bool)
     doc_of = token_map(cu_padded, cu_actual)[0][np.asarray(idx, dtype=np.int64)]
     hsel = np.array([kv_heads is None or h // G in kv_heads for h in range(Hq)])
+    rsel = np.ones(S, dtype=bool)
+    if rows is not None:
+        rsel = np.zeros(S, dtype=bool)
+        rsel[np.asarray(rows, dtype=np.int64)] = True
     for d in docs:
-        sel = doc_of == d
+        sel = (doc_of == d) & rsel
         computed |= sel
         o[np.ix_(sel, hsel)] = 0.0      # pads: O = 0, LSE = -inf (overwritten for actual rows below)
         lse[np.ix_(sel, hsel)] = -np.inf
-    for d, rows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
-        if rows.size == 0:
+    for d, drows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
+        keep = rsel[drows]
+        drows, qpos = drows[keep], qpos[keep]
+        if drows.size == 0:
             continue
         kpos = np.arange(a)
         for h in range(Hq):
@@ -221,8 +229,8 @@ def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None, kv_head
                 continue
             kd = k[start:start + a, h // G]
             vd = v[start:start + a, h // G]
-            for b0 in range(0, rows.size, _ROW_BLOCK):
-                r = rows[b0:b0 + _ROW_BLOCK]
+            for b0 in range(0, drows.size, _ROW_BLOCK):
+                r = drows[b0:b0 + _ROW_BLOCK]
                 allowed = kpos[None, :] <= qpos[b0:b0 + _ROW_BLOCK, None]
                 s = scale * (q_local[r, h] @ kd.T)
                 s = np.where(allowed, s, -np.inf)
@@ -234,13 +242,17 @@ def attn_fwd(q_local, k, v, idx, cu_padded, cu_actual, scale, docs=None, kv_head
     return o, lse, computed
 
 
-def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=None, kv_heads=None):
+def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=None, kv_heads=None, rows=None,
+             keys=None):
     """Backward for one rank: returns (dQ [S,Hq,D], dK [T,Hkv,D], dV [T,Hkv,D]) in float64.
 
     dK/dV are the gradients contributed by this rank's query rows only (rows of
     keys no query of the rank sees are 0).  With ``docs`` given, dQ rows and
     dK/dV rows outside those documents are NaN; ``kv_heads`` restricts the
-    work to those kv heads and their q heads in the same way.
+    work to those kv heads and their q heads in the same way.  ``rows`` (local
+    row indices) restricts dQ to those rows and ``keys`` (physical token
+    indices) restricts dK/dV to those keys (others NaN); a key's gradient still
+    sums over every query row of the rank that sees it.
     """
     q_local = np.asarray(q_local, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -258,22 +270,33 @@ def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=Non
     doc_of = token_map(cu_padded, cu_actual)[0][np.asarray(idx, dtype=np.int64)]
     hsel = np.array([kv_heads is None or h // G in kv_heads for h in range(Hq)])
     gsel = np.array([kv_heads is None or g in kv_heads for g in range(Hkv)])
+    rsel = np.ones(S, dtype=bool)
+    if rows is not None:
+        rsel = np.zeros(S, dtype=bool)
+        rsel[np.asarray(rows, dtype=np.int64)] = True
+    ksel = np.ones(T, dtype=bool)
+    if keys is not None:
+        ksel = np.zeros(T, dtype=bool)
+        ksel[np.asarray(keys, dtype=np.int64)] = True
     for d in docs:
-        dq[np.ix_(doc_of == d, hsel)] = 0.0
-        dk[cu_p[d]:cu_p[d + 1], gsel] = 0.0
-        dv[cu_p[d]:cu_p[d + 1], gsel] = 0.0
-    for d, rows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
-        if rows.size == 0:
+        dq[np.ix_((doc_of == d) & rsel, hsel)] = 0.0
+        slot = np.zeros(T, dtype=bool)
+        slot[cu_p[d]:cu_p[d + 1]] = True
+        dk[np.ix_(slot & ksel, gsel)] = 0.0
+        dv[np.ix_(slot & ksel, gsel)] = 0.0
+    for d, drows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
+        if drows.size == 0:
             continue
         kpos = np.arange(a)
+        kk = np.nonzero(ksel[start:start + a])[0]      # the requested keys among the document's actual keys
         for h in range(Hq):
             g = h // G
             if kv_heads is not None and g not in kv_heads:
                 continue
             kd = k[start:start + a, g]
             vd = v[start:start + a, g]
-            for b0 in range(0, rows.size, _ROW_BLOCK):
-                r = rows[b0:b0 + _ROW_BLOCK]
+            for b0 in range(0, drows.size, _ROW_BLOCK):
+                r = drows[b0:b0 + _ROW_BLOCK]
                 allowed = kpos[None, :] <= qpos[b0:b0 + _ROW_BLOCK, None]
                 s = scale * (q_local[r, h] @ kd.T)
                 s = np.where(allowed, s, -np.inf)
@@ -282,10 +305,13 @@ def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=Non
                 p = e / e.sum(axis=1)[:, None]              # softmax over allowed keys
                 o = p @ vd
                 dout = do_local[r, h]
-                dp = dout @ vd.T                             # dL/dP
                 delta = np.sum(dout * o, axis=1)             # rowsum(dO * O) = rowsum(P * dP)
-                ds = p * (dp - delta[:, None])               # dL/dS through the softmax
-                dq[r, h] = scale * (ds @ kd)
-                dk[start:start + a, g] += scale * (ds.T @ q_local[r, h])
-                dv[start:start + a, g] += p.T @ dout
+                rq = rsel[r]
+                if rq.any():                                 # dL/dS of the requested rows over all keys
+                    ds_r = p[rq] * (dout[rq] @ vd.T - delta[rq, None])
+                    dq[r[rq], h] = scale * (ds_r @ kd)
+                if kk.size:                                  # dL/dS of every row at the requested keys
+                    ds_k = p[:, kk] * (dout @ vd[kk].T - delta[:, None])
+                    dk[start + kk, g] += scale * (ds_k.T @ q_local[r, h])
+                    dv[start + kk, g] += p[:, kk].T @ dout
     return dq, dk, dv

@@ -1,6 +1,8 @@
 """Helpers for the GPU parity tests: upload seeded inputs, compare with the oracle."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -12,9 +14,26 @@ ATOL = 2e-2     # max-abs bound on attention outputs
 REL_L2 = 5e-3   # relative L2 bound on attention outputs
 
 
+# When CPTHD_MARGINS names a file, every attention comparison appends one JSON line there: the case being
+# checked (set_case), the tensor, its max-abs and relative-L2 error against the oracle and the entries compared.
+_MARGINS = os.environ.get("CPTHD_MARGINS")
+_CASE = {"case": ""}
+
+
+def set_case(label):
+    _CASE["case"] = label
+
+
 def log(msg):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def _record(name, mx, rel, n):
+    if _MARGINS:
+        with open(_MARGINS, "a") as f:
+            f.write(json.dumps({"case": _CASE["case"], "tensor": name, "max_abs": mx, "rel_l2": rel, "n": int(n)})
+                    + "\n")
 
 
 def bf16_dev(x):
@@ -60,5 +79,6 @@ def assert_attn_close(name, got, ref, valid=None):
         nrm = float(np.linalg.norm(r))
         rel = float(np.linalg.norm(g - r) / nrm) if nrm > 0 else float(np.linalg.norm(g - r))
         log(f"    {name}: max_abs={mx:.3e} rel_l2={rel:.3e} n={g.size}")
+        _record(name, mx, rel, g.size)
         assert mx <= ATOL, f"{name}: max abs error {mx:.4e} > {ATOL}"
         assert rel <= REL_L2, f"{name}: relative L2 error {rel:.4e} > {REL_L2}"

@@ -10,12 +10,16 @@ from context_causal_thd_amd import _lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "cpthd.h")
+HEADERS = [os.path.join(ROOT, "include", f) for f in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if f.endswith(".h")]
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cpthd_\w+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(cpthd_\w+)\s*\(", text))
+    return sorted(names)
 
 
 def _defines():
@@ -120,22 +124,28 @@ def test_attention_host_errors(lib):
 
     def call_fwd(**kw):
         a = dict(ok, **kw)
-        return fwd(P, P, P, a["T"], a["cap"], a["B"], a["cp"], a["r"], a["s"], a["hq"], a["hkv"], a["D"], 0.25,
-                   kw.get("causal", 1), kw.get("wl", -1), kw.get("wr", 0), P, P, P, ws_bytes, None, None, None, 0)
+        return fwd(P, P, P, kw.get("cua", P), P, a["B"], a["T"], a["cap"], a["cp"], a["r"], a["s"], a["hq"], a["hkv"],
+                   a["D"], 0.25, kw.get("causal", 1), kw.get("wl", -1), kw.get("wr", 0), P, P, P, ws_bytes, None, None)
 
     assert call_fwd(causal=0) == d["CPTHD_ERR_MASK"]
     assert call_fwd(wl=128) == d["CPTHD_ERR_MASK"]
     assert call_fwd(wr=1) == d["CPTHD_ERR_MASK"]
     assert call_fwd(cp=0) == d["CPTHD_ERR_RANK"]
     assert call_fwd(B=0) == d["CPTHD_ERR_TOKENS"]
-    assert fwd(P, None, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, ws_bytes, None, None, None, 0) \
+    assert call_fwd(cua=None) == d["CPTHD_ERR_NULL"]          # the cu arrays are required
+    assert fwd(P, None, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, ws_bytes, None, None) \
         == d["CPTHD_ERR_NULL"]
-    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, None, P, ws_bytes, None, None,
-               None, 0) == d["CPTHD_ERR_NULL"]
-    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 1, P, P, P, P, ws_bytes, None, None,
-               None, 0) == d["CPTHD_ERR_MASK"]
-    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, P, 16, None, None,
-               None, 0) == d["CPTHD_ERR_WORKSPACE"]
+
+    def call_bwd(**kw):
+        a = dict(ok, **kw)
+        return bwd(P, P, P, P, P, P, P, kw.get("cup", P), a["B"], a["T"], a["cap"], a["cp"], a["r"], a["s"], a["hq"],
+                   a["hkv"], a["D"], 0.25, 1, -1, kw.get("wr", 0), P, P, kw.get("dv", P), P, kw.get("wsb", ws_bytes),
+                   None, None)
+
+    assert call_bwd(dv=None) == d["CPTHD_ERR_NULL"]
+    assert call_bwd(cup=None) == d["CPTHD_ERR_NULL"]
+    assert call_bwd(wr=1) == d["CPTHD_ERR_MASK"]
+    assert call_bwd(wsb=16) == d["CPTHD_ERR_WORKSPACE"]
 
 
 def test_product_path_has_no_oracle_or_cpu_fallback():
@@ -167,21 +177,36 @@ def test_allgathered_attention_host_errors(lib):
     P = 0x100000
     fwd, bwd = lib.cpthd_attn_fwd_allgathered, lib.cpthd_attn_bwd_allgathered
     ws_small = lib.cpthd_attn_workspace_bytes(64, 2, 4, 2, 16, 4)
-    assert fwd(P, None, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, ws_small, None, None, None, 0) \
+    assert fwd(P, None, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, ws_small, None, None) \
         == d["CPTHD_ERR_NULL"]
-    assert fwd(P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 0, -1, 0, P, P, P, ws_small, None, None, None, 0) \
+    assert fwd(P, P, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 0, -1, 0, P, P, P, ws_small, None, None) \
         == d["CPTHD_ERR_MASK"]
-    assert bwd(P, P, P, P, P, P, 64, 64, 4, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, P, 16, None, None,
-               None, 0) == d["CPTHD_ERR_WORKSPACE"]
+    assert bwd(P, P, P, P, P, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, P, 16, None, None) \
+        == d["CPTHD_ERR_WORKSPACE"]
     # T * Hkv * D * 2 = 2^31 bytes: the gathered K/V would not fit one 32-bit buffer range
     T, cp, hq, hkv, D = 1 << 20, 4, 32, 8, 128
     wsb = lib.cpthd_attn_workspace_bytes(T, cp, hq, hkv, D, 16)
     assert wsb > 0
     for s in (0, 2):
-        assert fwd(P, P, P, T, T, 16, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, wsb, None, None, None, 0) \
+        assert fwd(P, P, P, P, P, 16, T, T, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, wsb, None, None) \
             == d["CPTHD_ERR_TOKENS"]
-        assert bwd(P, P, P, P, P, P, T, T, 16, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, P, wsb, None, None,
-                   None, 0) == d["CPTHD_ERR_TOKENS"]
+        assert bwd(P, P, P, P, P, P, P, P, 16, T, T, cp, 0, s, hq, hkv, D, 0.1, 1, -1, 0, P, P, P, P, wsb, None,
+                   None) == d["CPTHD_ERR_TOKENS"]
+
+
+def test_timed_variants_validate_like_the_product_calls(lib):
+    """The instrumentation entry points run the same host checks (and take no events when none are given)."""
+    d = _defines()
+    P = 0x100000
+    wsb = lib.cpthd_attn_workspace_bytes(64, 2, 4, 2, 16, 4)
+    fwd, bwd = lib.cpthd_attn_fwd_timed, lib.cpthd_attn_bwd_timed
+    for ag in (0, 1):
+        assert fwd(P, P, P, None, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, wsb, None, None, ag, None,
+                   0) == d["CPTHD_ERR_NULL"]
+        assert fwd(P, P, P, P, P, 4, 64, 64, 2, 5, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, wsb, None, None, ag, None,
+                   0) == d["CPTHD_ERR_RANK"]
+        assert bwd(P, P, P, P, P, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, P, 8, None, None,
+                   ag, None, 0) == d["CPTHD_ERR_WORKSPACE"]
 
 
 def test_bench_refuses_more_than_one_gpu():

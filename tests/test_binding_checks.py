@@ -9,8 +9,16 @@ from context_causal_thd_amd import api
 
 
 def _plan(T=64, cp=2, Hq=4, Hkv=2, D=16):
-    return types.SimpleNamespace(built=dict(total_tokens=T, num_docs=1, rank=0, strategy=0), cp_size=cp, Hq=Hq,
-                                 Hkv=Hkv, D=D, workspace=None)
+    lay = api.Layout(_t((2,), torch.int32), _t((2,), torch.int32), T, 0, 0)
+    return types.SimpleNamespace(layout=lay, cp_size=cp, Hq=Hq, Hkv=Hkv, D=D, workspace=None, status=None,
+                                 _args=lambda lay=None: ())
+
+
+def test_layout_refuses_bad_cu_arrays():
+    with pytest.raises(ValueError, match="cu_seqlens_padded: expected torch.int32"):
+        api.Layout(_t((3,), torch.int32), _t((3,), torch.int64), 64, 0, 0)
+    with pytest.raises(ValueError, match="same length"):
+        api.Layout(_t((4,), torch.int32), _t((3,), torch.int32), 64, 0, 0)
 
 
 def _t(shape, dtype=torch.bfloat16):

@@ -12,27 +12,31 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import assert_attn_close, bf16_dev, i32_dev, log, status_dev, to_np64
+from tests.gpu_util import assert_attn_close, bf16_dev, i32_dev, log, set_case, status_dev, to_np64
 
 pytestmark = pytest.mark.gpu
 
 cpthd = pytest.importorskip("context_causal_thd_amd")
+
+STRAT = {0: "dcs", 1: "contiguous", 2: "packed"}
 
 
 class Share:
     """One rank's share on the GPU: plan, forward and (optionally) backward."""
 
     def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False, allgathered=False,
-                 kv=None):
+                 kv=None, qdo=None):
         self.wl, self.s, self.r = wl, strategy, rank
         T, cp = wl.T, wl.cp
         S = T // cp
         cap = capacity or T
         capS = cap // cp
         self.idx = oracle.partition_indices(wl.cu_padded, cp, rank, strategy)
-        q = wl.q(self.idx)
-        k, v = kv if kv is not None else (wl.k(), wl.v())   # kv: the workload's K, V, generated once by the caller
+        # kv / qdo: the workload's physical-order K, V / Q, dO, generated once by the caller
+        q = qdo[0][self.idx] if qdo is not None else wl.q(self.idx)
+        k, v = kv if kv is not None else (wl.k(), wl.v())
         self.q_np, self.k_np, self.v_np = q, k, v
+        set_case(f"{wl.name} {STRAT[strategy]} r{rank}" + (" allgathered" if allgathered else ""))
         # rank-major all-gathered K/V (the simulated all-gather of every rank's local rows)
         self.allgathered = allgathered
         self.parts = [oracle.partition_indices(wl.cu_padded, cp, rr, strategy) for rr in range(cp)]
@@ -60,7 +64,7 @@ class Share:
                        kv_allgathered=allgathered)
         self.S, self.capS, self.cap = S, capS, cap
         if backward:
-            do = wl.do(self.idx)
+            do = qdo[1][self.idx] if qdo is not None else wl.do(self.idx)
             self.do_np = do
             self.do = buf((wl.Hq, wl.D), do, rows=capS)
             self.dq = torch.full((capS, wl.Hq, wl.D), canary, dtype=torch.float32, device="cuda")
@@ -78,36 +82,60 @@ class Share:
         if hasattr(self, "dq"):
             assert (self.dq[S:] == 7.0).all() and (self.dk[T:] == 7.0).all() and (self.dv[T:] == 7.0).all()
 
-    def compare(self, docs=None, kv_heads=None, backward=True):
+    def compare(self, docs=None, kv_heads=None, backward=True, rows=None, keys=None):
+        """GPU results against the oracle.  Everywhere (checked on the GPU): finite values, O = 0 and LSE = -inf on
+        pad rows, dQ = 0 on pad rows and dK = dV = 0 on pad keys.  Within tolerance, with pads exact: the sampled
+        documents (all by default) on the sampled kv heads (their q heads) and, optionally, only the given local
+        rows (O, LSE, dQ) and physical keys (dK, dV).  The oracle gets just the sampled documents' rows and kv
+        heads, which leaves each computed entry's arithmetic as it is; only those entries leave the GPU."""
         wl = self.wl
         S, T = self.S, wl.T
-        o_ref, lse_ref, _ = oracle.attn_fwd(self.q_np, self.k_np, self.v_np, self.idx, wl.cu_padded, wl.cu_actual,
-                                            wl.softmax_scale, docs=docs, kv_heads=kv_heads)
-        o = to_np64(self.o[:S])
-        lse = to_np64(self.lse[:S])
-        assert np.isfinite(o).all(), "O must be finite everywhere"
-        _, _, valid_tok = oracle.token_map(wl.cu_padded, wl.cu_actual)
+        G = wl.Hq // wl.Hkv
+        dev = self.o.device
+        gsel = list(range(wl.Hkv)) if kv_heads is None else list(kv_heads)
+        hsel = [g * G + j for g in gsel for j in range(G)]
+        doc, _, valid_tok = oracle.token_map(wl.cu_padded, wl.cu_actual)
         vq = valid_tok[self.idx]
-        assert np.isneginf(lse[~vq]).all() and (o[~vq] == 0).all(), "pad rows: O = 0, LSE = -inf"
-        assert np.isfinite(lse[vq]).all()
-        assert_attn_close("O", o, o_ref, vq[:, None, None])
-        assert_attn_close("LSE", lse, lse_ref, vq[:, None])
+        lsel = np.arange(S) if docs is None else np.nonzero(np.isin(doc[self.idx], list(docs)))[0]
+        sub_rows = None if rows is None else np.nonzero(np.isin(lsel, rows))[0]
+        q_s, idx_s = self.q_np[lsel][:, hsel], self.idx[lsel]
+        k_s, v_s = self.k_np[:, gsel], self.v_np[:, gsel]
+        lsel_d, hsel_d, gsel_d = (torch.from_numpy(np.asarray(x, dtype=np.int64)).to(dev) for x in (lsel, hsel, gsel))
+
+        def rows_of(t):   # the sampled local rows and q heads of a [S, Hq, ...] GPU tensor, as float64 on the host
+            return t[:S].index_select(0, lsel_d).index_select(1, hsel_d).double().cpu().numpy()
+
+        vq_d = torch.from_numpy(vq).to(dev)
+        o_d, lse_d = self.o[:S], self.lse[:S]
+        assert bool(torch.isfinite(o_d).all()), "O must be finite everywhere"
+        assert bool((o_d[~vq_d] == 0).all()) and bool(torch.isneginf(lse_d[~vq_d]).all()), "pad rows: O = 0, LSE = -inf"
+        assert bool(torch.isfinite(lse_d[vq_d]).all())
+        o_s, lse_s, _ = oracle.attn_fwd(q_s, k_s, v_s, idx_s, wl.cu_padded, wl.cu_actual, wl.softmax_scale,
+                                        docs=docs, rows=sub_rows)
+        assert_attn_close("O", rows_of(self.o), o_s, vq[lsel][:, None, None])
+        assert_attn_close("LSE", rows_of(self.lse), lse_s, vq[lsel][:, None])
         if not backward:
             return
-        dq_ref, dk_ref, dv_ref = oracle.attn_bwd(self.q_np, self.k_np, self.v_np, self.do_np, self.idx,
-                                                 wl.cu_padded, wl.cu_actual, wl.softmax_scale, docs=docs,
-                                                 kv_heads=kv_heads)
-        dq = to_np64(self.dq[:S])
-        dk = to_np64(self.dk[:T])
-        dv = to_np64(self.dv[:T])
-        if self.allgathered:   # back to physical order
-            dk, dv = oracle.restore(dk, self.parts), oracle.restore(dv, self.parts)
-        for name, x in (("dQ", dq), ("dK", dk), ("dV", dv)):
-            assert np.isfinite(x).all(), f"{name} must be finite everywhere"
-        assert (dq[~vq] == 0).all() and (dk[~valid_tok] == 0).all() and (dv[~valid_tok] == 0).all()
-        assert_attn_close("dQ", dq, dq_ref, vq[:, None, None])
-        assert_attn_close("dK", dk, dk_ref, valid_tok[:, None, None])
-        assert_attn_close("dV", dv, dv_ref, valid_tok[:, None, None])
+        # dK/dV rows: physical order, or the rank-major gathered order of the all-gathered entry points
+        order = oracle.all_gather(np.arange(T), self.parts) if self.allgathered else np.arange(T)
+        at = np.empty(T, dtype=np.int64)
+        at[order] = np.arange(T)                      # at[p]: row of physical token p in the output
+        vt_d = torch.from_numpy(valid_tok[order]).to(dev)
+        dq_d, dk_d, dv_d = self.dq[:S], self.dk[:T], self.dv[:T]
+        for name, x in (("dQ", dq_d), ("dK", dk_d), ("dV", dv_d)):
+            assert bool(torch.isfinite(x).all()), f"{name} must be finite everywhere"
+        assert bool((dq_d[~vq_d] == 0).all()) and bool((dk_d[~vt_d] == 0).all()) and bool((dv_d[~vt_d] == 0).all())
+        dq_s, dk_s, dv_s = oracle.attn_bwd(q_s, k_s, v_s, self.do_np[lsel][:, hsel], idx_s, wl.cu_padded,
+                                           wl.cu_actual, wl.softmax_scale, docs=docs, rows=sub_rows, keys=keys)
+        krows = np.arange(T) if docs is None else np.nonzero(np.isin(doc, list(docs)))[0]
+        krows_d = torch.from_numpy(at[krows]).to(dev)
+
+        def keys_of(t):
+            return t.index_select(0, krows_d).index_select(1, gsel_d).double().cpu().numpy()
+
+        assert_attn_close("dQ", rows_of(self.dq), dq_s, vq[lsel][:, None, None])
+        assert_attn_close("dK", keys_of(dk_d), dk_s[krows], valid_tok[krows][:, None, None])
+        assert_attn_close("dV", keys_of(dv_d), dv_s[krows], valid_tok[krows][:, None, None])
 
 
 def _small_cases():
@@ -165,7 +193,7 @@ def _sample_docs(wl, idx, n=3):
     return sorted(pick)[:n]
 
 
-@pytest.mark.parametrize("s", [0, 1, 2])
+@pytest.mark.parametrize("s", [2])
 @pytest.mark.parametrize("r", [0, 3])
 def test_t32768_gqa32x8_sampled(s, r):
     wl = W.t32768_gqa32x8()
@@ -176,31 +204,140 @@ def test_t32768_gqa32x8_sampled(s, r):
     sh.compare(docs=docs, kv_heads=[0, 7])
 
 
-@pytest.mark.parametrize("s", [1, 2])
+def _largest_doc_samples(wl, idx, doc_id, n=64):
+    """Local rows (the rank's first, middle and last n rows of the document) and physical keys (the document's
+    first, middle and last n actual keys) to check in a document too large to compare in full."""
+    doc, pos, valid = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    lr = np.nonzero((doc[idx] == doc_id) & valid[idx])[0]
+    keys = np.nonzero((doc == doc_id) & valid)[0]
+
+    def ends(x):
+        if x.size <= 3 * n:
+            return x
+        mid = x.size // 2 - n // 2
+        return np.concatenate([x[:n], x[mid:mid + n], x[-n:]])
+
+    return ends(lr), ends(keys)
+
+
 @pytest.mark.parametrize("r", [0, 7])
-def test_t131072_gqa64x8_sampled(s, r):
+def test_t131072_gqa64x8_bench_step(r):
+    """The headline share as the benchmark runs it: GPU partition (bit-exact against the oracle), restoration (none
+    under the contiguous strategy: the call returns with the gathered buffer in place), plan, forward, backward,
+    on the workload's seeded inputs.  Against the oracle: the largest document the rank touches on sampled query
+    rows (O, LSE, dQ) and sampled keys (dK, dV), kv head 5; the smallest and the first-row documents in full on
+    kv heads 2 and 5."""
     wl = W.t131072_gqa64x8()
-    log(f"t131072_gqa64x8 s={s} r={r}")
-    sh = Share(wl, s, r)
+    T, cp, s = wl.T, wl.cp, 1
+    st = status_dev()
+    cu_p = i32_dev(wl.cu_padded)
+    idx_gpu = cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=st)
+    kv = (wl.k(), wl.v())
+    k_dev, v_dev = bf16_dev(kv[0]), bf16_dev(kv[1])
+    cpthd.reorder_kv(k_dev, v_dev, cu_p, T, cp, s, k_out=k_dev, v_out=v_dev, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    sh = Share(wl, s, r, kv=kv)
+    np.testing.assert_array_equal(idx_gpu.cpu().numpy(), sh.idx)
+    assert torch.equal(sh.k, k_dev) and torch.equal(sh.v, v_dev)
     doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
     touched = np.unique(doc[sh.idx])
     L = np.diff(wl.cu_padded.astype(np.int64))[touched]
-    docs = sorted({int(touched[np.argmin(L)]), int(doc[sh.idx[0]])})
-    log(f"  docs {docs}")
-    sh.compare(docs=docs, kv_heads=[5])
+    big = int(touched[np.argmax(L)])
+    rows, keys = _largest_doc_samples(wl, sh.idx, big)
+    log(f"  largest document {big} ({int(L.max())} tokens): {rows.size} rows, {keys.size} keys")
+    set_case(f"{wl.name} contiguous r{r} largest document (sampled rows and keys)")
+    sh.compare(docs=[big], kv_heads=[5], rows=rows, keys=keys)
+    small = sorted({int(touched[np.argmin(L)]), int(doc[sh.idx[0]])} - {big})
+    if small:
+        log(f"  documents {small} in full")
+        set_case(f"{wl.name} contiguous r{r} smallest / first-row documents")
+        sh.compare(docs=small, kv_heads=[2, 5])
 
 
-def test_dynamic_t_capacity_microbatches():
-    """Fixed-capacity buffers, NaN-poisoned beyond the active T, canaries on output tails."""
-    for m in (0, 5, 11):
-        wl = W.dynamic_t(m)
-        for s in wl.strategies + (2,):
-            for r in (0, 3):
-                log(f"dynamic_t mb={m} T={wl.T} s={s} r={r}")
-                sh = Share(wl, s, r, capacity=W.DYNAMIC_T_CAPACITY, poison=True)
-                sh.check_tails()
-                docs = _sample_docs(wl, sh.idx, n=2)
-                sh.compare(docs=docs, kv_heads=[3])
+@pytest.mark.parametrize("m", range(W.DYNAMIC_T_MICROBATCHES))
+def test_dynamic_t_every_share(m):
+    """Every share of dynamic-T micro-batch m: ranks 0-3 under DualChunkSwap and contiguous ownership (and the
+    packed strategy on every fourth micro-batch), on buffers allocated for the 65,536-token capacity and
+    NaN-poisoned past the active T, with canaries on the output tails.  Each share's largest, smallest and
+    first-row documents are compared with the oracle on kv heads 1 and 6."""
+    wl = W.dynamic_t(m)
+    kv, qdo = (wl.k(), wl.v()), (wl.q(), wl.do())
+    for s in (0, 1) + ((2,) if m % 4 == 0 else ()):
+        for r in range(wl.cp):
+            log(f"dynamic_t mb={m} T={wl.T} s={s} r={r}")
+            sh = Share(wl, s, r, capacity=W.DYNAMIC_T_CAPACITY, poison=True, kv=kv, qdo=qdo)
+            sh.check_tails()
+            docs = _sample_docs(wl, sh.idx)
+            log(f"  docs {docs}")
+            sh.compare(docs=docs, kv_heads=[1, 6])
+            del sh
+
+
+def _many_docs_layout(cp, seed, n=1600):
+    """n documents of 2*cp to 16*cp tokens with random actual lengths (pads), plus a run of 20 longer ones."""
+    rng = np.random.default_rng([91, cp, seed])
+    units = rng.integers(1, 9, size=n)
+    units[n // 2:n // 2 + 20] = rng.integers(20, 60, size=20)
+    padded = 2 * cp * units
+    actual = np.array([int(rng.integers(0, L + 1)) for L in padded])
+    actual[::7] = padded[::7]
+    return W.Workload(f"many_docs.cp{cp}", [91, cp, seed], int(padded.sum()), 4, 2, 64, W._cu(padded), W._cu(actual),
+                      cp, (0, 1, 2), tuple(range(cp)), True, qkv_scale=0.5, do_scale=1.0, bf16=True)
+
+
+MANY = [_many_docs_layout(2, 0, 3000), _many_docs_layout(3, 1)]
+
+
+@pytest.mark.parametrize("wl", MANY, ids=lambda w: w.name)
+@pytest.mark.parametrize("allgathered", [False, True])
+def test_more_than_1024_documents(wl, allgathered):
+    """Layouts of more than 1024 documents take the plan kernel's chunked scan and emission (carries between
+    chunks of 1024 documents): plan, forward and backward under all three strategies, every rank, compared with
+    the oracle in full."""
+    assert wl.num_docs > 1024
+    kv, qdo = (wl.k(), wl.v()), (wl.q(), wl.do())
+    for s in (0, 1, 2):
+        for r in range(wl.cp):
+            log(f"{wl.name} docs={wl.num_docs} T={wl.T} s={s} r={r} allgathered={allgathered}")
+            Share(wl, s, r, kv=kv, qdo=qdo, allgathered=allgathered).compare()
+
+
+@pytest.mark.parametrize("s,r", [(0, 0), (0, 3), (1, 0), (1, 3)])
+def test_t32768_gqa32x8_chained_step(s, r):
+    """The benchmark's step on the Llama-3-8B-shaped workload as one chain of library calls: GPU partition indices,
+    the rank's Q and dO rows gathered by them (input partitioning), K/V restored from the rank-major gathered
+    buffer, plan, forward, backward; the indices and restored K/V bit-exact and the attention outputs against the
+    oracle on each share's largest, smallest and first-row documents, kv heads 0 and 7."""
+    wl = W.t32768_gqa32x8()
+    T, cp = wl.T, wl.cp
+    S = T // cp
+    st = status_dev()
+    cu_p, cu_a = i32_dev(wl.cu_padded), i32_dev(wl.cu_actual)
+    k_np, v_np, q_np, do_np = wl.k(), wl.v(), wl.q(), wl.do()
+    parts = [oracle.partition_indices(wl.cu_padded, cp, rr, s) for rr in range(cp)]
+    kg, vg = bf16_dev(oracle.all_gather(k_np, parts)), bf16_dev(oracle.all_gather(v_np, parts))  # simulated all-gather
+    q_full, do_full = bf16_dev(q_np), bf16_dev(do_np)
+    idx = cpthd.partition_indices(cu_p, T, cp, r, s, dev_status=st)
+    q_loc = cpthd.gather_rows(q_full, idx, dev_status=st)
+    do_loc = cpthd.gather_rows(do_full, idx, dev_status=st)
+    k, v = cpthd.reorder_kv(kg, vg, cu_p, T, cp, s, dev_status=st)
+    plan = cpthd.AttnPlan(T, cp, wl.Hq, wl.Hkv, wl.D, max_docs=wl.num_docs)
+    plan.build(cu_a, cu_p, T, r, s, st)
+    o, lse = cpthd.attn_fwd(q_loc, k, v, plan, wl.softmax_scale, dev_status=st)
+    dq, dk, dv = cpthd.attn_bwd(q_loc, k, v, o, do_loc, lse, plan, wl.softmax_scale, dev_status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    np.testing.assert_array_equal(idx.cpu().numpy(), parts[r])
+    assert torch.equal(k, bf16_dev(k_np)) and torch.equal(v, bf16_dev(v_np))
+    assert torch.equal(q_loc, bf16_dev(q_np[parts[r]]))
+    # compare through the Share helper's oracle path, with the chain's outputs in place of its own
+    sh = Share.__new__(Share)
+    sh.wl, sh.s, sh.r, sh.idx, sh.allgathered, sh.S = wl, s, r, parts[r], False, S
+    sh.q_np, sh.k_np, sh.v_np, sh.do_np = q_np[parts[r]], k_np, v_np, do_np[parts[r]]
+    sh.o, sh.lse, sh.dq, sh.dk, sh.dv = o, lse, dq, dk, dv
+    set_case(f"{wl.name} {STRAT[s]} r{r} chained step")
+    sh.compare(docs=_sample_docs(wl, parts[r]), kv_heads=[0, 7])
 
 
 # ---------------------------------------------------------------------------
@@ -281,18 +418,78 @@ def test_degenerate_layouts(wl, allgathered):
         Share(wl, s, r, allgathered=allgathered).compare()
 
 
-def test_plan_mismatch_sets_status_and_writes_nothing():
+def _shifted_layout(wl, seed):
+    """Another micro-batch of the same T and document count: one interior boundary moved by 2*cp tokens (actual
+    lengths clipped to the new slots), so every size argument of a call is unchanged."""
+    rng = np.random.default_rng(seed)
+    cu_p = wl.cu_padded.astype(np.int64).copy()
+    L = np.diff(cu_p)
+    step = 2 * wl.cp
+    cands = [i for i in range(1, wl.num_docs) if L[i - 1] > step and L[i] > step]
+    i = int(rng.choice(cands))
+    cu_p[i] += step if rng.integers(2) else -step
+    a = np.minimum(np.diff(wl.cu_actual.astype(np.int64)), np.diff(cu_p))
+    cu_a = np.concatenate([[0], np.cumsum(a)])
+    out = W.Workload(wl.name + ".shifted", wl.seed_key, wl.T, wl.Hq, wl.Hkv, wl.D, cu_p.astype(np.int32),
+                     cu_a.astype(np.int32), wl.cp, wl.strategies, wl.ranks, True, wl.qkv_scale, wl.do_scale, wl.bf16,
+                     wl.capacity)
+    oracle.check_layout(out.cu_padded, out.cu_actual, out.cp, 0)
+    return out
+
+
+@pytest.mark.parametrize("allgathered", [False, True])
+def test_call_with_other_microbatch_rebuilds_the_plan(allgathered):
+    """A workspace holding micro-batch A's plan, called with micro-batch B's cu arrays (same T, same document
+    count, same rank and strategy: every size argument equal), computes B's attention: the call checks the plan
+    against its own cu arrays and rebuilds it.  Backward with B after forward with A likewise."""
+    wl_a = W.small_random(21, 2, 0, max_docs=5, max_len=300, Hq=8, Hkv=2, D=64, bf16=True, qkv_scale=0.5,
+                          do_scale=1.0)
+    wl_b = _shifted_layout(wl_a, 3)
+    assert not np.array_equal(wl_a.cu_padded, wl_b.cu_padded) and wl_a.T == wl_b.T
+    sh_a = Share(wl_a, 0, 1, allgathered=allgathered)           # builds A's plan and runs A
+    sh_b = Share(wl_b, 0, 1, allgathered=allgathered)           # reference run of B on a fresh workspace
+    st = status_dev()
+    o = torch.full_like(sh_b.o, 3.0)
+    lse = torch.full_like(sh_b.lse, 3.0)
+    dq, dk, dv = (torch.full_like(x, 3.0) for x in (sh_b.dq, sh_b.dk, sh_b.dv))
+    lay_b = cpthd.Layout(sh_b.cu_a, sh_b.cu_p, wl_b.T, 1, 0)
+    # A's workspace, B's layout: forward, then backward
+    cpthd.attn_fwd(sh_b.q, sh_b.k, sh_b.v, sh_a.plan, wl_b.softmax_scale, o, lse, st, kv_allgathered=allgathered,
+                   layout=lay_b)
+    sh_a.plan.build(sh_a.cu_a, sh_a.cu_p, wl_a.T, 1, 0, st)    # A's plan again before B's backward
+    cpthd.attn_bwd(sh_b.q, sh_b.k, sh_b.v, o, sh_b.do, lse, sh_a.plan, wl_b.softmax_scale, dq, dk, dv, st,
+                   kv_allgathered=allgathered, layout=lay_b)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for x, y in ((o, sh_b.o), (lse, sh_b.lse), (dq, sh_b.dq), (dk, sh_b.dk), (dv, sh_b.dv)):
+        assert torch.equal(_bits(x), _bits(y))
+
+
+def test_rejected_layout_writes_no_output():
+    """A micro-batch whose cu arrays the plan rejects (a DualChunkSwap document not divisible by 2*cp_size) sets
+    the layout bit and the plan bit, and the attention calls leave every output untouched."""
     wl = W.tiny_t28(bf16=True)
     sh = Share(wl, 0, 0)
     st = status_dev()
     o = torch.full_like(sh.o, 3.0)
     lse = torch.full_like(sh.lse, 3.0)
-    # rank 1 against a plan built for rank 0
-    cpthd.cpthd_attn_fwd(sh.q, sh.k, sh.v, wl.T, wl.T, wl.num_docs, wl.cp, 1, 0, wl.Hq, wl.Hkv, wl.D,
-                         wl.softmax_scale, 1, -1, 0, o, lse, sh.plan.workspace, st)
+    dq, dk, dv = (torch.full_like(x, 3.0) for x in (sh.dq, sh.dk, sh.dv))
+    bad = cpthd.Layout(i32_dev([0, 6, 20, 28]), i32_dev([0, 6, 20, 28]), wl.T, 0, 0)   # 6 % 4 != 0
+    cpthd.attn_fwd(sh.q, sh.k, sh.v, sh.plan, wl.softmax_scale, o, lse, st, layout=bad)
+    cpthd.attn_bwd(sh.q, sh.k, sh.v, sh.o, sh.do, sh.lse, sh.plan, wl.softmax_scale, dq, dk, dv, st, layout=bad)
     torch.cuda.synchronize()
-    assert int(st.item()) & 16
-    assert (o.float() == 3.0).all() and (lse == 3.0).all()
+    assert int(st.item()) & 4 and int(st.item()) & 16
+    for x in (o, lse, dq, dk, dv):
+        assert (x.float() == 3.0).all()
+
+
+def test_attention_wrapper_raises_on_a_rejected_layout():
+    wl = W.tiny_t28(bf16=True)
+    sh = Share(wl, 0, 0)
+    plan = cpthd.AttnPlan(wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D, max_docs=wl.num_docs)
+    plan.build(i32_dev([0, 6, 20, 28]), i32_dev([0, 6, 20, 28]), wl.T, 0, 0)
+    with pytest.raises(ValueError, match="divisible"):
+        cpthd.attention(sh.q[:wl.T // wl.cp], sh.k, sh.v, plan, wl.softmax_scale)
 
 
 def test_plan_rejects_bad_layouts():
@@ -324,33 +521,31 @@ def test_plan_rejects_documents_of_2gib_kv():
 
 @pytest.mark.parametrize("allgathered", [False, True])
 def test_autograd_wrapper_matches_entry_points(allgathered):
-    """cpthd.attention (autograd) gives the entry points' O bit for bit, and gradients equal to the fp32
-    dQ/dK/dV cast to the inputs' dtype; a plan rebuilt in any way before backward is refused."""
+    """cpthd.attention (autograd) on capacity-sized, NaN-poisoned inputs gives the entry points' O bit for bit and
+    gradients equal to the fp32 dQ/dK/dV cast to the inputs' dtype, with zero gradients on the capacity tails;
+    backward runs with the layout captured in forward even when the plan was rebuilt for another in between."""
     wl = W.small_random(5, 2, 0, max_docs=4, max_len=300, Hq=8, Hkv=2, D=64, bf16=True, qkv_scale=0.5,
                         do_scale=1.0)
     S, T = wl.T // wl.cp, wl.T
-    sh = Share(wl, 0, 1, allgathered=allgathered)
-    q = sh.q[:S].clone().requires_grad_()
-    k = sh.k[:T].clone().requires_grad_()
-    v = sh.v[:T].clone().requires_grad_()
-    o = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
-    assert torch.equal(o.detach(), sh.o[:S])
-    o.backward(sh.do[:S])
-    torch.cuda.synchronize()
-    assert torch.equal(q.grad, sh.dq[:S].to(torch.bfloat16))
-    assert torch.equal(k.grad, sh.dk[:T].to(torch.bfloat16))
-    assert torch.equal(v.grad, sh.dv[:T].to(torch.bfloat16))
-    o2 = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
-    sh.plan.build(sh.cu_a, sh.cu_p, T, 0, 0, sh.st)          # another rank's layout
-    with pytest.raises(RuntimeError, match="rebuilt"):
-        o2.backward(sh.do[:S])
-    # a rebuild with the same sizes, rank and strategy (as for the next micro-batch of equal length) is
-    # refused as well: other document boundaries would give other tiles
-    sh.plan.build(sh.cu_a, sh.cu_p, T, 1, 0, sh.st)
-    o3 = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
-    sh.plan.build(sh.cu_a, sh.cu_p, T, 1, 0, sh.st)
-    with pytest.raises(RuntimeError, match="rebuilt"):
-        o3.backward(sh.do[:S])
+    cap = T + 64
+    sh = Share(wl, 0, 1, allgathered=allgathered, capacity=cap, poison=True)
+    q = sh.q.clone().requires_grad_()          # [cap/cp, ...] with NaN past S
+    k = sh.k.clone().requires_grad_()          # [cap, ...] with NaN past T
+    v = sh.v.clone().requires_grad_()
+    for rebuild in (False, True):
+        q.grad = k.grad = v.grad = None
+        o = cpthd.attention(q, k, v, sh.plan, wl.softmax_scale, kv_allgathered=allgathered)
+        assert torch.equal(o.detach(), sh.o[:S])
+        if rebuild:   # another rank's layout in the same workspace before backward
+            sh.plan.build(sh.cu_a, sh.cu_p, T, 0, 0, sh.st)
+        o.backward(sh.do[:S])
+        torch.cuda.synchronize()
+        assert torch.equal(q.grad[:S], sh.dq[:S].to(torch.bfloat16))
+        assert torch.equal(k.grad[:T], sh.dk[:T].to(torch.bfloat16))
+        assert torch.equal(v.grad[:T], sh.dv[:T].to(torch.bfloat16))
+        assert (q.grad[S:] == 0).all() and (k.grad[T:] == 0).all() and (v.grad[T:] == 0).all()
+        if rebuild:
+            sh.plan.build(sh.cu_a, sh.cu_p, T, 1, 0, sh.st)
 
 
 # dK/dV sum G heads of P * dO, so their magnitude (and the absolute rounding of the bf16 P operand) grows

@@ -243,3 +243,30 @@ def test_kv_head_subset_matches_full():
         np.testing.assert_array_equal(sdk[:, g], dk[:, g])
         np.testing.assert_array_equal(sdv[:, g], dv[:, g])
         assert np.isnan(so[:, 2 * (1 - g)]).all() and np.isnan(sdk[:, 1 - g]).all()
+
+
+def test_row_and_key_sampling_matches_full():
+    """Restricting the oracle to sampled query rows (O, LSE, dQ) and sampled keys (dK, dV) gives exactly the full
+    computation's values on those entries and NaN elsewhere."""
+    for seed, cp, strat in ((31, 2, 0), (32, 3, 1), (33, 2, 2)):
+        wl = W.small_random(seed, cp, strat, max_docs=5, max_len=120, Hq=4, Hkv=2, D=16)
+        for r in range(cp):
+            idx = oracle.partition_indices(wl.cu_padded, cp, r, strat)
+            q, k, v, do = wl.q(idx), wl.k(), wl.v(), wl.do(idx)
+            rng = np.random.default_rng(seed + r)
+            rows = np.unique(rng.integers(0, max(idx.size, 1), size=max(idx.size // 3, 1)))
+            keys = np.unique(rng.integers(0, wl.T, size=max(wl.T // 3, 1)))
+            o, lse, _ = oracle.attn_fwd(q, k, v, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale)
+            dq, dk, dv = oracle.attn_bwd(q, k, v, do, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale)
+            o_s, lse_s, comp = oracle.attn_fwd(q, k, v, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale, rows=rows)
+            dq_s, dk_s, dv_s = oracle.attn_bwd(q, k, v, do, idx, wl.cu_padded, wl.cu_actual, wl.softmax_scale,
+                                               rows=rows, keys=keys)
+            rmask = np.zeros(idx.size, dtype=bool)
+            rmask[rows[rows < idx.size]] = True
+            kmask = np.zeros(wl.T, dtype=bool)
+            kmask[keys] = True
+            assert np.array_equal(comp, rmask)
+            for full, samp, m in ((o, o_s, rmask), (lse, lse_s, rmask), (dq, dq_s, rmask), (dk, dk_s, kmask),
+                                  (dv, dv_s, kmask)):
+                assert np.isnan(samp[~m]).all()
+                np.testing.assert_allclose(samp[m], full[m], rtol=1e-12, atol=1e-12)

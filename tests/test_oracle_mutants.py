@@ -30,10 +30,14 @@ MUTANTS = [
     ("gqa_map", "kd = k[start:start + a, h // G]", "kd = k[start:start + a, h % k.shape[1]]"),
     ("no_scale_fwd", "s = scale * (q_local[r, h] @ kd.T)", "s = (q_local[r, h] @ kd.T)"),
     ("lse_no_max", "lse[r, h] = m + np.log(den)", "lse[r, h] = np.log(den)"),
-    ("dk_no_scale", "dk[start:start + a, g] += scale * (ds.T @ q_local[r, h])", "dk[start:start + a, g] += (ds.T @ q_local[r, h])"),
-    ("dq_wrong_operand", "dq[r, h] = scale * (ds @ kd)", "dq[r, h] = scale * (ds @ vd)"),
-    ("ds_sign", "ds = p * (dp - delta[:, None])", "ds = p * (delta[:, None] - dp)"),
-    ("dv_wrong_operand", "dv[start:start + a, g] += p.T @ dout", "dv[start:start + a, g] += ds.T @ dout"),
+    ("dk_no_scale", "dk[start + kk, g] += scale * (ds_k.T @ q_local[r, h])", "dk[start + kk, g] += (ds_k.T @ q_local[r, h])"),
+    ("dq_wrong_operand", "dq[r[rq], h] = scale * (ds_r @ kd)", "dq[r[rq], h] = scale * (ds_r @ vd)"),
+    ("ds_sign_dq", "ds_r = p[rq] * (dout[rq] @ vd.T - delta[rq, None])", "ds_r = p[rq] * (delta[rq, None] - dout[rq] @ vd.T)"),
+    ("ds_sign_dk", "ds_k = p[:, kk] * (dout @ vd[kk].T - delta[:, None])", "ds_k = p[:, kk] * (delta[:, None] - dout @ vd[kk].T)"),
+    ("dv_wrong_operand", "dv[start + kk, g] += p[:, kk].T @ dout", "dv[start + kk, g] += ds_k.T @ dout"),
+    ("key_subset_drops_a_key", "kk = np.nonzero(ksel[start:start + a])[0]", "kk = np.nonzero(ksel[start:start + a])[0][1:]"),
+    ("row_subset_drops_rows", "rq = rsel[r]", "rq = rsel[r] & (qpos[b0:b0 + _ROW_BLOCK] != 1)"),
+    ("fwd_row_subset_drops_rows", "keep = rsel[drows]", "keep = rsel[drows] & (qpos != 1)"),
     ("delta_dropped", "delta = np.sum(dout * o, axis=1)", "delta = np.sum(dout * o, axis=1) * 0"),
     ("packed_per_half", "return partition_indices([0, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)",
      "return partition_indices([0, cu_p[-1] // 2, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)"),

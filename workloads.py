@@ -47,10 +47,11 @@ ROW_BLOCK = 4096
 # ----------------------------------------------------------------------------
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """float32 -> bf16 bit patterns (uint16), round to nearest, ties to even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    bits = r.astype(np.uint16)
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    # u + 0x7FFF + lsb stays below 2^32 for every finite value (the largest is 0x7F7FFFFF); NaNs are set below
+    r = u + (np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+    bits = (r >> np.uint32(16)).astype(np.uint16)
     nan = np.isnan(x)
     if nan.any():
         bits[nan] = np.uint16(0x7FC0)
