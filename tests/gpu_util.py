@@ -37,7 +37,11 @@ def _record(name, mx, rel, n):
 
 
 def bf16_dev(x):
-    bits = W.to_bf16_bits(np.ascontiguousarray(x, dtype=np.float32))
+    """float32 values -> a bf16 device tensor (round to nearest even; values the seeded generators already rounded
+    to bf16 keep their bits)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32)
+    bits = (u >> np.uint32(16)).astype(np.uint16) if not (u & np.uint32(0xFFFF)).any() else W.to_bf16_bits(x)
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to("cuda")
 
 

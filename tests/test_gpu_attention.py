@@ -25,14 +25,15 @@ class Share:
     """One rank's share on the GPU: plan, forward and (optionally) backward."""
 
     def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False, allgathered=False,
-                 kv=None, qdo=None):
+                 kv=None, qdo=None, dev_in=None):
         self.wl, self.s, self.r = wl, strategy, rank
         T, cp = wl.T, wl.cp
         S = T // cp
         cap = capacity or T
         capS = cap // cp
         self.idx = oracle.partition_indices(wl.cu_padded, cp, rank, strategy)
-        # kv / qdo: the workload's physical-order K, V / Q, dO, generated once by the caller
+        # kv / qdo: the workload's physical-order K, V / Q, dO on the host, generated once by the caller;
+        # dev_in: the same four as bf16 device tensors (uploaded once by the caller)
         q = qdo[0][self.idx] if qdo is not None else wl.q(self.idx)
         k, v = kv if kv is not None else (wl.k(), wl.v())
         self.q_np, self.k_np, self.v_np = q, k, v
@@ -40,14 +41,24 @@ class Share:
         # rank-major all-gathered K/V (the simulated all-gather of every rank's local rows)
         self.allgathered = allgathered
         self.parts = [oracle.partition_indices(wl.cu_padded, cp, rr, strategy) for rr in range(cp)]
-        if allgathered:
+        idx_d = torch.from_numpy(self.idx).to("cuda") if dev_in is not None else None
+        if dev_in is not None:
+            k, v = dev_in["k"], dev_in["v"]
+            if allgathered:
+                order = torch.from_numpy(oracle.all_gather(np.arange(T), self.parts)).to("cuda")
+                k, v = k[order], v[order]
+            q = dev_in["q"][idx_d]
+        elif allgathered:
             k, v = oracle.all_gather(k, self.parts), oracle.all_gather(v, self.parts)
         fill = float("nan") if poison else 0.0
 
         def buf(shape_tail, src, dtype=torch.bfloat16, rows=cap):
             t = torch.full((rows,) + shape_tail, fill, dtype=dtype, device="cuda")
             if src is not None:
-                t[:src.shape[0]] = bf16_dev(src) if dtype == torch.bfloat16 else src
+                if isinstance(src, torch.Tensor):
+                    t[:src.shape[0]] = src
+                else:
+                    t[:src.shape[0]] = bf16_dev(src) if dtype == torch.bfloat16 else src
             return t
 
         self.q = buf((wl.Hq, wl.D), q, rows=capS)
@@ -66,6 +77,8 @@ class Share:
         if backward:
             do = qdo[1][self.idx] if qdo is not None else wl.do(self.idx)
             self.do_np = do
+            if dev_in is not None:
+                do = dev_in["do"][idx_d]
             self.do = buf((wl.Hq, wl.D), do, rows=capS)
             self.dq = torch.full((capS, wl.Hq, wl.D), canary, dtype=torch.float32, device="cuda")
             self.dk = torch.full((cap, wl.Hkv, wl.D), canary, dtype=torch.float32, device="cuda")
@@ -263,10 +276,11 @@ def test_dynamic_t_every_share(m):
     first-row documents are compared with the oracle on kv heads 1 and 6."""
     wl = W.dynamic_t(m)
     kv, qdo = (wl.k(), wl.v()), (wl.q(), wl.do())
+    dev_in = dict(k=bf16_dev(kv[0]), v=bf16_dev(kv[1]), q=bf16_dev(qdo[0]), do=bf16_dev(qdo[1]))
     for s in (0, 1) + ((2,) if m % 4 == 0 else ()):
         for r in range(wl.cp):
             log(f"dynamic_t mb={m} T={wl.T} s={s} r={r}")
-            sh = Share(wl, s, r, capacity=W.DYNAMIC_T_CAPACITY, poison=True, kv=kv, qdo=qdo)
+            sh = Share(wl, s, r, capacity=W.DYNAMIC_T_CAPACITY, poison=True, kv=kv, qdo=qdo, dev_in=dev_in)
             sh.check_tails()
             docs = _sample_docs(wl, sh.idx)
             log(f"  docs {docs}")
@@ -297,10 +311,11 @@ def test_more_than_1024_documents(wl, allgathered):
     the oracle in full."""
     assert wl.num_docs > 1024
     kv, qdo = (wl.k(), wl.v()), (wl.q(), wl.do())
+    dev_in = dict(k=bf16_dev(kv[0]), v=bf16_dev(kv[1]), q=bf16_dev(qdo[0]), do=bf16_dev(qdo[1]))
     for s in (0, 1, 2):
         for r in range(wl.cp):
             log(f"{wl.name} docs={wl.num_docs} T={wl.T} s={s} r={r} allgathered={allgathered}")
-            Share(wl, s, r, kv=kv, qdo=qdo, allgathered=allgathered).compare()
+            Share(wl, s, r, kv=kv, qdo=qdo, dev_in=dev_in, allgathered=allgathered).compare()
 
 
 @pytest.mark.parametrize("s,r", [(0, 0), (0, 3), (1, 0), (1, 3)])
@@ -575,7 +590,8 @@ def test_strategies_agree_on_every_row(name):
     wl = W.t32768_gqa32x8() if name == "t32768_gqa32x8" else W.t131072_gqa64x8()
     strategies = (0, 1, 2) if name == "t32768_gqa32x8" else (1, 2)
     T, cp = wl.T, wl.cp
-    kv = (wl.k(), wl.v())
+    kv, qdo = (wl.k(), wl.v()), (wl.q(), wl.do())
+    dev_in = dict(k=bf16_dev(kv[0]), v=bf16_dev(kv[1]), q=bf16_dev(qdo[0]), do=bf16_dev(qdo[1]))
     res = {}
     for s in strategies:
         o = torch.zeros((T, wl.Hq, wl.D), dtype=torch.float32, device="cuda")
@@ -585,7 +601,7 @@ def test_strategies_agree_on_every_row(name):
         dv = torch.zeros((T, wl.Hkv, wl.D), dtype=torch.float32, device="cuda")
         for r in range(cp):
             log(f"{name} s={s} r={r}")
-            sh = Share(wl, s, r, kv=kv)
+            sh = Share(wl, s, r, kv=kv, qdo=qdo, dev_in=dev_in)
             idx = torch.from_numpy(sh.idx.astype(np.int64)).to("cuda")
             S = T // cp
             o[idx] = sh.o[:S].float()

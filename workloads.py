@@ -34,6 +34,7 @@ Q, K, V and dO are all in physical token order ``[T, H, D]``.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
@@ -127,25 +128,46 @@ def docs_composition(rng, units, parts, unit_len):
 def normal_rows(seed_key, tid, n_rows, heads, dim, scale=1.0, rows=None, bf16=True):
     """Rows of an [n_rows, heads, dim] N(0,1)*scale tensor, drawn block-wise.
 
-    ``rows`` (int array) selects physical rows; None means all of them.
+    ``rows`` (int array) selects physical rows; None means all of them.  Blocks
+    are independent draws, so they are generated (and rounded) on a few threads.
     """
     key = list(seed_key) if isinstance(seed_key, (list, tuple)) else [int(seed_key)]
-    if rows is None:
+    whole = rows is None
+    if whole:
         rows = np.arange(n_rows, dtype=np.int64)
     rows = np.asarray(rows, dtype=np.int64)
     out = np.empty((rows.size, heads, dim), dtype=np.float32)
     if rows.size == 0:
         return out
-    blocks = np.unique(rows // ROW_BLOCK)
-    for b in blocks:
-        lo = int(b) * ROW_BLOCK
+    order = np.argsort(rows // ROW_BLOCK, kind="stable")
+    blk_of = rows[order] // ROW_BLOCK
+    starts = np.searchsorted(blk_of, np.unique(blk_of))
+    ends = list(starts[1:]) + [rows.size]
+
+    def one(i):
+        b = int(blk_of[starts[i]])
+        lo = b * ROW_BLOCK
         nb = min(ROW_BLOCK, n_rows - lo)
-        blk = np.random.default_rng(key + [tid, int(b)]).standard_normal((nb, heads, dim), dtype=np.float32)
+        blk = np.random.default_rng(key + [tid, b]).standard_normal((nb, heads, dim), dtype=np.float32)
         if scale != 1.0:
             blk *= np.float32(scale)
-        sel = np.nonzero((rows // ROW_BLOCK) == b)[0]
-        out[sel] = blk[rows[sel] - lo]
-    return round_to_bf16(out) if bf16 else out
+        if bf16:
+            blk = round_to_bf16(blk)
+        if whole:
+            out[lo:lo + nb] = blk
+        else:
+            sel = order[starts[i]:ends[i]]
+            out[sel] = blk[rows[sel] - lo]
+
+    n = len(starts)
+    if n == 1 or rows.size * heads * dim < (1 << 22):
+        for i in range(n):
+            one(i)
+    else:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1, n)) as ex:
+            list(ex.map(one, range(n)))
+    return out
 
 
 @dataclass
