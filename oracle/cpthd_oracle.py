@@ -285,10 +285,14 @@ def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=Non
         dk[np.ix_(slot & ksel, gsel)] = 0.0
         dv[np.ix_(slot & ksel, gsel)] = 0.0
     for d, drows, qpos, start, a in _doc_rows(idx, cu_padded, cu_actual, docs):
-        if drows.size == 0:
-            continue
         kpos = np.arange(a)
         kk = np.nonzero(ksel[start:start + a])[0]      # the requested keys among the document's actual keys
+        # the rows whose results are requested (dQ) or that see a requested key (dK, dV); no other row
+        # contributes to a requested output
+        need = rsel[drows] | (qpos >= (kk[0] if kk.size else a))
+        drows, qpos = drows[need], qpos[need]
+        if drows.size == 0:
+            continue
         for h in range(Hq):
             g = h // G
             if kv_heads is not None and g not in kv_heads:
@@ -307,11 +311,15 @@ def attn_bwd(q_local, k, v, do_local, idx, cu_padded, cu_actual, scale, docs=Non
                 dout = do_local[r, h]
                 delta = np.sum(dout * o, axis=1)             # rowsum(dO * O) = rowsum(P * dP)
                 rq = rsel[r]
-                if rq.any():                                 # dL/dS of the requested rows over all keys
-                    ds_r = p[rq] * (dout[rq] @ vd.T - delta[rq, None])
+                if rq.all() or kk.size == a:                 # dL/dS of the whole block serves both
+                    ds = p * (dout @ vd.T - delta[:, None])
+                    ds_r, ds_k, p_k = ds[rq], ds[:, kk], p[:, kk]
+                else:                                        # the requested rows over all keys, every row at
+                    ds_r = p[rq] * (dout[rq] @ vd.T - delta[rq, None])       # the requested keys
+                    ds_k, p_k = p[:, kk] * (dout @ vd[kk].T - delta[:, None]), p[:, kk]
+                if rq.any():
                     dq[r[rq], h] = scale * (ds_r @ kd)
-                if kk.size:                                  # dL/dS of every row at the requested keys
-                    ds_k = p[:, kk] * (dout @ vd[kk].T - delta[:, None])
+                if kk.size:
                     dk[start + kk, g] += scale * (ds_k.T @ q_local[r, h])
-                    dv[start + kk, g] += p[:, kk].T @ dout
+                    dv[start + kk, g] += p_k.T @ dout
     return dq, dk, dv

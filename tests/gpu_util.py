@@ -86,3 +86,56 @@ def assert_attn_close(name, got, ref, valid=None):
         _record(name, mx, rel, g.size)
         assert mx <= ATOL, f"{name}: max abs error {mx:.4e} > {ATOL}"
         assert rel <= REL_L2, f"{name}: relative L2 error {rel:.4e} > {REL_L2}"
+
+
+def oracle_sampled(q_s, k_s, v_s, do_s, idx_s, cu_padded, cu_actual, scale, G, docs=None, rows=None, keys=None):
+    """The oracle's forward (and backward when do_s is given) on pre-selected inputs: q_s / do_s hold the query
+    rows idx_s (local order) of the sampled documents with the q heads of the sampled kv heads (G per kv head,
+    kv head j's at columns j*G .. j*G+G-1), k_s / v_s all T rows of those kv heads.  The work is split into one
+    oracle call per (document, kv head) and the calls run on a thread pool with a small BLAS thread count each:
+    numpy's element-wise passes are single-threaded, and the units are independent (every output entry is
+    computed by exactly one call, with the oracle's own arithmetic).  Returns o, lse, dq over the q_s rows and
+    heads, and dk, dv over all T rows of the sampled kv heads (NaN where nothing was computed)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+    from threadpoolctl import threadpool_limits
+
+    n, nh = q_s.shape[0], k_s.shape[1]
+    T, D = k_s.shape[0], k_s.shape[2]
+    doc_of = oracle.token_map(cu_padded, cu_actual)[0][np.asarray(idx_s, dtype=np.int64)]
+    units = [(d, j) for d in (docs if docs is not None else [None]) for j in range(nh)]
+    o = np.full((n, nh * G, D), np.nan)
+    lse = np.full((n, nh * G), np.nan)
+    dq = np.full((n, nh * G, D), np.nan)
+    dk = np.full((T, nh, D), np.nan)
+    dv = np.full((T, nh, D), np.nan)
+    cu_p = np.asarray(cu_padded, dtype=np.int64)
+
+    def run(unit):
+        d, j = unit
+        ru = np.arange(n) if d is None else np.nonzero(doc_of == d)[0]
+        rr = None if rows is None else np.nonzero(np.isin(ru, rows))[0]
+        hs = slice(j * G, (j + 1) * G)
+        qu, iu = q_s[ru][:, hs], np.asarray(idx_s)[ru]
+        ku, vu = k_s[:, j:j + 1], v_s[:, j:j + 1]
+        dd = None if d is None else [d]
+        ou, lu, _ = oracle.attn_fwd(qu, ku, vu, iu, cu_padded, cu_actual, scale, docs=dd, rows=rr)
+        out = [ou, lu]
+        if do_s is not None:
+            out += list(oracle.attn_bwd(qu, ku, vu, do_s[ru][:, hs], iu, cu_padded, cu_actual, scale, docs=dd,
+                                        rows=rr, keys=keys))
+        return unit, ru, out
+
+    with threadpool_limits(limits=2):
+        with ThreadPoolExecutor(max_workers=min(len(units), os.cpu_count() or 1, 16)) as ex:
+            results = list(ex.map(run, units))
+    for (d, j), ru, out in results:
+        hs = slice(j * G, (j + 1) * G)
+        o[ru, hs], lse[ru, hs] = out[0], out[1]
+        if do_s is not None:
+            dq[ru, hs] = out[2]
+            slot = slice(None) if d is None else slice(int(cu_p[d]), int(cu_p[d + 1]))
+            dk[slot, j] = out[3][slot, 0]
+            dv[slot, j] = out[4][slot, 0]
+    return o, lse, dq, dk, dv

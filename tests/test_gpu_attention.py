@@ -12,7 +12,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import assert_attn_close, bf16_dev, i32_dev, log, set_case, status_dev, to_np64
+from tests.gpu_util import assert_attn_close, bf16_dev, i32_dev, log, oracle_sampled, set_case, status_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -123,8 +123,9 @@ class Share:
         assert bool(torch.isfinite(o_d).all()), "O must be finite everywhere"
         assert bool((o_d[~vq_d] == 0).all()) and bool(torch.isneginf(lse_d[~vq_d]).all()), "pad rows: O = 0, LSE = -inf"
         assert bool(torch.isfinite(lse_d[vq_d]).all())
-        o_s, lse_s, _ = oracle.attn_fwd(q_s, k_s, v_s, idx_s, wl.cu_padded, wl.cu_actual, wl.softmax_scale,
-                                        docs=docs, rows=sub_rows)
+        o_s, lse_s, dq_s, dk_s, dv_s = oracle_sampled(
+            q_s, k_s, v_s, self.do_np[lsel][:, hsel] if backward else None, idx_s, wl.cu_padded, wl.cu_actual,
+            wl.softmax_scale, G, docs=docs, rows=sub_rows, keys=keys)
         assert_attn_close("O", rows_of(self.o), o_s, vq[lsel][:, None, None])
         assert_attn_close("LSE", rows_of(self.lse), lse_s, vq[lsel][:, None])
         if not backward:
@@ -138,8 +139,6 @@ class Share:
         for name, x in (("dQ", dq_d), ("dK", dk_d), ("dV", dv_d)):
             assert bool(torch.isfinite(x).all()), f"{name} must be finite everywhere"
         assert bool((dq_d[~vq_d] == 0).all()) and bool((dk_d[~vt_d] == 0).all()) and bool((dv_d[~vt_d] == 0).all())
-        dq_s, dk_s, dv_s = oracle.attn_bwd(q_s, k_s, v_s, self.do_np[lsel][:, hsel], idx_s, wl.cu_padded,
-                                           wl.cu_actual, wl.softmax_scale, docs=docs, rows=sub_rows, keys=keys)
         krows = np.arange(T) if docs is None else np.nonzero(np.isin(doc, list(docs)))[0]
         krows_d = torch.from_numpy(at[krows]).to(dev)
 
@@ -197,6 +196,39 @@ def test_t8192_mha16_forward_both_strategies():
             sh.compare(backward=False)
 
 
+def _late_keys(wl, idx, doc_id, n=64):
+    """The n actual keys of a document ending at the rank's last actual row in it: few of the rank's rows see them,
+    so the oracle's dK/dV there costs little however long the document is."""
+    doc, pos, valid = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    mine = idx[(doc[idx] == doc_id) & valid[idx]]
+    if mine.size == 0:
+        return np.zeros(0, dtype=np.int64)
+    p_last = int(mine.max())
+    lo = max(int(wl.cu_padded[doc_id]), p_last - n + 1)
+    return np.arange(lo, p_last + 1)
+
+
+FULL_DOC_WORK = 4_000_000   # (rank rows in a document) x (document length) up to which a document is compared in full
+
+
+def compare_share(sh, kv_heads):
+    """The share's largest, smallest and first-row documents: in full where the oracle's work is small (the rank's
+    rows in the document times its length up to FULL_DOC_WORK), otherwise on sampled rows (first, middle and last
+    64 of the rank's rows there: O, LSE, dQ) and the 64 keys up to the rank's last row there (dK, dV)."""
+    wl = sh.wl
+    doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
+    L = np.diff(wl.cu_padded.astype(np.int64))
+    full, sampled = [], []
+    for d in _sample_docs(wl, sh.idx):
+        (full if np.count_nonzero(doc[sh.idx] == d) * L[d] <= FULL_DOC_WORK else sampled).append(d)
+    log(f"  docs {full} in full, {sampled} sampled")
+    if full:
+        sh.compare(docs=full, kv_heads=kv_heads)
+    for d in sampled:
+        rows, _ = _largest_doc_samples(wl, sh.idx, d)
+        sh.compare(docs=[d], kv_heads=kv_heads, rows=rows, keys=_late_keys(wl, sh.idx, d))
+
+
 def _sample_docs(wl, idx, n=3):
     """Largest document the rank touches, smallest, and the one holding the rank's first row."""
     doc, _, _ = oracle.token_map(wl.cu_padded, wl.cu_actual)
@@ -209,12 +241,10 @@ def _sample_docs(wl, idx, n=3):
 @pytest.mark.parametrize("s", [2])
 @pytest.mark.parametrize("r", [0, 3])
 def test_t32768_gqa32x8_sampled(s, r):
+    """The packed strategy at the Llama-3-8B shape (DualChunkSwap and contiguous run in the chained-step test)."""
     wl = W.t32768_gqa32x8()
     log(f"t32768_gqa32x8 s={s} r={r}")
-    sh = Share(wl, s, r)
-    docs = _sample_docs(wl, sh.idx)
-    log(f"  docs {docs}")
-    sh.compare(docs=docs, kv_heads=[0, 7])
+    compare_share(Share(wl, s, r), [0, 7])
 
 
 def _largest_doc_samples(wl, idx, doc_id, n=64):
@@ -238,8 +268,8 @@ def test_t131072_gqa64x8_bench_step(r):
     """The headline share as the benchmark runs it: GPU partition (bit-exact against the oracle), restoration (none
     under the contiguous strategy: the call returns with the gathered buffer in place), plan, forward, backward,
     on the workload's seeded inputs.  Against the oracle: the largest document the rank touches on sampled query
-    rows (O, LSE, dQ) and sampled keys (dK, dV), kv head 5; the smallest and the first-row documents in full on
-    kv heads 2 and 5."""
+    rows (O, LSE, dQ) and its first, middle and last keys (dK, dV), kv head 5; then the usual share sample (the
+    largest, smallest and first-row documents, in full where small) on kv heads 2 and 5."""
     wl = W.t131072_gqa64x8()
     T, cp, s = wl.T, wl.cp, 1
     st = status_dev()
@@ -261,19 +291,16 @@ def test_t131072_gqa64x8_bench_step(r):
     log(f"  largest document {big} ({int(L.max())} tokens): {rows.size} rows, {keys.size} keys")
     set_case(f"{wl.name} contiguous r{r} largest document (sampled rows and keys)")
     sh.compare(docs=[big], kv_heads=[5], rows=rows, keys=keys)
-    small = sorted({int(touched[np.argmin(L)]), int(doc[sh.idx[0]])} - {big})
-    if small:
-        log(f"  documents {small} in full")
-        set_case(f"{wl.name} contiguous r{r} smallest / first-row documents")
-        sh.compare(docs=small, kv_heads=[2, 5])
+    set_case(f"{wl.name} contiguous r{r}")
+    compare_share(sh, [2, 5])
 
 
 @pytest.mark.parametrize("m", range(W.DYNAMIC_T_MICROBATCHES))
 def test_dynamic_t_every_share(m):
     """Every share of dynamic-T micro-batch m: ranks 0-3 under DualChunkSwap and contiguous ownership (and the
     packed strategy on every fourth micro-batch), on buffers allocated for the 65,536-token capacity and
-    NaN-poisoned past the active T, with canaries on the output tails.  Each share's largest, smallest and
-    first-row documents are compared with the oracle on kv heads 1 and 6."""
+    NaN-poisoned past the active T, with canaries on the output tails.  Each share's smallest and first-row
+    documents are compared with the oracle in full and its largest on sampled rows and keys, kv heads 1 and 6."""
     wl = W.dynamic_t(m)
     kv, qdo = (wl.k(), wl.v()), (wl.q(), wl.do())
     dev_in = dict(k=bf16_dev(kv[0]), v=bf16_dev(kv[1]), q=bf16_dev(qdo[0]), do=bf16_dev(qdo[1]))
@@ -282,9 +309,7 @@ def test_dynamic_t_every_share(m):
             log(f"dynamic_t mb={m} T={wl.T} s={s} r={r}")
             sh = Share(wl, s, r, capacity=W.DYNAMIC_T_CAPACITY, poison=True, kv=kv, qdo=qdo, dev_in=dev_in)
             sh.check_tails()
-            docs = _sample_docs(wl, sh.idx)
-            log(f"  docs {docs}")
-            sh.compare(docs=docs, kv_heads=[1, 6])
+            compare_share(sh, [1, 6])
             del sh
 
 
@@ -323,7 +348,8 @@ def test_t32768_gqa32x8_chained_step(s, r):
     """The benchmark's step on the Llama-3-8B-shaped workload as one chain of library calls: GPU partition indices,
     the rank's Q and dO rows gathered by them (input partitioning), K/V restored from the rank-major gathered
     buffer, plan, forward, backward; the indices and restored K/V bit-exact and the attention outputs against the
-    oracle on each share's largest, smallest and first-row documents, kv heads 0 and 7."""
+    oracle on each share's smallest and first-row documents in full and its largest on sampled rows and keys, kv
+    heads 0 and 7."""
     wl = W.t32768_gqa32x8()
     T, cp = wl.T, wl.cp
     S = T // cp
@@ -352,7 +378,7 @@ def test_t32768_gqa32x8_chained_step(s, r):
     sh.q_np, sh.k_np, sh.v_np, sh.do_np = q_np[parts[r]], k_np, v_np, do_np[parts[r]]
     sh.o, sh.lse, sh.dq, sh.dk, sh.dv = o, lse, dq, dk, dv
     set_case(f"{wl.name} {STRAT[s]} r{r} chained step")
-    sh.compare(docs=_sample_docs(wl, parts[r]), kv_heads=[0, 7])
+    compare_share(sh, [0, 7])
 
 
 # ---------------------------------------------------------------------------

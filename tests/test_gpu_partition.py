@@ -108,9 +108,11 @@ def test_partition_device_status_bits():
 
 
 def _rand_rows(T, row_elems, seed):
-    rng = np.random.default_rng(seed)
-    bits = rng.integers(0, 1 << 16, size=(T, row_elems), dtype=np.uint16)   # any bit pattern, NaNs included
-    return torch.from_numpy(bits.view(np.int16)).to("cuda")
+    """Rows of arbitrary 16-bit patterns (NaNs included), drawn on the GPU by a seeded generator: the restoration
+    copies bits, so any pattern is a valid input and the expected output is the input itself."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randint(-(1 << 15), 1 << 15, (T, row_elems), dtype=torch.int16, device="cuda", generator=g)
 
 
 # every named workload (config 4 has no DualChunkSwap layout, but its contiguous copy is checked), every
@@ -124,13 +126,13 @@ def test_reorder_bit_exact(name, wl):
     log(f"reorder {name}")
     row_elems = 1024 if wl.T >= 4096 else 8 * (1 + wl.T % 3)
     cap = max(wl.T, wl.capacity) + 16
+    k_phys = _rand_rows(wl.T, row_elems, 1)
+    v_phys = _rand_rows(wl.T, row_elems, 2)
     for s in (0, 1, 2):
         try:
             oracle.check_layout(wl.cu_padded, wl.cu_actual, wl.cp, s)
         except ValueError:
             continue
-        k_phys = _rand_rows(wl.T, row_elems, 1)
-        v_phys = _rand_rows(wl.T, row_elems, 2)
         parts = [oracle.partition_indices(wl.cu_padded, wl.cp, r, s) for r in range(wl.cp)]
         order = torch.from_numpy(oracle.all_gather(np.arange(wl.T), parts)).to("cuda")
         kg = torch.full((cap, row_elems), 0x7FC0, dtype=torch.int16, device="cuda")

@@ -32,12 +32,17 @@ MUTANTS = [
     ("lse_no_max", "lse[r, h] = m + np.log(den)", "lse[r, h] = np.log(den)"),
     ("dk_no_scale", "dk[start + kk, g] += scale * (ds_k.T @ q_local[r, h])", "dk[start + kk, g] += (ds_k.T @ q_local[r, h])"),
     ("dq_wrong_operand", "dq[r[rq], h] = scale * (ds_r @ kd)", "dq[r[rq], h] = scale * (ds_r @ vd)"),
-    ("ds_sign_dq", "ds_r = p[rq] * (dout[rq] @ vd.T - delta[rq, None])", "ds_r = p[rq] * (delta[rq, None] - dout[rq] @ vd.T)"),
-    ("ds_sign_dk", "ds_k = p[:, kk] * (dout @ vd[kk].T - delta[:, None])", "ds_k = p[:, kk] * (delta[:, None] - dout @ vd[kk].T)"),
-    ("dv_wrong_operand", "dv[start + kk, g] += p[:, kk].T @ dout", "dv[start + kk, g] += ds_k.T @ dout"),
+    ("ds_sign", "ds = p * (dout @ vd.T - delta[:, None])", "ds = p * (delta[:, None] - dout @ vd.T)"),
+    ("ds_sign_sampled_rows", "ds_r = p[rq] * (dout[rq] @ vd.T - delta[rq, None])",
+     "ds_r = p[rq] * (delta[rq, None] - dout[rq] @ vd.T)"),
+    ("ds_sign_sampled_keys", "ds_k, p_k = p[:, kk] * (dout @ vd[kk].T - delta[:, None]), p[:, kk]",
+     "ds_k, p_k = p[:, kk] * (delta[:, None] - dout @ vd[kk].T), p[:, kk]"),
+    ("dv_wrong_operand", "dv[start + kk, g] += p_k.T @ dout", "dv[start + kk, g] += ds_k.T @ dout"),
     ("key_subset_drops_a_key", "kk = np.nonzero(ksel[start:start + a])[0]", "kk = np.nonzero(ksel[start:start + a])[0][1:]"),
     ("row_subset_drops_rows", "rq = rsel[r]", "rq = rsel[r] & (qpos[b0:b0 + _ROW_BLOCK] != 1)"),
     ("fwd_row_subset_drops_rows", "keep = rsel[drows]", "keep = rsel[drows] & (qpos != 1)"),
+    ("bwd_needed_rows_too_few", "need = rsel[drows] | (qpos >= (kk[0] if kk.size else a))",
+     "need = rsel[drows] | (qpos > (kk[0] if kk.size else a))"),
     ("delta_dropped", "delta = np.sum(dout * o, axis=1)", "delta = np.sum(dout * o, axis=1) * 0"),
     ("packed_per_half", "return partition_indices([0, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)",
      "return partition_indices([0, cu_p[-1] // 2, cu_p[-1]], cp_size, rank, DUAL_CHUNK_SWAP)"),
@@ -63,6 +68,7 @@ PINS = [
     TA.test_fwd_single_unpadded_document_matches_sdpa,
     lambda: [TA.test_union_of_ranks_equals_unpartitioned_and_autograd(w) for w in [TA.W.tiny_t28()]],
     TA.test_bwd_pads_and_first_token_exact,
+    TA.test_row_and_key_sampling_matches_full,
 ]
 
 
