@@ -30,6 +30,8 @@ SIGNATURES = {
 # K/V in rank-major all-gathered order: same arguments as the physical-order calls
 SIGNATURES["cpthd_attn_fwd_allgathered"] = SIGNATURES["cpthd_attn_fwd"]
 SIGNATURES["cpthd_attn_bwd_allgathered"] = SIGNATURES["cpthd_attn_bwd"]
+# allocation-free backward: cpthd_attn_bwd without the workspace pointer and size
+SIGNATURES["cpthd_attn_bwd_noalloc"] = (c_i32, SIGNATURES["cpthd_attn_bwd"][1][:24] + [c_vp, c_vp])
 # instrumentation variants (include/cpthd_timing.h): + kv_allgathered, events, n_events
 SIGNATURES["cpthd_attn_fwd_timed"] = (c_i32, SIGNATURES["cpthd_attn_fwd"][1] + [c_i32, c_vp, c_i32])
 SIGNATURES["cpthd_attn_bwd_timed"] = (c_i32, SIGNATURES["cpthd_attn_bwd"][1] + [c_i32, c_vp, c_i32])

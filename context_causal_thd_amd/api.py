@@ -174,6 +174,17 @@ def cpthd_attn_bwd_allgathered(q_local, k_gathered, v_gathered, o_local, do_loca
         causal, window_left, window_right, dq_local, dk_gathered, dv_gathered, workspace, dev_status, stream))
 
 
+def cpthd_attn_bwd_noalloc(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs,
+                           total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads,
+                           head_dim, softmax_scale, causal, window_left, window_right, dq_local, dk, dv,
+                           dev_status=None, stream=None):
+    """cpthd_attn_bwd with the library's static scratch array in place of a workspace (no device allocation)."""
+    return _lib.call("cpthd_attn_bwd_noalloc", _p(q_local), _p(k), _p(v), _p(o_local), _p(do_local), _p(lse_local),
+                     _p(cu_seqlens), _p(cu_seqlens_padded), num_docs, total_tokens, capacity_tokens, cp_size, rank,
+                     strategy, num_q_heads, num_kv_heads, head_dim, softmax_scale, causal, window_left,
+                     window_right, _p(dq_local), _p(dk), _p(dv), _p(dev_status), _s(stream))
+
+
 def cpthd_attn_bwd_timed(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs,
                          total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
                          softmax_scale, causal, window_left, window_right, dq_local, dk, dv, workspace, dev_status,

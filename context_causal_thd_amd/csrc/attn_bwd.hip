@@ -24,6 +24,8 @@
 // double-buffered LDS tiles while computing the current one.  K/V (and dK/dV)
 // rows are in physical order, or in rank-major all-gathered order for the
 // all-gathered entry point.
+#include <mutex>
+
 #include "attn_common.h"
 #include "cpthd_host.h"
 
@@ -613,4 +615,65 @@ extern "C" int cpthd_attn_bwd_allgathered(CPTHD_BWD_ARGS) {
 
 extern "C" int cpthd_attn_bwd_timed(CPTHD_BWD_ARGS, int32_t kv_allgathered, hipEvent_t* events, int32_t n_events) {
   return attn_bwd_entry(CPTHD_BWD_PASS, events, n_events, kv_allgathered != 0);
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free backward: the workspace is a fixed device array
+// ---------------------------------------------------------------------------
+// For callers that cannot allocate (code under HIP graph capture, serving
+// loops, harnesses that forbid hipMalloc).  The array lives in the library's
+// code object: every GPU the library runs on holds its own copy until the
+// process ends, and every call on that GPU shares it (the plan it leaves is
+// checked and rebuilt like any workspace's, and the -delta / LSE rows are
+// written before they are read, so nothing needs clearing).
+static __device__ __align__(256) char scratch[CPTHD_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];   // the array's device address on each device, taken once
+
+// The current device's copy of the array.  In host code `scratch` only names a
+// host-side stand-in, so its device address comes from hipGetSymbolAddress.
+int scratch_address(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CPTHD_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return CPTHD_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CPTHD_OK;
+}
+}  // namespace
+
+extern "C" int cpthd_attn_bwd_noalloc(const void* q_local, const void* k, const void* v, const void* o_local,
+                                      const void* do_local, const float* lse_local, const int32_t* cu_seqlens,
+                                      const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                                      int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy,
+                                      int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                      float softmax_scale, int32_t causal, int32_t window_left,
+                                      int32_t window_right, float* dq_local, float* dk, float* dv,
+                                      int32_t* dev_status, hipStream_t stream) {
+  if (!q_local || !k || !v || !o_local || !do_local || !lse_local || !dq_local || !dk || !dv || !cu_seqlens ||
+      !cu_seqlens_padded)
+    return CPTHD_ERR_NULL;
+  // the host checks of cpthd_attn_bwd against the array's size (a stand-in address: nothing is dereferenced),
+  // so a call the array cannot hold is refused before any device is touched
+  {
+    PlanLayout lay;
+    AttnParams prm;
+    if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
+                                num_kv_heads, head_dim, causal, window_left, window_right,
+                                reinterpret_cast<void*>(uintptr_t(256)), CPTHD_STATIC_SCRATCH_BYTES, lay, prm))
+      return e == CPTHD_ERR_WORKSPACE ? CPTHD_ERR_SCRATCH : e;
+  }
+  void* ws = nullptr;
+  if (int e = scratch_address(&ws)) return e;
+  return attn_bwd_entry(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs,
+                        total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads, head_dim,
+                        softmax_scale, causal, window_left, window_right, dq_local, dk, dv, ws,
+                        CPTHD_STATIC_SCRATCH_BYTES, dev_status, stream, nullptr, 0, false);
 }

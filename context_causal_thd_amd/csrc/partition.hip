@@ -307,6 +307,7 @@ extern "C" const char* cpthd_status_string(int status) {
   switch (status) {
     case CPTHD_OK: return "ok";
     case CPTHD_ERR_NULL: return "a required pointer is NULL";
+    case CPTHD_ERR_SCRATCH: return "the call needs more scratch than the library's static array holds";
     case CPTHD_ERR_RANK: return "cp_size < 1 or rank outside [0, cp_size)";
     case CPTHD_ERR_STRATEGY: return "unknown load-balancing strategy";
     case CPTHD_ERR_TOKENS: return "bad token count (T <= 0, T > capacity, T % cp_size != 0, or num_docs < 1)";

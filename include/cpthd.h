@@ -91,6 +91,7 @@ extern "C" {
 #define CPTHD_ERR_LAUNCH (-8)     /* a HIP launch failed */
 #define CPTHD_ERR_ALIGN (-9)      /* reorder rows not a multiple of 16 bytes or pointers not 16-byte aligned */
 #define CPTHD_ERR_ALIAS (-10)     /* an output buffer overlaps an input buffer */
+#define CPTHD_ERR_SCRATCH (-11)   /* cpthd_attn_bwd_noalloc: the call needs more than CPTHD_STATIC_SCRATCH_BYTES */
 
 /* Device-detected status bits, OR-ed into *dev_status. */
 #define CPTHD_DEV_CU_ORDER 1      /* cu_seqlens_padded not non-decreasing, or [0] != 0 */
@@ -280,6 +281,30 @@ int cpthd_attn_bwd_allgathered(const void* q_local, const void* k_gathered, cons
                                float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
                                float* dq_local, float* dk_gathered, float* dv_gathered, void* workspace,
                                size_t workspace_bytes, int32_t* dev_status, hipStream_t stream);
+
+/*
+ * cpthd_attn_bwd_noalloc -- cpthd_attn_bwd (physical-order K/V) without a
+ * workspace argument, for callers that cannot allocate device memory: code
+ * under HIP graph capture, serving loops, harnesses that forbid hipMalloc.
+ * Its scratch (the plan, -delta and LSE rows) is a device array of
+ * CPTHD_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call allocates and frees nothing.  The array is the
+ * current device's: call with the device of the buffers current.
+ * Every call on one GPU shares that GPU's array, so calls that overlap on one
+ * GPU (different streams, or host threads without ordering) race; order them
+ * on one stream.  A call whose plan and rows need more than the array holds
+ * (cpthd_attn_workspace_bytes(capacity_tokens, ..., num_docs) above the
+ * limit) returns CPTHD_ERR_SCRATCH before launching anything.
+ * Arguments, results and other errors as cpthd_attn_bwd.
+ */
+#define CPTHD_STATIC_SCRATCH_BYTES 16777216u /* 16 MiB */
+int cpthd_attn_bwd_noalloc(const void* q_local, const void* k, const void* v, const void* o_local,
+                           const void* do_local, const float* lse_local, const int32_t* cu_seqlens,
+                           const int32_t* cu_seqlens_padded, int32_t num_docs, int64_t total_tokens,
+                           int64_t capacity_tokens, int32_t cp_size, int32_t rank, int32_t strategy,
+                           int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, float softmax_scale,
+                           int32_t causal, int32_t window_left, int32_t window_right, float* dq_local, float* dk,
+                           float* dv, int32_t* dev_status, hipStream_t stream);
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* cpthd_status_string(int status);

@@ -219,3 +219,19 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "--gpus 1" in r.stderr
+
+
+def test_noalloc_backward_host_checks(lib):
+    """The allocation-free backward refuses NULL pointers and calls whose plan and rows exceed its static array,
+    on the host, before it touches a device."""
+    d = _defines()
+    P = 0x100000
+    f = lib.cpthd_attn_bwd_noalloc
+    assert f(P, P, P, P, P, P, None, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 1, -1, 0, P, P, P, None, None) \
+        == d["CPTHD_ERR_NULL"]
+    assert f(P, P, P, P, P, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 0, -1, 0, P, P, P, None, None) \
+        == d["CPTHD_ERR_MASK"]
+    T = 1 << 20   # -delta and LSE rows alone: 2 * 2^20 * 64 * 4 bytes, beyond the array
+    assert lib.cpthd_attn_workspace_bytes(T, 1, 64, 8, 128, 1) > d["CPTHD_STATIC_SCRATCH_BYTES"]
+    assert f(P, P, P, P, P, P, P, P, 1, T, T, 1, 0, 1, 64, 8, 128, 0.1, 1, -1, 0, P, P, P, None, None) \
+        == d["CPTHD_ERR_SCRATCH"]
