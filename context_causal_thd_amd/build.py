@@ -1,6 +1,11 @@
 """Build libcpthd.so (the C-ABI library) in-tree for gfx950 with hipcc.
 
     python -m context_causal_thd_amd.build        # or: from context_causal_thd_amd.build import build; build()
+
+Kernel variants kept for measurement are compile-time switches (CPTHD_* macros in csrc/); build one into another
+file without touching the in-tree library with
+
+    python -m context_causal_thd_amd.build --out <path.so> -DCPTHD_BWD_FUSED=1
 """
 from __future__ import annotations
 
@@ -33,23 +38,24 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
-    objs = [os.path.join(OBJDIR, s.replace(".hip", ".o")) for s in SOURCES]
+def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
+    objdir = OBJDIR if out == LIB else out + ".objs"
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s.replace(".hip", ".o")) for s in SOURCES]
 
     def compile_one(pair):
         src, obj = pair
-        return _run([HIPCC, *CFLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        return _run([HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj])
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        for out in ex.map(compile_one, zip(SOURCES, objs)):
-            if verbose and out:
-                print(out)
-    tmp = LIB + ".tmp"
+        for log in ex.map(compile_one, zip(SOURCES, objs)):
+            if verbose and log:
+                print(log)
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-mcode-object-version=5", "-shared", "-fPIC", *objs, "-o", tmp])
     _check_defined(tmp)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def _check_defined(path):
@@ -62,4 +68,10 @@ def _check_defined(path):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    args = sys.argv[1:]
+    out = LIB
+    if "--out" in args:
+        i = args.index("--out")
+        out = os.path.abspath(args[i + 1])
+        del args[i:i + 2]
+    print(build(verbose="-v" in args, out=out, defines=[a for a in args if a.startswith("-D")]))

@@ -24,6 +24,7 @@
 // double-buffered LDS tiles while computing the current one.  K/V (and dK/dV)
 // rows are in physical order, or in rank-major all-gathered order for the
 // all-gathered entry point.
+#include <algorithm>
 #include <mutex>
 
 #include "attn_common.h"
@@ -51,6 +52,13 @@ constexpr int kDqSplit = CPTHD_DQ_SPLIT;
 #endif
 #ifndef CPTHD_DKDV_PIPE
 #define CPTHD_DKDV_PIPE 2   // dK/dV score products: row reads kept this many ahead (0: no hint)
+#endif
+#ifndef CPTHD_BWD_FUSED
+#define CPTHD_BWD_FUSED 0   // head dim 64 / 128: one backward pass with dQ atomics instead of two passes
+#endif
+constexpr bool kBwdFused = CPTHD_BWD_FUSED;
+#ifndef CPTHD_FUSED_KD_REGS
+#define CPTHD_FUSED_KD_REGS 0   // one-pass backward: the dQ product's K operand held in registers (else read per step)
 #endif
 #ifndef CPTHD_DKDV_REVERSE
 #define CPTHD_DKDV_REVERSE 1   // dK/dV: visit a key tile's query chunks last first
@@ -525,11 +533,362 @@ __global__ __launch_bounds__(256 * SD, 1) CPTHD_WAVES_PER_EU(SD) void attn_bwd_d
   }
 }
 
+// ---------------------------------------------------------------------------
+// one-pass backward: the key-tile pass that also accumulates dQ
+// ---------------------------------------------------------------------------
+// The key-tile pass above holds dS for 128 keys and 64 query rows at every
+// step; dQ of those rows is dS K over the tile's keys.  This variant computes it
+// there, so the query-tile pass and its recompute of S and dP go away: a small
+// prologue writes -delta and LSE*log2(e) per row and zeroes dQ, and every key
+// tile adds its partial dQ with fp32 atomics (the order of the additions, and so
+// the last bits of dQ, depend on the schedule).
+//   - the tile's K rows sit in LDS: the S products read their K operand by rows
+//     from it, and each wave keeps the dQ product's K operand (its 32 dQ columns
+//     over the 128 keys, read once through the transpose read) in registers;
+//   - the waves write P and dS of their 32 query rows as [key][query] tiles in
+//     LDS: the partner wave of the key group reads its dK/dV operands from them by
+//     rows, and every wave reads the dQ product's dS operand through the
+//     transpose read;
+//   - wave w computes dQ for query block w/4 and columns 32*(w%4) .. +31 over all
+//     128 keys (8 products) and issues its 16 atomic adds per lane at the start of
+//     the next step, after that step's loads, so the end-of-step wait (which
+//     counts both) gives them a whole step to complete.
+// Needs SD = 2 (head dim 64 or 128): eight waves, two per key group, and a power-of-two G.
+// Measured, and not the default (CPTHD_BWD_FUSED=0): parity-green, but 2.3x (t32768_gqa32x8) to 4.7x
+// (t131072_gqa64x8) slower than the two passes.  Each key tile adds 128 x D floats per 64-row step, 10-33 GB
+// of atomic adds per step of those workloads, and the chip's L2 retires fp32 atomic adds at about 1 TB/s.
+template <int DP, bool AG>
+__global__ __launch_bounds__(512, 1) CPTHD_WAVES_PER_EU(2) void attn_bwd_fused_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    const uint16_t* __restrict__ dout, float* __restrict__ dq, float* __restrict__ dk, float* __restrict__ dv,
+    const char* __restrict__ ws, PlanLayout lay, AttnParams prm, int32_t* status) {
+  constexpr int NW = 8;
+  constexpr int NDB = DP / 64;       // 32-column blocks of dK/dV per wave (the pair splits the head dim)
+  using QT = LdsTile<DP, true>;      // Q, dO (64 rows) and the two halves of the tile's K (64 keys each)
+  using PT = LdsTile<64, true>;      // P and dS: [key][query], two 64-key halves each
+  __shared__ __align__(16) uint16_t Q0[QT::ELEMS], Q1[QT::ELEMS];
+  __shared__ __align__(16) uint16_t O0[QT::ELEMS], O1[QT::ELEMS];
+  __shared__ __align__(16) float L0[kQChunk], L1[kQChunk], E0[kQChunk], E1[kQChunk];   // LSE*log2(e), -delta
+  // keys 0-63 and 64-127 of K, P and dS.  Each pair is one array (halves indexed by the key group), so every LDS
+  // access has one underlying object and the compiler can tell it from the in-flight direct loads into Q / dO
+  __shared__ __align__(16) uint16_t K2[2 * QT::ELEMS];
+  __shared__ __align__(16) uint16_t P2[2 * PT::ELEMS], S2[2 * PT::ELEMS];
+  uint16_t* const KA = K2;
+  uint16_t* const KB = K2 + QT::ELEMS;
+  uint16_t* const SA = S2;
+  uint16_t* const SB = S2 + PT::ELEMS;
+
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
+  const int tile = blockIdx.x / prm.Hkv, kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
+  const KVTile kt = reinterpret_cast<const KVTile*>(ws + lay.kvtiles)[tile];
+  const bool kt_ok = (kt.doc >= 0) & (kt.doc < prm.num_docs) & (kt.k0 >= 0) & (kt.nkeys >= 0) &
+                     (kt.nkeys <= kKeysPerWG) & (kt.k0 <= prm.T - kt.nkeys);
+  if (!tile_usable(plan_matches(hdr, prm, lay), tile < hdr->n_kvtiles, kt_ok, status)) return;
+  const DocSeg ds = reinterpret_cast<const DocSeg*>(ws + lay.docs)[kt.doc];
+  const bool ds_ok = docseg_ok(ds, prm) &
+                     (!AG | (prm.strategy != kDCS) |
+                      ((kt.k0 >= ds.ds) & (kt.k0 - ds.ds <= 2 * prm.cp * ds.na - kt.nkeys)));
+  if (!tile_usable(true, true, ds_ok, status)) return;
+  const float* ndelta = reinterpret_cast<const float*>(ws + lay.delta);
+  const float* lse2w = reinterpret_cast<const float*>(ws + lay.lse2);
+
+  const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
+  const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv, S = prm.S;
+  const int kw = wave & 3, dh = wave >> 2;
+  const int key = kt.k0 + kw * 32 + l32;
+  const bool key_in = kw * 32 + l32 < kt.nkeys;
+  AgMap agm;
+  if constexpr (AG) agm = ag_map(ds, prm);
+  auto kv_row = [&](int p) __attribute__((always_inline)) -> int64_t {
+    if constexpr (AG) return (int64_t)agm.row(p) * Hkv + kvh;
+    return (int64_t)p * Hkv + kvh;
+  };
+  const int64_t krow = kv_row(key);
+
+  const int tpc = kQChunk / G;
+  int plo[2], phi[2], sl[2], sp[2], nch[2];
+#pragma unroll
+  for (int si = 0; si < 2; ++si) {
+    sp[si] = si == 0 ? ds.pa : ds.pb;
+    const int sn = si == 0 ? ds.na : ds.nb;
+    sl[si] = si == 0 ? ds.la : ds.lb;
+    plo[si] = max(sp[si], kt.k0);
+    phi[si] = min(sp[si] + sn, ds.ve);
+    nch[si] = (phi[si] > plo[si] && sl[si] >= 0 && sl[si] + (phi[si] - sp[si]) <= S)
+                  ? (phi[si] - plo[si] + tpc - 1) / tpc : 0;
+  }
+  const int nchunks = nch[0] + nch[1];
+  auto chunk_at = [&](int i, int& c0, int& l0, int& ntok) __attribute__((always_inline)) {
+    i = nchunks - 1 - i;   // last chunk first (concurrent key tiles of a document share their Q / dO reads)
+    const int si = i < nch[0] ? 0 : 1;
+    c0 = plo[si] + (i - (si ? nch[0] : 0)) * tpc;
+    l0 = sl[si] + (c0 - sp[si]);
+    ntok = min(tpc, phi[si] - c0);
+  };
+
+  const uint32_t tok_bytes = (uint32_t)Hq * D * 2;
+  TileLoader<DP, true, NW> qld;
+  auto qrowoff = [&](int r) __attribute__((always_inline)) -> int64_t {
+    const int t2 = r / G;
+    return r < tpc * G ? (int64_t)t2 * tok_bytes + (int64_t)(kvh * G + r - t2 * G) * D * 2 : -1;
+  };
+  qld.init(wave, lane, D, qrowoff);
+  const uint32_t ld_off = lane < tpc * G ? (uint32_t)((lane / G) * Hq + kvh * G + lane % G) * 4u : 0x80000000u;
+  auto issue = [&](int i, uint16_t* Qn, uint16_t* On, float* Ln, float* En) __attribute__((always_inline)) {
+    int c0, l0, ntok;
+    chunk_at(i, c0, l0, ntok);
+    issue_q_chunk<DP, NW>(qld, q, dout, lse2w, ndelta, (int64_t)l0 * Hq, ntok, tok_bytes, Hq, D, ld_off, wave, Qn,
+                          On, Ln, En);
+  };
+  if (nchunks > 0) issue(0, Q0, O0, L0, E0);
+
+  // the tile's K rows into LDS (plain loads and stores; once per work-group), V of the lane's key in registers
+  {
+    constexpr int CPR = DP / 8;   // 16-byte pieces per row
+#pragma unroll
+    for (int i = 0; i < (kKeysPerWG * CPR + 511) / 512; ++i) {
+      const int pc = tid + 512 * i;
+      const int kk = pc / CPR, ch = pc - kk * CPR;
+      if (kk < kKeysPerWG) {
+        u32x4 val = {0u, 0u, 0u, 0u};
+        if (kk < kt.nkeys && ch * 8 < D && nchunks > 0)
+          val = *reinterpret_cast<const u32x4*>(k + kv_row(kt.k0 + kk) * D + ch * 8);
+        uint16_t* Kt = kk < 64 ? KA : KB;
+        *reinterpret_cast<u32x4*>(Kt + QT::row(kk & 63) * QT::STRIDE + ch * 8) = val;
+      }
+    }
+  }
+  bf16x8 vf[DP / 16];
+#pragma unroll
+  for (int s = 0; s < DP / 16; ++s) {
+    u32x4 b = {0u, 0u, 0u, 0u};
+    const int d = 16 * s + 8 * h;
+    if (key_in && d < D && nchunks > 0) b = *reinterpret_cast<const u32x4*>(v + krow * D + d);
+    vf[s] = as_bf16x8(b);
+  }
+  f32x16 dka[NDB], dva[NDB];
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    dka[j] = f32x16{};
+    dva[j] = f32x16{};
+  }
+  lds_loads_barrier();
+
+  // dQ of this wave: query block qbq, columns 32*dbq .. +31; its K operand over the 128 keys in registers
+  const int qbq = wave >> 2, dbq = wave & 3;
+  const bool dq_cols = 32 * dbq < D;
+  const int dq_c0 = dq_cols ? 32 * dbq : 0;
+#if CPTHD_FUSED_KD_REGS
+  bf16x8 kd[8];
+#pragma unroll
+  for (int s = 0; s < 8; ++s)
+    kd[s] = lds_tr8<DP, true>(s < 4 ? KA : KB, 16 * (s & 3) + 4 * h, 16 * (s & 3) + 8 + 4 * h, dq_c0);
+#endif
+
+  const float sl2 = prm.scale_log2;
+  const int kmax = kt.k0 + kt.nkeys - 1;
+  const uint16_t* Kown = K2 + (kw >> 1) * QT::ELEMS;   // this wave's 32 keys: rows 32*(kw%2) .. of one half
+  uint16_t* Pown = P2 + (kw >> 1) * PT::ELEMS;
+  uint16_t* Sown = S2 + (kw >> 1) * PT::ELEMS;
+  const int krow_lds = 32 * (kw & 1) + l32;
+
+  // dQ atomics of one step: rows of query block qbq (row r of the step = token r / G, head r % G)
+  f32x16 dqa = f32x16{};
+  int pend_l0 = 0, pend_rows = 0;   // the pending step's first local row and its query rows (tokens * G)
+  // G is a power of two on this path: row r of a step is token r >> lg, head r & (G - 1)
+  const int lg = __builtin_ctz((unsigned)G), gm = G - 1;
+  auto flush_dq = [&]() __attribute__((always_inline)) {
+    if (!dq_cols) return;
+    // the lane's rows are recomputed at every flush: kept across the loop, their 16 offsets would cost registers
+    int hh = h;
+    asm volatile("" : "+v"(hh));
+    const int q0 = 32 * qbq + 4 * hh;
+    float* base = dq + ((int64_t)pend_l0 * Hq + kvh * G) * D + 32 * dbq + l32;
+    const float sc = prm.scale;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int qr = q0 + 8 * (r >> 2) + (r & 3);
+      if (qr < pend_rows) atomicAdd(base + ((qr >> lg) * Hq + (qr & gm)) * D, dqa[r] * sc);
+    }
+  };
+
+  auto step = [&](int i, const uint16_t* Qt, const uint16_t* Dt, const float* Lt, const float* Et, uint16_t* Qn,
+                  uint16_t* On, float* Ln, float* En) __attribute__((always_inline)) {
+    int c0, l0, ntok;
+    chunk_at(i, c0, l0, ntok);
+    if (i + 1 < nchunks) issue(i + 1, Qn, On, Ln, En);
+    if (i > 0) flush_dq();   // the previous step's dQ, behind this step's loads
+    __builtin_amdgcn_sched_barrier(0);   // (its registers free before the score products)
+    const bool need_mask = kmax > c0;
+    const int thr = (key - c0) * G - 4 * h;
+    // P and dS of this wave's query block dh (key as the lane index)
+    bf16x8 pd[4];
+    {
+      f32x16 sc = f32x16{}, dp;
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 e4 = *reinterpret_cast<const f32x4*>(Et + 32 * dh + 8 * g4 + 4 * h);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dp[4 * g4 + j] = e4[j];
+      }
+#pragma unroll
+      for (int s = 0; s < DP / 16; ++s) {
+        sc = mfma32(lds_row8<DP, true>(Qt, 32 * dh + l32, 16 * s, h), lds_row8<DP, true>(Kown, krow_lds, 16 * s, h),
+                    sc);
+        dp = mfma32(lds_row8<DP, true>(Dt, 32 * dh + l32, 16 * s, h), vf[s], dp);
+      }
+      auto probs = [&](auto masked) __attribute__((always_inline)) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(Lt + 32 * dh + 8 * g4 + 4 * h);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int r = 4 * g4 + j;
+            float pv = exp2_fast(fmaf(sc[r], sl2, -l4[j]));
+            if constexpr (decltype(masked)::value)
+              if (32 * dh + 8 * g4 + j < thr) pv = 0.f;
+            sc[r] = pv;
+            dp[r] = pv * dp[r];
+          }
+        }
+      };
+      if (need_mask)
+        probs(std::true_type{});
+      else
+        probs(std::false_type{});
+      pd[0] = acc_to_bf16(sc, 0);
+      pd[1] = acc_to_bf16(sc, 8);
+      pd[2] = acc_to_bf16(dp, 0);
+      pd[3] = acc_to_bf16(dp, 8);
+    }
+    // P and dS as [key][query] rows: query 32*dh + 8*g4 + 4h .. +3 is one 8-byte piece of the lane's key row
+    {
+      const int base = PT::row(krow_lds) * PT::STRIDE + 32 * dh + 4 * h;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 p4 = __builtin_bit_cast(u32x4, pd[j]);
+        const u32x4 s4 = __builtin_bit_cast(u32x4, pd[2 + j]);
+        *reinterpret_cast<u32x2*>(Pown + base + 16 * j) = u32x2{p4.x, p4.y};
+        *reinterpret_cast<u32x2*>(Pown + base + 16 * j + 8) = u32x2{p4.z, p4.w};
+        *reinterpret_cast<u32x2*>(Sown + base + 16 * j) = u32x2{s4.x, s4.y};
+        *reinterpret_cast<u32x2*>(Sown + base + 16 * j + 8) = u32x2{s4.z, s4.w};
+      }
+    }
+    // dV += P^T dO, dK += dS^T Q for one query block over this wave's column blocks
+    auto accumulate = [&](int qb, const bf16x8 (&p)[4]) __attribute__((always_inline)) {
+      const int r0 = 32 * qb + 4 * h;
+#pragma unroll
+      for (int j = 0; j < NDB; ++j) {
+        const int c0l = 32 * (dh * NDB + j);
+        dva[j] = mfma32(p[0], lds_tr8<DP, true>(Dt, r0, r0 + 8, c0l), dva[j]);
+        dva[j] = mfma32(p[1], lds_tr8<DP, true>(Dt, r0 + 16, r0 + 24, c0l), dva[j]);
+        dka[j] = mfma32(p[2], lds_tr8<DP, true>(Qt, r0, r0 + 8, c0l), dka[j]);
+        dka[j] = mfma32(p[3], lds_tr8<DP, true>(Qt, r0 + 16, r0 + 24, c0l), dka[j]);
+      }
+    };
+    accumulate(dh, pd);
+    lds_barrier();   // every wave's P and dS of the step are in LDS
+    {
+      // the partner's block: its P and dS rows of this lane's key
+      const int base = PT::row(krow_lds) * PT::STRIDE + 32 * (dh ^ 1) + 4 * h;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x2 a = *reinterpret_cast<const u32x2*>(Pown + base + 16 * j);
+        const u32x2 b = *reinterpret_cast<const u32x2*>(Pown + base + 16 * j + 8);
+        const u32x2 c = *reinterpret_cast<const u32x2*>(Sown + base + 16 * j);
+        const u32x2 e = *reinterpret_cast<const u32x2*>(Sown + base + 16 * j + 8);
+        pd[j] = as_bf16x8(u32x4{a.x, a.y, b.x, b.y});
+        pd[2 + j] = as_bf16x8(u32x4{c.x, c.y, e.x, e.y});
+      }
+      accumulate(dh ^ 1, pd);
+    }
+    // dQ[query][col] = sum over the 128 keys of dS[query][key] K[key][col] (scaled at the atomic add)
+    dqa = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+#if CPTHD_FUSED_KD_REGS
+      const bf16x8 kop = kd[s];
+#else
+      const bf16x8 kop = lds_tr8<DP, true>(s < 4 ? KA : KB, 16 * (s & 3) + 4 * h, 16 * (s & 3) + 8 + 4 * h, dq_c0);
+#endif
+      dqa = mfma32(lds_tr8<64, true>(s < 4 ? SA : SB, 16 * (s & 3) + 4 * h, 16 * (s & 3) + 8 + 4 * h, 32 * qbq),
+                   kop, dqa);
+    }
+    pend_l0 = l0;
+    pend_rows = ntok * G;
+    lds_loads_barrier();
+  };
+  for (int i = 0; i < nchunks; i += 2) {
+    step(i, Q0, O0, L0, E0, Q1, O1, L1, E1);
+    if (i + 1 < nchunks) step(i + 1, Q1, O1, L1, E1, Q0, O0, L0, E0);
+  }
+  if (nchunks > 0) flush_dq();
+
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    const int d = 32 * (dh * NDB + j) + l32;
+    if (d >= D) continue;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int kl = kw * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (kl < kt.nkeys) {
+        const int64_t row = kv_row(kt.k0 + kl);
+        dv[row * D + d] = dva[j][r];
+        dk[row * D + d] = dka[j][r] * prm.scale;
+      }
+    }
+  }
+}
+
+// Prologue of the one-pass backward: per local row and q head, -delta = -rowsum(dO * O) and LSE * log2(e) into the
+// workspace, and that row of dQ set to zero (the key tiles add into it).  Sixteen lanes per row: 4 rows per wave.
+__global__ __launch_bounds__(256) void attn_bwd_prep_kernel(const uint16_t* __restrict__ o,
+                                                            const uint16_t* __restrict__ dout,
+                                                            const float* __restrict__ lse, float* __restrict__ dq,
+                                                            char* __restrict__ ws, PlanLayout lay, int64_t rows,
+                                                            int D) {
+  float* ndelta = reinterpret_cast<float*>(ws + lay.delta);
+  float* lse2w = reinterpret_cast<float*>(ws + lay.lse2);
+  const int sub = threadIdx.x & 15;
+  const int64_t stride = (int64_t)gridDim.x * (blockDim.x / 16);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 16) + (threadIdx.x >> 4); r < rows; r += stride) {
+    float acc = 0.f;
+    for (int c = 8 * sub; c < D; c += 128) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(dout + r * D + c);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(o + r * D + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        acc += __uint_as_float(a[i] << 16) * __uint_as_float(b[i] << 16) +
+               __uint_as_float(a[i] & 0xFFFF0000u) * __uint_as_float(b[i] & 0xFFFF0000u);
+      *reinterpret_cast<f32x4*>(dq + r * D + c) = f32x4{};
+      *reinterpret_cast<f32x4*>(dq + r * D + c + 4) = f32x4{};
+    }
+#pragma unroll
+    for (int m = 8; m > 0; m >>= 1) acc += __shfl_xor(acc, m, 16);
+    if (sub == 0) {
+      ndelta[r] = -acc;
+      lse2w[r] = lse[r] * 1.4426950408889634f;
+    }
+  }
+}
+
 template <int DP, bool AG>
 static int launch_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                       const float* lse, float* dq, float* dk, float* dv, char* ws, const PlanLayout& lay,
                       const AttnParams& prm, int32_t* status, unsigned grid_q, unsigned grid_kv,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
+  if (kBwdFused && DP >= 64 && (prm.G & (prm.G - 1)) == 0) {
+    // one pass: prologue (-delta, LSE*log2(e), dQ = 0), then the key tiles with dQ atomics
+    const int64_t rows = (int64_t)prm.S * prm.Hq;
+    const unsigned gp = (unsigned)std::min<int64_t>((rows + 15) / 16, 4096);
+    int e = launch(attn_bwd_prep_kernel, dim3(gp), dim3(256), 0, stream, ev, nev, 1, (const uint16_t*)o,
+                   (const uint16_t*)dout, lse, dq, ws, lay, rows, prm.D);
+    if (e) return e;
+    return launch(attn_bwd_fused_kernel<(DP >= 64 ? DP : 64), AG>, dim3(grid_kv), dim3(512), 0, stream, ev, nev, 2,
+                  (const uint16_t*)q,
+                  (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)dout, dq, dk, dv, (const char*)ws, lay,
+                  prm, status);
+  }
   constexpr int QB = kDqRowBlocks;
   int e = launch(attn_bwd_dq_kernel<DP, QB, AG>, dim3(grid_q * kDqSplit), dim3(64 * (kQWaves / QB / kDqSplit)), 0,
                  stream, ev, nev, 1, (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (const uint16_t*)o,

@@ -128,6 +128,12 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int 
 // then lives in scalar registers instead of being kept per lane.
 __device__ inline int wave_index() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Work-group barrier over LDS only: waits for this wave's LDS accesses, not for its outstanding global loads, so
+// direct-to-LDS prefetches into other buffers stay in flight across it.  (__syncthreads() also waits for every
+// global memory operation of the wave.)  One asm statement with a memory clobber, so the compiler moves no
+// memory access across it.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ inline float log2_fast(float x) { return __builtin_amdgcn_logf(x); }
 
