@@ -50,7 +50,8 @@ import workloads as W  # noqa: E402
 PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 STRAT_NAME = {0: "dcs", 1: "contiguous", 2: "packed"}
-KERNELS = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv"]
+KERNELS = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_merge",
+           "attn_bwd_merge"]
 
 KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
 # the physical-order kernels a step launches at head_dim 128 (rocprofv3 kernel names)
@@ -291,7 +292,7 @@ class ShareSet:
     def make_events(self):
         t = self.torch
         return [([[t.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)],
-                 [self.cpthd.HipEvents(4), self.cpthd.HipEvents(6)]) for _ in self.shares]
+                 [self.cpthd.HipEvents(6), self.cpthd.HipEvents(8)]) for _ in self.shares]
 
     def step(self, evs=None, allgathered=False):
         """partition -> restoration -> plan -> forward -> backward for every share; `evs` from make_events()
@@ -333,6 +334,9 @@ class ShareSet:
                 acc[i, 3] += he[0].elapsed_ms(2, 3)
                 acc[i, 4] += he[1].elapsed_ms(2, 3)
                 acc[i, 5] += he[1].elapsed_ms(4, 5)
+                # the merge kernels of split tiles (launched when the workspace has partial slots)
+                acc[i, 6] += he[0].elapsed_ms(4, 5)
+                acc[i, 7] += he[1].elapsed_ms(6, 7)
         return acc / max(len(events), 1)
 
     def timed(self, steps, warmup, allgathered=False, clock=False):
@@ -366,8 +370,8 @@ class ShareSet:
         for i, sh in enumerate(self.shares):
             per_share.append({
                 "strategy": STRAT_NAME[sh["s"]], "rank": sh["r"], "causal_pairs_per_head": int(sh["pairs"]),
-                "fwd_tflops": float(self.flops_fwd[i] / (pk[i, 3] * 1e-3) / 1e12),
-                "bwd_tflops": float(self.flops_bwd[i] / ((pk[i, 4] + pk[i, 5]) * 1e-3) / 1e12),
+                "fwd_tflops": float(self.flops_fwd[i] / ((pk[i, 3] + pk[i, 6]) * 1e-3) / 1e12),
+                "bwd_tflops": float(self.flops_bwd[i] / ((pk[i, 4] + pk[i, 5] + pk[i, 7]) * 1e-3) / 1e12),
                 "fwd_bwd_tflops": float((self.flops_fwd[i] + self.flops_bwd[i]) / (pk[i, 3:].sum() * 1e-3) / 1e12),
                 "ms": {n: float(pk[i, j]) for j, n in enumerate(KERNELS)}})
         attn_ms = float(pk[:, 3:].sum())

@@ -18,6 +18,7 @@ SIGNATURES = {
     "cpthd_reorder_kv": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_vp, c_vp]),
     "cpthd_gather_rows": (c_i32, [c_vp, c_i64, c_i64, c_vp, c_i64, c_vp, c_vp, c_vp]),
     "cpthd_attn_workspace_bytes": (c_sz, [c_i64, c_i32, c_i32, c_i32, c_i32, c_i32]),
+    "cpthd_attn_workspace_min_bytes": (c_sz, [c_i64, c_i32, c_i32, c_i32, c_i32, c_i32]),
     "cpthd_attn_plan": (c_i32, [c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32, c_i32,
                                 c_vp, c_sz, c_vp, c_vp]),
     "cpthd_attn_fwd": (c_i32, [c_vp, c_vp, c_vp, c_vp, c_vp, c_i32, c_i64, c_i64, c_i32, c_i32, c_i32, c_i32, c_i32,

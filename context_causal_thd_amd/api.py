@@ -96,6 +96,11 @@ def cpthd_attn_workspace_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_hea
                                                       head_dim, max_docs))
 
 
+def cpthd_attn_workspace_min_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs):
+    return int(_lib.load().cpthd_attn_workspace_min_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads,
+                                                          head_dim, max_docs))
+
+
 def cpthd_attn_plan(cu_seqlens, cu_seqlens_padded, num_docs, total_tokens, capacity_tokens, cp_size, rank,
                     strategy, num_q_heads, num_kv_heads, head_dim, workspace, dev_status=None, stream=None):
     return _lib.call("cpthd_attn_plan", _p(cu_seqlens), _p(cu_seqlens_padded), num_docs, total_tokens,
@@ -174,6 +179,11 @@ def cpthd_attn_bwd_allgathered(q_local, k_gathered, v_gathered, o_local, do_loca
         causal, window_left, window_right, dq_local, dk_gathered, dv_gathered, workspace, dev_status, stream))
 
 
+# Bytes of the static scratch array cpthd_attn_bwd_noalloc uses as its workspace (CPTHD_STATIC_SCRATCH_BYTES).
+# An AttnPlan with workspace_bytes=STATIC_SCRATCH_BYTES gets the plan that entry point builds.
+STATIC_SCRATCH_BYTES = 16 << 20
+
+
 def cpthd_attn_bwd_noalloc(q_local, k, v, o_local, do_local, lse_local, cu_seqlens, cu_seqlens_padded, num_docs,
                            total_tokens, capacity_tokens, cp_size, rank, strategy, num_q_heads, num_kv_heads,
                            head_dim, softmax_scale, causal, window_left, window_right, dq_local, dk, dv,
@@ -217,6 +227,7 @@ class HipEvents:
         return ctypes.cast(self._arr, ctypes.c_void_p)
 
     def elapsed_ms(self, i: int, j: int) -> float:
+        """ms between events i and j (both must have been recorded)."""
         ms = ctypes.c_float()
         rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(self._arr[i]),
                                            ctypes.c_void_p(self._arr[j]))
@@ -312,9 +323,14 @@ class AttnPlan:
     layout of the current micro-batch (set by ``build``) and a device status word.
 
     The C entry points check the plan held in the workspace against the cu arrays of every call and rebuild it
-    when it was built from others, so a call always computes with its own layout."""
+    when it was built from others, so a call always computes with its own layout.
 
-    def __init__(self, capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, device="cuda"):
+    ``workspace_bytes`` (default: ``cpthd_attn_workspace_bytes``) sizes the workspace otherwise: a larger one
+    changes nothing, a smaller one (down to ``cpthd_attn_workspace_min_bytes``) holds fewer partial slots for split
+    tiles, so the plan splits fewer of them.  Two workspaces of the same size get the same plan, and the same results."""
+
+    def __init__(self, capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, device="cuda",
+                 workspace_bytes=None):
         self.capacity = capacity_tokens
         self.cp_size = cp_size
         self.Hq, self.Hkv, self.D = num_q_heads, num_kv_heads, head_dim
@@ -322,6 +338,8 @@ class AttnPlan:
         nbytes = cpthd_attn_workspace_bytes(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs)
         if nbytes == 0:
             raise ValueError("unsupported attention configuration")
+        if workspace_bytes is not None:
+            nbytes = int(workspace_bytes)
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
         self.status = torch.zeros(1, dtype=torch.int32, device=device)
         self.layout = None
@@ -357,7 +375,8 @@ def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, ls
              events=None, kv_allgathered=False, layout=None):
     """O and LSE of the rank's query rows for ``layout`` (default: the plan's current one).  ``kv_allgathered``:
     k and v are in rank-major all-gathered order (as an all-gather of the ranks' local K/V leaves them) instead
-    of physical order.  ``events`` (HipEvents of 4) times the call's two kernels."""
+    of physical order.  ``events`` (HipEvents of 6) times the call's kernels: plan check, attention, and the merge
+    of split tiles (when the workspace has partial slots)."""
     lay = layout or plan.layout
     args = plan._args(lay)
     T = lay.total_tokens
@@ -389,7 +408,8 @@ def attn_bwd(q_local, k, v, o_local, do_local, lse_local, plan: AttnPlan, softma
     """dQ of the rank's rows and its partial dK, dV (fp32) for ``layout`` (default: the plan's current one).
     With ``kv_allgathered`` k, v and the returned dk, dv are in rank-major all-gathered order.  Gradients this
     function allocates have the inputs' row counts; rows past the active S (dq) or T (dk, dv) are zero.
-    ``events`` (HipEvents of 6) times the call's three kernels."""
+    ``events`` (HipEvents of 8) times the call's kernels: plan check, query-tile pass, key-tile pass, and the merge
+    of split tiles (when the workspace has partial slots)."""
     lay = layout or plan.layout
     args = plan._args(lay)
     T = lay.total_tokens

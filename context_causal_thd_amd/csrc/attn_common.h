@@ -14,6 +14,8 @@ namespace cpthd {
 
 struct AttnParams {
   int T, S, cp, rank, strategy, Hq, Hkv, D, G, num_docs;
+  int num_cu;         // compute units of the device (the plan's split rule balances over them)
+  int qsplit;         // 1: query tiles may be split (their work-groups cannot fill the device)
   float scale;        // softmax scale
   float scale_log2;   // softmax scale * log2(e)
 };
@@ -27,8 +29,16 @@ __device__ inline bool plan_matches(const PlanHeader* hp, const AttnParams& p, c
   const PlanHeader h = *hp;
   return (h.valid == 1) & (h.magic == kPlanMagic) & (h.version == kPlanVersion) & (h.T == p.T) & (h.S == p.S) &
          (h.cp == p.cp) & (h.rank == p.rank) & (h.strategy == p.strategy) & (h.Hq == p.Hq) & (h.Hkv == p.Hkv) &
-         (h.D == p.D) & (h.num_docs == p.num_docs) & (h.max_qtiles == (int)lay.max_qtiles) &
-         (h.max_kvtiles == (int)lay.max_kvtiles) & (h.max_docs == (int)lay.max_docs);
+         (h.D == p.D) & (h.num_docs == p.num_docs) & (h.num_cu == p.num_cu) & (h.max_qtiles == (int)lay.max_qtiles) &
+         (h.max_kvtiles == (int)lay.max_kvtiles) & (h.max_docs == (int)lay.max_docs) &
+         (h.max_parts == (int)lay.max_parts);
+}
+
+// The part fields of a tile entry: a whole tile (slot -1, one part), or part
+// `part` of `nparts` >= 2 whose partial slots lie inside the workspace's.
+__device__ inline bool parts_ok(int slot, int part, int nparts, const PlanLayout& lay) {
+  return ((slot == -1) & (part == 0) & (nparts == 1)) |
+         ((slot >= 0) & (nparts >= 2) & (part >= 0) & (part < nparts) & (slot <= (int)lay.max_parts - nparts));
 }
 
 // A document's segments lie inside the rank's local rows and its slot inside
@@ -45,10 +55,10 @@ __device__ inline bool docseg_ok(const DocSeg& d, const AttnParams& p) {
 
 // Check a query tile descriptor against the tensors' extents (bitwise, so
 // its fields load together).
-__device__ inline bool check_qtile(const QTile& t, const AttnParams& p) {
+__device__ inline bool check_qtile(const QTile& t, const AttnParams& p, const PlanLayout& lay) {
   return (t.lrow0 >= 0) & (t.ntok >= 0) & (t.lrow0 <= p.S - t.ntok) & (t.ds >= 0) & (t.ds <= p.T) &
          (t.kv_end >= t.ds) & (t.kv_end <= p.T) & (t.p0 >= 0) & (t.p0 <= p.T - t.ntok) & (t.doc >= 0) &
-         (t.doc < p.num_docs);
+         (t.doc < p.num_docs) & (t.s0 >= 0) & (t.s1 >= t.s0) & parts_ok(t.slot, t.part, t.nparts, lay);
 }
 
 // The start of every attention work-group: is the plan the one built for these
@@ -354,7 +364,17 @@ __device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buff
 int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32_t strategy, int32_t num_docs,
                     int32_t Hq, int32_t Hkv, int32_t D, int32_t causal, int32_t wl, int32_t wr, const void* ws,
                     size_t ws_bytes, PlanLayout& lay, AttnParams& prm);
-int64_t qtile_grid(const AttnParams& prm);
+int64_t qtile_grid(const AttnParams& prm, const PlanLayout& lay);
+int64_t kvtile_grid(const AttnParams& prm, const PlanLayout& lay);
+// The compute units of the current device (cached per device), and whether
+// query tiles may be split: only when the whole query tiles of the call, times
+// the kv heads, are fewer work-groups than compute units.  Splitting then adds
+// parallelism; on a full device the merge's launch and partial traffic cost
+// more than the balance gains.
+int device_cus(AttnParams& prm);
+// Work-groups of a merge kernel over one list of split tiles (one per split
+// tile and kv head; a split tile has at least two parts).
+inline int64_t split_grid(const AttnParams& prm, const PlanLayout& lay) { return lay.max_parts / 2 * prm.Hkv; }
 // Launch the plan kernel: build the plan (ensure = false), or make sure the
 // workspace holds the plan of these arguments and cu arrays, rebuilding it
 // only when it does not (ensure = true).  Event slot `slot` times it.

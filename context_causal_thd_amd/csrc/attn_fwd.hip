@@ -23,6 +23,8 @@
 // all-gathered entry point, in rank-major order and read through the inverse
 // of the partition.  Key steps past the causal diagonal are never visited;
 // only steps that straddle it apply the per-element mask.
+#include <mutex>
+
 #include "attn_common.h"
 #include "cpthd_host.h"
 
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   // the tile is read beside the header (the workspace holds a tile slot for
   // every work-group the launch can have); it is used only once both check out
   const QTile t = reinterpret_cast<const QTile*>(ws + lay.qtiles)[tile];
-  if (!tile_usable(plan_matches(hdr, prm, lay), tile < hdr->n_qtiles, check_qtile(t, prm), status)) return;
+  if (!tile_usable(plan_matches(hdr, prm, lay), tile < hdr->n_qtiles, check_qtile(t, prm, lay), status)) return;
 
   const int tid = threadIdx.x, wave = wave_index(), lane = tid & 63, l32 = lane & 31, h = lane >> 5;
   const int G = prm.G, D = prm.D, Hq = prm.Hq, Hkv = prm.Hkv;
@@ -72,7 +74,8 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   // row offsets through the map.
   const uint32_t row_bytes = (uint32_t)Hkv * D * 2;
   const int kend = t.kv_end;
-  const int nsteps = (kend - t.ds + kKvStep - 1) / kKvStep;
+  // this entry's steps [s0, s1) of the tile's (a whole tile: all of them)
+  const int s0 = t.s0, s1 = min(t.s1, (kend - t.ds + kKvStep - 1) / kKvStep);
   const int64_t kv0 = AG ? 0 : (int64_t)t.ds * Hkv * D;
   const uint32_t kv_bytes = AG ? (uint32_t)prm.T * row_bytes : (uint32_t)(kend - t.ds) * row_bytes;
   const __amdgpu_buffer_rsrc_t krs = make_rsrc(k + kv0, kv_bytes);
@@ -82,7 +85,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   AgCursor cur{0, 0};
   if constexpr (AG) {
     agm = ag_map(reinterpret_cast<const DocSeg*>(ws + lay.docs)[t.doc], prm);
-    agm.chunk_of(t.ds, cur.j, cur.start);
+    agm.chunk_of(t.ds + s0 * kKvStep, cur.j, cur.start);
   }
   auto issue_kv = [&](int kb, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
     issue_kv_step<AG>(kvld, krs, vrs, agm, cur, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     auto rowoff = [&](int r) __attribute__((always_inline)) -> int64_t { return (int64_t)r * row_bytes + (int64_t)kvh * D * 2; };
     kvld.init(wave, lane, D, rowoff);
   }
-  if (nsteps > 0) issue_kv(t.ds, K0, V0);
+  if (s1 > s0) issue_kv(t.ds + s0 * kKvStep, K0, V0);
 
   // the lane's query row in each of the wave's 32-row blocks
   bool row_in[QB], valid[QB];
@@ -243,21 +246,44 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   };
   auto step = [&](int it, const uint16_t* Kt, const uint16_t* Vt, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
     const int kb = t.ds + it * kKvStep;
-    if (it + 1 < nsteps) issue_kv(kb + kKvStep, Kn, Vn);
+    if (it + 1 < s1) issue_kv(kb + kKvStep, Kn, Vn);
     bf16x8 pb[QB][4];
     s_products(Kt);
     softmax(kb, pb);
     pv_products(Vt, pb);
     lds_loads_barrier();
   };
-  for (int it = 0; it < nsteps_w; it += 2) {
-    step(it, K0, V0, K1, V1);
-    if (it + 1 < nsteps_w) step(it + 1, K1, V1, K0, V0);
+  // step s0 + j uses buffer j % 2
+  const int n_all = max(s1 - s0, 0), n_w = max(min(nsteps_w, s1) - s0, 0);
+  for (int j = 0; j < n_w; j += 2) {
+    step(s0 + j, K0, V0, K1, V1);
+    if (j + 1 < n_w) step(s0 + j + 1, K1, V1, K0, V0);
   }
-  // the rest of the tile's steps: the same loads and barriers, no products
-  for (int it = nsteps_w; it < nsteps; ++it) {
-    if (it + 1 < nsteps) issue_kv(t.ds + (it + 1) * kKvStep, (it & 1) ? K0 : K1, (it & 1) ? V0 : V1);
+  // the rest of the entry's steps: the same loads and barriers, no products
+  for (int j = n_w; j < n_all; ++j) {
+    if (j + 1 < n_all) issue_kv(t.ds + (s0 + j + 1) * kKvStep, (j & 1) ? K0 : K1, (j & 1) ? V0 : V1);
     lds_loads_barrier();
+  }
+
+  if (t.slot >= 0) {
+    // One part of a split tile: its unnormalised output and its softmax
+    // statistics (the running maximum, in log2 units, and the sum relative to
+    // it) go to its partial slot, in the lanes' own order; the merge kernel
+    // combines the parts.
+    float* slot = reinterpret_cast<float*>(const_cast<char*>(ws) + lay.qpart) +
+                  ((int64_t)(t.slot + t.part) * Hkv + kvh) * lay.qpart_stride;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) {
+      const int blk = wave * QB + qb;
+#pragma unroll
+      for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+        for (int gi = 0; gi < 4; ++gi)
+          reinterpret_cast<f32x4*>(slot)[((blk * (DP / 32) + db) * 4 + gi) * 64 + lane] =
+              f32x4{acc[qb][db][4 * gi], acc[qb][db][4 * gi + 1], acc[qb][db][4 * gi + 2], acc[qb][db][4 * gi + 3]};
+      reinterpret_cast<float2*>(slot + kRowsPerWG * DP)[blk * 64 + lane] = float2{m_i[qb], sum_xor32(l_i[qb])};
+    }
+    return;
   }
 
 #pragma unroll
@@ -282,13 +308,81 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
   }
 }
 
+// Merge of split query tiles: one wave per (split tile, kv head, 32-row
+// block), each lane reading the partial values the attention kernel's lane of
+// that block held.  With m_p the parts' running maxima and l_p their sums,
+// M = max m_p, w_p = 2^(m_p - M), O = sum w_p O_p / sum w_p l_p and
+// LSE = (M + log2 sum w_p l_p) ln 2, summed in part order.
+template <int DP>
+__global__ __launch_bounds__(64) void attn_fwd_merge_kernel(uint16_t* __restrict__ o, float* __restrict__ lse,
+                                                            const char* __restrict__ ws, PlanLayout lay,
+                                                            AttnParams prm, int32_t* status) {
+  constexpr int NBLK = kRowsPerWG / 32;
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
+  const int Hkv = prm.Hkv;
+  const int blk = blockIdx.x % NBLK, pair = blockIdx.x / NBLK;
+  const int si = pair / Hkv, kvh = pair - si * Hkv;
+  const SplitTile sp = reinterpret_cast<const SplitTile*>(ws + lay.qsplit)[si];
+  const bool ok = (sp.slot >= 0) & (sp.nparts >= 2) & (sp.slot <= (int)lay.max_parts - sp.nparts) & (sp.a >= 0) &
+                  (sp.b >= 0) & (sp.a <= prm.S - sp.b) & (sp.c >= 0) & (sp.c <= prm.T - sp.b);
+  if (!tile_usable(plan_matches(hdr, prm, lay), si < hdr->n_qsplit, ok, status)) return;
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  const int G = prm.G, D = prm.D, Hq = prm.Hq;
+  const int m = 32 * blk + l32, tt = m / G, g = m - tt * G;
+  const bool row_in = m < (kRowsPerWG / G) * G && tt < sp.b;
+  const bool valid = row_in && sp.c + tt < sp.d;
+  const float* part0 = reinterpret_cast<const float*>(ws + lay.qpart) + ((int64_t)sp.slot * Hkv + kvh) * lay.qpart_stride;
+  const int64_t pstride = (int64_t)Hkv * lay.qpart_stride;   // floats from one part's slot to the next
+  float mx = -INFINITY;
+  for (int p = 0; p < sp.nparts; ++p)
+    mx = fmaxf(mx, reinterpret_cast<const float2*>(part0 + p * pstride + kRowsPerWG * DP)[blk * 64 + lane].x);
+  float l_tot = 0.f;
+  f32x16 acc[DP / 32];
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db) acc[db] = f32x16{};
+  for (int p = 0; p < sp.nparts; ++p) {
+    const float* src = part0 + p * pstride;
+    const float2 st = reinterpret_cast<const float2*>(src + kRowsPerWG * DP)[blk * 64 + lane];
+    const float w = st.x == -INFINITY ? 0.f : exp2_fast(st.x - mx);
+    l_tot = fmaf(w, st.y, l_tot);
+#pragma unroll
+    for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+      for (int gi = 0; gi < 4; ++gi) {
+        const f32x4 x = reinterpret_cast<const f32x4*>(src)[((blk * (DP / 32) + db) * 4 + gi) * 64 + lane];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[db][4 * gi + e] = fmaf(w, x[e], acc[db][4 * gi + e]);
+      }
+  }
+  if (!row_in) return;
+  const int64_t qrow = (int64_t)(sp.a + tt) * Hq + kvh * G + g;
+  const float inv = (valid && l_tot > 0.f) ? 1.f / l_tot : 0.f;
+#pragma unroll
+  for (int db = 0; db < DP / 32; ++db)
+#pragma unroll
+    for (int gi = 0; gi < 4; ++gi) {
+      const int d0 = 32 * db + 8 * gi + 4 * h;
+      if (d0 < D) {
+        u32x2 w;
+        w.x = pack_bf16x2(acc[db][4 * gi + 0] * inv, acc[db][4 * gi + 1] * inv);
+        w.y = pack_bf16x2(acc[db][4 * gi + 2] * inv, acc[db][4 * gi + 3] * inv);
+        *reinterpret_cast<u32x2*>(o + qrow * D + d0) = w;
+      }
+    }
+  if (h == 0) lse[qrow] = (valid && l_tot > 0.f) ? (mx + log2_fast(l_tot)) * 0.69314718055994531f : -INFINITY;
+}
+
 template <int DP, bool AG>
 static int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const char* ws,
                       const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kFwdRowBlocks;
-  return launch(attn_fwd_kernel<DP, QB, AG>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 1,
-                (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+  int e = launch(attn_fwd_kernel<DP, QB, AG>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 1,
+                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+  if (e) return e;
+  if (lay.max_parts < 2 || !prm.qsplit) return skip_launch(ev, nev, 2, stream);   // no split query tile possible
+  return launch(attn_fwd_merge_kernel<DP>, dim3((unsigned)(split_grid(prm, lay) * (kRowsPerWG / 32))), dim3(64), 0,
+                stream, ev, nev, 2, (uint16_t*)o, lse, ws, lay, prm, status);
 }
 
 template <bool AG>
@@ -312,7 +406,7 @@ int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32
   if (int e = check_strategy_tokens(strategy, T, cp)) return e;
   if (int e = check_heads(Hq, Hkv, D)) return e;
   if (causal != 1 || wl != -1 || wr != 0) return CPTHD_ERR_MASK;
-  lay = plan_layout(capacity, cp, Hq, Hkv, num_docs);
+  lay = call_layout(capacity, cp, Hq, Hkv, D, num_docs, ws_bytes);
   if (!ws || ws_bytes < lay.total || reinterpret_cast<uintptr_t>(ws) % 256) return CPTHD_ERR_WORKSPACE;
   prm.T = (int)T;
   prm.S = (int)(T / cp);
@@ -324,15 +418,46 @@ int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32
   prm.D = D;
   prm.G = Hq / Hkv;
   prm.num_docs = num_docs;
+  prm.num_cu = 0;
+  prm.qsplit = 0;
   return CPTHD_OK;
 }
 
-// Work-groups for the query tiles: an upper bound from the active S (the plan
-// holds the exact count; surplus work-groups exit at once).
-int64_t qtile_grid(const AttnParams& prm) {
+// Work-groups for the query tiles: an upper bound from the active S, plus the
+// parts split tiles may add (the plan holds the exact count; surplus
+// work-groups exit at once).
+int64_t qtile_grid(const AttnParams& prm, const PlanLayout& lay) {
   const int64_t bm = tokens_per_qtile(prm.G);
   const int64_t seg = (prm.strategy == CPTHD_NO_LOAD_BALANCE ? 1 : 2) * (int64_t)prm.num_docs;
-  return ((prm.S + bm - 1) / bm + seg) * prm.Hkv;
+  return ((prm.S + bm - 1) / bm + seg + lay.max_parts) * prm.Hkv;
+}
+
+// The same for the key tiles: 128-key tiles of the active T, one more per document, plus the parts.
+int64_t kvtile_grid(const AttnParams& prm, const PlanLayout& lay) {
+  return (((int64_t)prm.T + kKeysPerWG - 1) / kKeysPerWG + prm.num_docs + lay.max_parts) * prm.Hkv;
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_cu_mutex;
+int g_cus[kMaxDevices];   // compute units per device, read once
+}  // namespace
+
+int device_cus(AttnParams& prm) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CPTHD_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_cu_mutex);
+  if (g_cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      return CPTHD_ERR_LAUNCH;
+    g_cus[dev] = n;
+  }
+  prm.num_cu = g_cus[dev];
+  const int64_t bm = tokens_per_qtile(prm.G);
+  const int64_t seg = (prm.strategy == CPTHD_NO_LOAD_BALANCE ? 1 : 2) * (int64_t)prm.num_docs;
+  prm.qsplit = ((prm.S + bm - 1) / bm + seg) * prm.Hkv < prm.num_cu ? 1 : 0;
+  return CPTHD_OK;
 }
 
 }  // namespace cpthd
@@ -360,8 +485,9 @@ static int attn_fwd_entry(const void* q_local, const void* k, const void* v, con
   }
   prm.scale = softmax_scale;
   prm.scale_log2 = softmax_scale * 1.4426950408889634f;
-  const int64_t grid = qtile_grid(prm);
+  const int64_t grid = qtile_grid(prm, lay);
   if (grid > INT32_MAX) return CPTHD_ERR_TOKENS;   // more work-groups than one launch takes
+  if (int e = device_cus(prm)) return e;
   char* ws = (char*)workspace;
   if (int e = launch_plan(cu_seqlens, cu_seqlens_padded, prm, ws, lay, true, dev_status, stream, events, n_events, 0))
     return e;

@@ -100,48 +100,206 @@ __device__ inline DocSeg doc_segments(const int32_t* cu_a, const int32_t* cu_p, 
   return d;
 }
 
-// Query chunks of kQChunk rows the rank iterates for keys from k0 on.
+// Query chunks (kQChunk / G tokens each, the key-tile kernel's steps) the
+// rank iterates for keys from k0 on.
 __device__ inline int kv_tile_cost(const DocSeg& d, int k0, int G) {
+  const int tpc = kQChunk / G;
   int cost = 0;
   int lo = max(d.pa, k0), hi = min(d.pa + d.na, d.ve);
-  if (hi > lo) cost += cdiv((hi - lo) * G, kQChunk);
+  if (hi > lo) cost += cdiv(hi - lo, tpc);
   lo = max(d.pb, k0);
   hi = min(d.pb + d.nb, d.ve);
-  if (hi > lo) cost += cdiv((hi - lo) * G, kQChunk);
+  if (hi > lo) cost += cdiv(hi - lo, tpc);
   return cost;
 }
 
-// Counting sort of n tiles by cost, longest first; s_hist holds the count of
-// tiles per cost bin (filled while the tiles were emitted).
+__device__ inline void set_range(QTile& e, int a, int b) {
+  e.s0 = a;
+  e.s1 = b;
+}
+__device__ inline void set_range(KVTile& e, int a, int b) {
+  e.c0 = a;
+  e.c1 = b;
+}
+
+// The merge-list entry of a split tile.
+__device__ inline SplitTile split_entry(const QTile& e, int slot, int np) {
+  return SplitTile{slot, np, e.lrow0, e.ntok, e.p0, e.ve, {0, 0}};
+}
+__device__ inline SplitTile split_entry(const KVTile& e, int slot, int np) {
+  return SplitTile{slot, np, e.k0, e.nkeys, e.doc, 0, {0, 0}};
+}
+
+// Parts a tile of this cost becomes: tiles above the threshold `thr` are cut
+// into parts of at most `P` steps; a tile that would stay one part is whole.
+__device__ inline int parts_of(int cost, int thr, int P) {
+  const int n = (P > 0 && cost > thr) ? (cost - 1) / P + 1 : 1;
+  return n >= 2 ? n : 1;
+}
+
+constexpr int kSplitTries = 16;     // part sizes P0 * 2^j tried by the split rule
+constexpr int kMinPartSteps = 16;   // no part has fewer steps (its partial results cost about as much as 16 steps' loads)
+constexpr int kMaxCandidates = 256;
+constexpr int kLdsCosts = 2048;     // tiles per list whose costs the plan also keeps in LDS
+
+// Shared state of the split rule of one tile list.
+struct SplitScratch {
+  unsigned long long sum;
+  int max_cost, n_cand, thr, P;
+  int parts[kSplitTries];
+  int cand[kMaxCandidates];       // tiles above the threshold (list index) ...
+  int cand_cost[kMaxCandidates];  // ... their costs
+  int cand_slot[kMaxCandidates];  // ... their first partial slots (-1: whole)
+  int cand_split[kMaxCandidates]; // ... and merge-list entries
+  int cost[kLdsCosts];            // costs of the list's first tiles (a candidate's: -1 - its index once split)
+};
+
+// The split rule of one tile list (n whole tiles, each run for Hkv heads, of
+// total cost W and largest cost max_cost; C compute units): a tile whose cost
+// exceeds the share W * Hkv / C of one unit is cut into parts of P steps, the
+// smallest of P0 * 2^j (P0 = max(ceil(share / 2), 16)) whose parts fit the
+// `max_parts` partial slots, and longest-first dispatch balances the rest.
+// At most C / Hkv tiles exceed the share (their costs add up to less than W);
+// they are listed in sc with the first partial slot and the merge-list entry
+// of each split one; the cost histogram trades a split tile for its parts.
+// Sets sc.thr and sc.P (P = 0: nothing split); returns the number of split
+// tiles.
 template <typename Tile>
-__device__ void sort_by_cost_desc(const Tile* tmp, Tile* out, int n, int* s_hist, int* s_wave) {
-  // position of bin b = number of tiles in bins above b
-  const int hi = kCostBins - 1 - 2 * threadIdx.x;
-  const int v0 = s_hist[hi], v1 = s_hist[hi - 1];
-  int total;
-  const int excl = block_exclusive_scan(v0 + v1, s_wave, total);
-  s_hist[hi] = excl;
-  s_hist[hi - 1] = excl + v0;
+__device__ int split_tiles(const Tile* tmp, int n, int Hkv, int num_cu, int max_parts, int* s_hist, int* s_wave,
+                           SplitScratch& sc) {
+  const int tid = threadIdx.x;
+  const unsigned long long share =
+      (sc.sum * (unsigned long long)Hkv + num_cu - 1) / (unsigned long long)max(num_cu, 1);
+  const int thr = (int)min(share, (unsigned long long)INT32_MAX), max_cost = sc.max_cost;
+  __syncthreads();   // (sc.sum and sc.max_cost read by every thread)
+  if (tid == 0) {
+    sc.thr = thr;
+    sc.P = 0;
+    sc.n_cand = 0;
+  }
+  if (max_cost <= thr || max_parts < 2) return 0;   // (uniform)
+  const int P0 = max(thr / 2 + (thr & 1), kMinPartSteps);
+  if (tid < kSplitTries) sc.parts[tid] = 0;
   __syncthreads();
-  for (int t = threadIdx.x; t < n; t += kPlanThreads) {
-    const Tile e = tmp[t];
-    const int pos = atomicAdd(&s_hist[min(e.cost, kCostBins - 1)], 1);
-    out[pos] = e;
+  for (int t = tid; t < n; t += kPlanThreads) {
+    const int c = t < kLdsCosts ? sc.cost[t] : tmp[t].cost;
+    if (c <= thr) continue;
+    const int k = atomicAdd(&sc.n_cand, 1);
+    if (k < kMaxCandidates) {
+      sc.cand[k] = t;
+      sc.cand_cost[k] = c;
+    }
+    // parts at P0 * 2^j: ceil(c / (P0 2^j)) = ceil(ceil(c / P0) / 2^j)
+    const int q0 = (c - 1) / P0 + 1;
+#pragma unroll
+    for (int j = 0; j < kSplitTries; ++j) {
+      const int np = (q0 - 1) / (1 << j) + 1;
+      if (np >= 2) atomicAdd(&sc.parts[j], min(np, max_parts + 1));
+    }
   }
   __syncthreads();
+  const int n_cand = sc.n_cand;
+  int P = 0;
+  if (n_cand <= kMaxCandidates) {   // (else more compute units than the list tracks: nothing split)
+    for (int j = 0; j < kSplitTries && ((int64_t)P0 << j) < max_cost; ++j) {
+      if (sc.parts[j] <= max_parts) {
+        P = P0 << j;   // (< max_cost, so in range)
+        break;
+      }
+    }
+  }
+  if (P == 0) {
+    __syncthreads();
+    if (tid == 0) sc.n_cand = 0;
+    __syncthreads();
+    return 0;
+  }
+  // the candidates' slots and merge-list entries from one scan of (np | 1 << 16)
+  int np = 1, c = 0;
+  if (tid < n_cand) {
+    c = sc.cand_cost[tid];
+    np = parts_of(c, thr, P);
+  }
+  int total;
+  const int ex = block_exclusive_scan(np >= 2 ? (np | (1 << 16)) : 0, s_wave, total);
+  if (tid < n_cand) {
+    sc.cand_slot[tid] = np >= 2 ? (ex & 0xFFFF) : -1;
+    sc.cand_split[tid] = ex >> 16;
+    if (sc.cand[tid] < kLdsCosts) sc.cost[sc.cand[tid]] = -1 - tid;
+    if (np >= 2) {
+      const int base = c / np, rem = c - base * np;
+      atomicSub(&s_hist[min(c, kCostBins - 1)], 1);
+      if (rem) atomicAdd(&s_hist[min(base + 1, kCostBins - 1)], rem);
+      atomicAdd(&s_hist[min(base, kCostBins - 1)], np - rem);
+    }
+  }
+  if (tid == 0) sc.P = P;
+  __syncthreads();
+  return total >> 16;
+}
+
+// Bin offsets of a counting sort by cost, longest first: bin b starts after
+// the entries of the bins above it.  Returns the entry count.
+__device__ inline int bin_offsets(int* s_hist, int* s_wave) {
+  const int hi = kCostBins - 1 - 2 * threadIdx.x;
+  const int v0 = s_hist[hi], v1 = s_hist[hi - 1];
+  int entries;
+  const int excl = block_exclusive_scan(v0 + v1, s_wave, entries);
+  s_hist[hi] = excl;
+  s_hist[hi - 1] = excl + v0;
+  return entries;
+}
+
+// Place tile t of a list: the whole tile, or its parts (and its merge-list
+// entry) when it is split.
+template <typename Tile>
+__device__ inline void place_tile(Tile e, int t, Tile* out, SplitTile* splits, int* s_hist, const SplitScratch& sc) {
+  const int c = e.cost;
+  int slot = -1, si = 0;
+  if (sc.P > 0 && c > sc.thr) {
+    int k = -1;
+    if (t < kLdsCosts) {
+      const int v = sc.cost[t];
+      k = v < 0 ? -1 - v : -1;
+    } else {
+      for (int j = 0; j < sc.n_cand; ++j)
+        if (sc.cand[j] == t) k = j;
+    }
+    if (k >= 0) {
+      slot = sc.cand_slot[k];
+      si = sc.cand_split[k];
+    }
+  }
+  if (slot >= 0) {
+    const int np = parts_of(c, sc.thr, sc.P), base = c / np, rem = c - base * np;
+    splits[si] = split_entry(e, slot, np);
+    e.slot = slot;
+    e.nparts = np;
+    for (int p = 0; p < np; ++p) {
+      const int a = p * base + min(p, rem), len = base + (p < rem ? 1 : 0);
+      set_range(e, a, a + len);
+      e.cost = len;
+      e.part = p;
+      out[atomicAdd(&s_hist[min(len, kCostBins - 1)], 1)] = e;
+    }
+  } else {
+    set_range(e, 0, c);
+    out[atomicAdd(&s_hist[min(c, kCostBins - 1)], 1)] = e;
+  }
 }
 
 // The header and stored cu arrays of a plan built from exactly these arguments?
 __device__ inline bool plan_current(const char* ws, const PlanLayout& lay, const int32_t* cu_a, const int32_t* cu_p,
-                                    int B, int T, int cp, int rank, int strategy, int Hq, int Hkv, int D,
+                                    int B, int T, int cp, int rank, int strategy, int Hq, int Hkv, int D, int num_cu,
                                     int* s_flag) {
   const int tid = threadIdx.x;
   if (tid == 0) {
     const PlanHeader h = *reinterpret_cast<const PlanHeader*>(ws);
     *s_flag = (h.valid == 1) & (h.magic == kPlanMagic) & (h.version == kPlanVersion) & (h.T == T) &
               (h.S == T / cp) & (h.cp == cp) & (h.rank == rank) & (h.strategy == strategy) & (h.Hq == Hq) &
-              (h.Hkv == Hkv) & (h.D == D) & (h.num_docs == B) & (h.max_qtiles == (int)lay.max_qtiles) &
-              (h.max_kvtiles == (int)lay.max_kvtiles) & (h.max_docs == (int)lay.max_docs);
+              (h.Hkv == Hkv) & (h.D == D) & (h.num_docs == B) & (h.num_cu == num_cu) &
+              (h.max_qtiles == (int)lay.max_qtiles) & (h.max_kvtiles == (int)lay.max_kvtiles) &
+              (h.max_docs == (int)lay.max_docs) & (h.max_parts == (int)lay.max_parts);
   }
   __syncthreads();
   if (!*s_flag) return false;   // uniform: every thread read the same flag
@@ -154,13 +312,14 @@ __device__ inline bool plan_current(const char* ws, const PlanLayout& lay, const
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __restrict__ cu_a,
                                                             const int32_t* __restrict__ cu_p, int B, int T, int cp,
                                                             int rank, int strategy, int Hq, int Hkv, int D,
-                                                            char* __restrict__ ws, PlanLayout lay, int32_t* status,
-                                                            int ensure) {
+                                                            int num_cu, int qsplit, char* __restrict__ ws,
+                                                            PlanLayout lay, int32_t* status, int ensure) {
   __shared__ int s_bits;
   __shared__ int s_flag;
   __shared__ int s_wave[40];
   __shared__ int s_qoff[kPlanThreads], s_kvoff[kPlanThreads];
-  __shared__ int s_hist_q[kCostBins], s_hist_kv[kCostBins];   // tiles per cost bin, counted at emission
+  __shared__ int s_hist_q[kCostBins], s_hist_kv[kCostBins];   // entries per cost bin
+  __shared__ SplitScratch s_split[2];                           // query and key lists
   __shared__ DocSeg s_docs[kPlanThreads];                       // this chunk's documents
   __shared__ int s_len[kPlanThreads];                           // and their padded lengths
 
@@ -174,7 +333,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
   const int tid = threadIdx.x;
   const int S = T / cp, G = Hq / Hkv, bm = tokens_per_qtile(G);
   // ensure mode: nothing to do when the workspace holds this call's plan
-  if (ensure && plan_current(ws, lay, cu_a, cu_p, B, T, cp, rank, strategy, Hq, Hkv, D, &s_flag)) return;
+  if (ensure && plan_current(ws, lay, cu_a, cu_p, B, T, cp, rank, strategy, Hq, Hkv, D, num_cu, &s_flag)) return;
   if (tid == 0) {
     s_bits = 0;
     hdr->valid = 0;
@@ -202,13 +361,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       if (status) atomicOr(status, s_bits);
       hdr->n_qtiles = 0;
       hdr->n_kvtiles = 0;
+      hdr->n_qsplit = 0;
+      hdr->n_kvsplit = 0;
     }
     return;
   }
 
-  // 2. documents in chunks of 1024: segments, tile counts, scan, emission
+  // 2. documents in chunks of 1024: segments, tile counts, scan, emission of
+  //    the whole tiles, their cost histograms, totals and maxima
   for (int b = tid; b < kCostBins; b += kPlanThreads) s_hist_q[b] = s_hist_kv[b] = 0;   // (the scans' barriers
                                                                                           //  order this first)
+  if (tid < 2) {
+    s_split[tid].sum = 0ull;
+    s_split[tid].max_cost = 0;
+  }
+  unsigned long long sum_q = 0, sum_kv = 0;
+  int max_q = 0, max_kv = 0;
   int carry_q = 0, carry_kv = 0;
   for (int base = 0; base < B; base += kPlanThreads) {
     const int i = base + tid;
@@ -254,8 +422,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       e.kv_end = e.p0 < d.ve ? min(e.p0 + e.ntok, d.ve) : d.ds;
       e.cost = cdiv(e.kv_end - d.ds, kKvStep);
       e.doc = base + lo;
+      e.slot = -1;
+      e.part = 0;
+      e.nparts = 1;
       qtmp[carry_q + t] = e;
+      if (carry_q + t < kLdsCosts) s_split[0].cost[carry_q + t] = e.cost;
       atomicAdd(&s_hist_q[min(e.cost, kCostBins - 1)], 1);
+      sum_q += (unsigned long long)e.cost;
+      max_q = max(max_q, e.cost);
     }
     for (int t = tid; t < tkv; t += kPlanThreads) {
       int lo = 0, hi = cnt - 1;
@@ -271,8 +445,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       e.nkeys = min(kKeysPerWG, L - k * kKeysPerWG);
       e.doc = base + lo;
       e.cost = kv_tile_cost(d, e.k0, G);
+      e.slot = -1;
+      e.part = 0;
+      e.nparts = 1;
       kvtmp[carry_kv + t] = e;
+      if (carry_kv + t < kLdsCosts) s_split[1].cost[carry_kv + t] = e.cost;
       atomicAdd(&s_hist_kv[min(e.cost, kCostBins - 1)], 1);
+      sum_kv += (unsigned long long)e.cost;
+      max_kv = max(max_kv, e.cost);
     }
     carry_q += tq;
     carry_kv += tkv;
@@ -280,11 +460,37 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     __syncthreads();
   }
 
-  // 3. longest first
+  // 3. split the tiles that exceed a compute unit's share; longest first
+  // (one shared atomic per wave: 1024 on one address would serialise)
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    sum_q += __shfl_xor(sum_q, o, 64);
+    sum_kv += __shfl_xor(sum_kv, o, 64);
+    max_q = max(max_q, __shfl_xor(max_q, o, 64));
+    max_kv = max(max_kv, __shfl_xor(max_kv, o, 64));
+  }
+  if ((tid & 63) == 0) {
+    atomicAdd(&s_split[0].sum, sum_q);
+    atomicMax(&s_split[0].max_cost, max_q);
+    atomicAdd(&s_split[1].sum, sum_kv);
+    atomicMax(&s_split[1].max_cost, max_kv);
+  }
   __threadfence_block();
   __syncthreads();
-  sort_by_cost_desc(qtmp, qt, carry_q, s_hist_q, s_wave);
-  sort_by_cost_desc(kvtmp, kvt, carry_kv, s_hist_kv, s_wave);
+  const int n_qsplit = split_tiles(qtmp, carry_q, Hkv, num_cu, qsplit ? (int)lay.max_parts : 0, s_hist_q, s_wave,
+                                   s_split[0]);
+  const int n_kvsplit = split_tiles(kvtmp, carry_kv, Hkv, num_cu, (int)lay.max_parts, s_hist_kv, s_wave, s_split[1]);
+  const int n_q = bin_offsets(s_hist_q, s_wave);
+  const int n_kv = bin_offsets(s_hist_kv, s_wave);
+  __syncthreads();
+  for (int t = tid; t < max(carry_q, carry_kv); t += kPlanThreads) {
+    QTile eq;
+    KVTile ek;
+    if (t < carry_q) eq = qtmp[t];
+    if (t < carry_kv) ek = kvtmp[t];
+    if (t < carry_q) place_tile(eq, t, qt, reinterpret_cast<SplitTile*>(ws + lay.qsplit), s_hist_q, s_split[0]);
+    if (t < carry_kv) place_tile(ek, t, kvt, reinterpret_cast<SplitTile*>(ws + lay.kvsplit), s_hist_kv, s_split[1]);
+  }
 
   // 4. the cu arrays the plan was built from, then the header
   int32_t* cpy = reinterpret_cast<int32_t*>(ws + lay.cu_copy);
@@ -292,8 +498,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     cpy[i] = cu_p[i];
     cpy[B + 1 + i] = cu_a[i];
   }
-  __threadfence();
-  __syncthreads();
+  // (no device-scope fences: the plan's readers are later kernels on the stream)
   if (tid == 0) {
     hdr->magic = kPlanMagic;
     hdr->version = kPlanVersion;
@@ -308,12 +513,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     hdr->G = G;
     hdr->num_docs = B;
     hdr->bm_tok = bm;
-    hdr->n_qtiles = carry_q;
-    hdr->n_kvtiles = carry_kv;
+    hdr->n_qtiles = n_q;
+    hdr->n_kvtiles = n_kv;
     hdr->max_qtiles = (int)lay.max_qtiles;
     hdr->max_kvtiles = (int)lay.max_kvtiles;
     hdr->max_docs = (int)lay.max_docs;
-    __threadfence();
+    hdr->max_parts = (int)lay.max_parts;
+    hdr->num_cu = num_cu;
+    hdr->q_part_steps = n_qsplit ? s_split[0].P : 0;
+    hdr->kv_part_chunks = n_kvsplit ? s_split[1].P : 0;
+    hdr->n_qsplit = n_qsplit;
+    hdr->n_kvsplit = n_kvsplit;
     hdr->valid = 1;
   }
 }
@@ -327,7 +537,17 @@ extern "C" size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp
   if (cp_size < 1 || max_docs < 1) return 0;
   if (check_tokens(capacity_tokens, capacity_tokens, cp_size, max_docs)) return 0;
   if (check_heads(num_q_heads, num_kv_heads, head_dim)) return 0;
-  return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, max_docs).total;
+  return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs,
+                     default_split_parts(num_kv_heads, capacity_tokens))
+      .total;
+}
+
+extern "C" size_t cpthd_attn_workspace_min_bytes(int64_t capacity_tokens, int32_t cp_size, int32_t num_q_heads,
+                                                 int32_t num_kv_heads, int32_t head_dim, int32_t max_docs) {
+  if (cp_size < 1 || max_docs < 1) return 0;
+  if (check_tokens(capacity_tokens, capacity_tokens, cp_size, max_docs)) return 0;
+  if (check_heads(num_q_heads, num_kv_heads, head_dim)) return 0;
+  return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, 0).total;
 }
 
 namespace cpthd {
@@ -335,7 +555,8 @@ namespace cpthd {
 int launch_plan(const int32_t* cu_a, const int32_t* cu_p, const AttnParams& prm, char* ws, const PlanLayout& lay,
                 bool ensure, int32_t* status, hipStream_t stream, hipEvent_t* ev, int nev, int slot) {
   return launch(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, ev, nev, slot, cu_a, cu_p, prm.num_docs, prm.T,
-                prm.cp, prm.rank, prm.strategy, prm.Hq, prm.Hkv, prm.D, ws, lay, status, ensure ? 1 : 0);
+                prm.cp, prm.rank, prm.strategy, prm.Hq, prm.Hkv, prm.D, prm.num_cu, prm.qsplit, ws, lay, status,
+                ensure ? 1 : 0);
 }
 
 }  // namespace cpthd
@@ -351,6 +572,7 @@ extern "C" int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seql
   if (int e = check_attn_args(total_tokens, capacity_tokens, cp_size, rank, strategy, num_docs, num_q_heads,
                               num_kv_heads, head_dim, 1, -1, 0, workspace, workspace_bytes, lay, prm))
     return e;
+  if (int e = device_cus(prm)) return e;
   return launch_plan(cu_seqlens, cu_seqlens_padded, prm, (char*)workspace, lay, false, dev_status, stream, nullptr,
                      0, 0);
 }

@@ -49,10 +49,15 @@ constexpr int kKvStep = 64;       // keys per inner step of the fwd / dq kernels
 constexpr int kQChunk = 64;       // query rows per inner step of the dk/dv kernel
 constexpr int kCostBins = 2048;   // counting-sort bins for longest-first ordering
 constexpr int kPlanMagic = 0x43505444;  // "CPTD"
-constexpr int kPlanVersion = 2;
+constexpr int kPlanVersion = 3;
 
 // Query tile: `ntok` consecutive local rows of one segment (a run of the rank's
-// rows inside one document), all q heads of one kv group.  Keys [ds, kv_end).
+// rows inside one document), all q heads of one kv group.  Keys [ds, kv_end),
+// visited in 64-key steps [s0, s1) of that range: the whole range, or one part
+// of a tile the plan split so that no work-group holds far more than its share
+// of the launch.  The parts of a split tile write their partial results to
+// partial slots slot .. slot + nparts - 1; a merge kernel, launched after the
+// attention kernel, combines them in part order.
 struct QTile {
   int32_t lrow0;   // first local row
   int32_t ntok;    // rows (tokens) in the tile
@@ -60,16 +65,37 @@ struct QTile {
   int32_t ds;      // document start (physical)
   int32_t kv_end;  // one past the last key any actual row of the tile sees
   int32_t ve;      // end of the document's actual tokens
-  int32_t cost;
+  int32_t cost;    // steps s1 - s0
   int32_t doc;
+  int32_t s0, s1;  // the key steps this entry visits
+  int32_t slot;    // first partial slot of the split tile, -1 when the tile is whole
+  int32_t part, nparts;
+  int32_t pad_[3];
 };
+static_assert(sizeof(QTile) == 64, "query tile is 64 bytes");
 
-// Key tile of one document: keys [k0, k0 + nkeys) (inside the document's slot).
+// Key tile of one document: keys [k0, k0 + nkeys) (inside the document's slot),
+// and of the rank's query chunks that see it, those with index [c0, c1) in the
+// order the kernel visits them (all of them, or one part of a split tile, as
+// for query tiles).
 struct KVTile {
   int32_t k0;
   int32_t nkeys;
   int32_t doc;
-  int32_t cost;
+  int32_t cost;    // chunks c1 - c0
+  int32_t c0, c1;
+  int32_t slot, part, nparts;
+  int32_t pad_[3];
+};
+static_assert(sizeof(KVTile) == 48, "key tile is 48 bytes");
+
+// A split tile, for the merge kernels: its first partial slot, its part count,
+// and the tile's rows (query tiles: a = lrow0, b = ntok, c = p0, d = ve) or
+// keys (key tiles: a = k0, b = nkeys, c = doc).
+struct SplitTile {
+  int32_t slot, nparts;
+  int32_t a, b, c, d;
+  int32_t pad_[2];
 };
 
 // The rank's rows of one document: up to two segments (DualChunkSwap chunks
@@ -83,41 +109,83 @@ struct PlanHeader {
   int32_t magic, version, valid;
   int32_t T, S, cp, rank, strategy, Hq, Hkv, D, G, num_docs;
   int32_t bm_tok;               // tokens per query tile
-  int32_t n_qtiles, n_kvtiles;
-  int32_t max_qtiles, max_kvtiles, max_docs;
-  int32_t pad_[45];
+  int32_t n_qtiles, n_kvtiles;  // entries of the tile lists (parts included)
+  int32_t max_qtiles, max_kvtiles, max_docs, max_parts;
+  int32_t num_cu;               // compute units the split rule balanced the work over
+  int32_t q_part_steps, kv_part_chunks;   // part sizes of split tiles (0: nothing split)
+  int32_t n_qsplit, n_kvsplit;            // split tiles (entries of the merge lists)
+  int32_t pad_[39];
 };
 static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
 
 // Workspace layout (byte offsets), identical on host and device.
 struct PlanLayout {
-  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, cu_copy, delta, lse2, total;
+  size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, cu_copy, qsplit, kvsplit, qpart, kvpart, delta, lse2, total;
   int64_t max_qtiles, max_kvtiles, max_docs;
+  int64_t max_parts;                     // partial slots of each tile list (its entries hold up to that many more)
+  int64_t qpart_stride, kvpart_stride;   // floats per (partial slot, kv head)
 };
 
 __host__ __device__ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 __host__ __device__ inline int tokens_per_qtile(int G) { return kRowsPerWG / G; }
 
-__host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int Hq, int Hkv, int max_docs) {
+// The head dimension the kernels are instantiated for.
+__host__ __device__ inline int padded_head_dim(int D) { return D <= 32 ? 32 : (D <= 64 ? 64 : 128); }
+
+// Partial slots the default workspace holds: 256 / Hkv, at least 8, and at
+// most one per 128 tokens of capacity (a small buffer has no long tiles to
+// split).  One slot holds, per kv head, a query tile's 256 rows (output and
+// softmax statistics) and a key tile's 128 keys (dK and dV) in fp32.
+__host__ __device__ inline int default_split_parts(int Hkv, int64_t capacity) {
+  const int n = 256 / Hkv > 8 ? 256 / Hkv : 8;
+  return capacity / 128 < n ? (int)(capacity / 128) : n;
+}
+
+__host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int Hq, int Hkv, int D, int max_docs,
+                                                  int max_parts) {
   PlanLayout L;
   const int G = Hq / Hkv;
   const int64_t S = capacity / cp;
   const int bm = tokens_per_qtile(G);
+  const int64_t dp = padded_head_dim(D);
   L.max_docs = max_docs;
-  L.max_qtiles = (S + bm - 1) / bm + 2 * (int64_t)max_docs;
-  L.max_kvtiles = (capacity + kKeysPerWG - 1) / kKeysPerWG + (int64_t)max_docs;
+  L.max_parts = max_parts;
+  const int64_t nq = (S + bm - 1) / bm + 2 * (int64_t)max_docs;          // whole query tiles
+  const int64_t nkv = (capacity + kKeysPerWG - 1) / kKeysPerWG + (int64_t)max_docs;
+  L.max_qtiles = nq + max_parts;
+  L.max_kvtiles = nkv + max_parts;
+  L.qpart_stride = (int64_t)kRowsPerWG * (dp + 4);   // per row: the output columns, then (max, sum) pairs
+  L.kvpart_stride = (int64_t)kKeysPerWG * 2 * dp;    // per key: dK and dV columns
   size_t off = sizeof(PlanHeader);
   L.qtiles = off;       off = align_up(off + L.max_qtiles * sizeof(QTile), 256);
-  L.qtiles_tmp = off;   off = align_up(off + L.max_qtiles * sizeof(QTile), 256);
+  L.qtiles_tmp = off;   off = align_up(off + nq * sizeof(QTile), 256);
   L.kvtiles = off;      off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
-  L.kvtiles_tmp = off;  off = align_up(off + L.max_kvtiles * sizeof(KVTile), 256);
+  L.kvtiles_tmp = off;  off = align_up(off + nkv * sizeof(KVTile), 256);
   L.docs = off;         off = align_up(off + (size_t)max_docs * sizeof(DocSeg), 256);
   L.cu_copy = off;      off = align_up(off + 2 * ((size_t)max_docs + 1) * sizeof(int32_t), 256);
+  L.qsplit = off;       off = align_up(off + (size_t)max_parts * sizeof(SplitTile), 256);
+  L.kvsplit = off;      off = align_up(off + (size_t)max_parts * sizeof(SplitTile), 256);
+  L.qpart = off;        off = align_up(off + (size_t)max_parts * Hkv * L.qpart_stride * sizeof(float), 256);
+  L.kvpart = off;       off = align_up(off + (size_t)max_parts * Hkv * L.kvpart_stride * sizeof(float), 256);
   L.delta = off;        off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
   L.lse2 = off;         off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
   L.total = off;
   return L;
+}
+
+// The layout of a call with a workspace of ws_bytes: the most partial slots,
+// up to the default, that it holds (none when it holds only the plan itself).
+inline PlanLayout call_layout(int64_t capacity, int cp, int Hq, int Hkv, int D, int max_docs, size_t ws_bytes) {
+  int lo = 0, hi = default_split_parts(Hkv, capacity);
+  if (plan_layout(capacity, cp, Hq, Hkv, D, max_docs, hi).total > ws_bytes) {
+    while (lo < hi) {   // the layout grows with the slot count
+      const int mid = (lo + hi + 1) / 2;
+      if (plan_layout(capacity, cp, Hq, Hkv, D, max_docs, mid).total <= ws_bytes) lo = mid; else hi = mid - 1;
+    }
+    hi = lo;
+  }
+  return plan_layout(capacity, cp, Hq, Hkv, D, max_docs, hi);
 }
 
 // ---------------------------------------------------------------------------

@@ -162,11 +162,24 @@ int cpthd_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, cons
 
 /*
  * cpthd_attn_workspace_bytes -- workspace size for cpthd_attn_plan /
- * cpthd_attn_fwd / cpthd_attn_bwd at a token capacity and document count.
+ * cpthd_attn_fwd / cpthd_attn_bwd at a token capacity and document count:
+ * the plan, per-row backward scratch, and partial-result slots for split
+ * tiles (see cpthd_attn_plan).  A smaller workspace is accepted down to the
+ * size of the plan and row scratch alone (below it: CPTHD_ERR_WORKSPACE); it
+ * holds fewer partial slots, so fewer tiles are split.  The plan, and so the
+ * results, depend on the workspace size only through that slot count.
  * Returns 0 for arguments no call would accept.
  */
 size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp_size, int32_t num_q_heads,
                                   int32_t num_kv_heads, int32_t head_dim, int32_t max_docs);
+
+/*
+ * cpthd_attn_workspace_min_bytes -- the smallest workspace the attention calls
+ * accept for the same arguments: the plan and row scratch without partial
+ * slots, so no tile is split.  Returns 0 where cpthd_attn_workspace_bytes does.
+ */
+size_t cpthd_attn_workspace_min_bytes(int64_t capacity_tokens, int32_t cp_size, int32_t num_q_heads,
+                                      int32_t num_kv_heads, int32_t head_dim, int32_t max_docs);
 
 /*
  * cpthd_attn_plan -- build the rank's attention metadata into `workspace`
@@ -176,14 +189,21 @@ size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp_size, int3
  * lists the rank's query tiles (each inside one document, with its causal key
  * range) and the key tiles of every document with the rank's query rows that
  * see them, ordered longest first; it records the arguments and a copy of the
- * cu arrays it was built from.  Every attention call checks the workspace's
+ * cu arrays it was built from.  A tile whose work exceeds one compute unit's
+ * share of its launch (the list's work times Hkv over the device's compute
+ * units) is cut into parts -- a key tile along its query chunks; a query tile
+ * along its key steps, only when the call's query tiles times Hkv are fewer
+ * than the compute units -- as far as the workspace's partial slots allow;
+ * the parts write fp32 partial results that a merge kernel combines in part
+ * order, so results do not depend on the order in which work-groups run.  Every attention call checks the workspace's
  * plan against its own arguments and cu arrays and rebuilds it when they
  * differ, so calling this first is optional: it moves the build of a
  * micro-batch's plan ahead of its first attention call.
  *
  *   cu_seqlens, cu_seqlens_padded  device int32 [num_docs + 1]
- *   workspace                      device, >= cpthd_attn_workspace_bytes(...)
- *                                  for capacity_tokens and num_docs, 256-byte aligned
+ *   workspace                      device, cpthd_attn_workspace_bytes(...) bytes
+ *                                  for capacity_tokens and num_docs (or fewer, see
+ *                                  there), 256-byte aligned
  * Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, WORKSPACE, LAUNCH; device bits
  * CU_ORDER, CU_TOTAL, DCS_DIVISIBLE, ACTUAL, DOC_BYTES (the kernels address a
  * document's K/V rows through one 32-bit buffer range).  A layout that raises
@@ -207,10 +227,13 @@ int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded,
  *   q_local   device bf16 [S, Hq, D]          k, v  device bf16 [T, Hkv, D] (physical order)
  *   cu_seqlens, cu_seqlens_padded             device int32 [num_docs + 1], the micro-batch's documents
  *   o_local   device bf16 [S, Hq, D] (out)    lse_local  device float [S, Hq] (out)
- *   workspace device, >= cpthd_attn_workspace_bytes(capacity_tokens, ..., num_docs), 256-byte aligned;
- *             holds the plan (built or checked by this call, see cpthd_attn_plan)
+ *   workspace device, cpthd_attn_workspace_bytes(capacity_tokens, ..., num_docs) bytes (or fewer, see
+ *             there), 256-byte aligned; holds the plan (built or checked by this call, see
+ *             cpthd_attn_plan) and the partial results of split tiles
  * Launches two kernels: the plan check (a rebuild when the workspace holds
- * another plan) and the attention kernel.
+ * another plan) and the attention kernel, then, when query tiles may be split
+ * (see cpthd_attn_plan) and the workspace has partial slots, a third that
+ * merges the parts of split tiles.
  * Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, MASK, WORKSPACE, LAUNCH; device
  * bits as cpthd_attn_plan (then nothing is written) and PLAN.
  */
@@ -238,7 +261,8 @@ int cpthd_attn_fwd(const void* q_local, const void* k, const void* v, const int3
  *   dq_local                    device float [S, Hq, D] (out)
  *   dk, dv                      device float [T, Hkv, D] (out)
  * Launches three kernels (plan check; query-tile pass: delta and dq; key-tile
- * pass: dk, dv).  Errors as cpthd_attn_fwd.
+ * pass: dk, dv), then, when the workspace has partial slots, a fourth that
+ * merges the parts of split tiles.  Errors as cpthd_attn_fwd.
  */
 int cpthd_attn_bwd(const void* q_local, const void* k, const void* v, const void* o_local,
                    const void* do_local, const float* lse_local, const int32_t* cu_seqlens,
@@ -286,15 +310,15 @@ int cpthd_attn_bwd_allgathered(const void* q_local, const void* k_gathered, cons
  * cpthd_attn_bwd_noalloc -- cpthd_attn_bwd (physical-order K/V) without a
  * workspace argument, for callers that cannot allocate device memory: code
  * under HIP graph capture, serving loops, harnesses that forbid hipMalloc.
- * Its scratch (the plan, -delta and LSE rows) is a device array of
- * CPTHD_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
- * process ends; the call allocates and frees nothing.  The array is the
+ * Its scratch (the plan, -delta and LSE rows, partial slots) is a device
+ * array of CPTHD_STATIC_SCRATCH_BYTES inside the library, one per GPU, held
+ * until the process ends; the call allocates and frees nothing.  It builds the
+ * plan a workspace of CPTHD_STATIC_SCRATCH_BYTES bytes gets.  The array is the
  * current device's: call with the device of the buffers current.
  * Every call on one GPU shares that GPU's array, so calls that overlap on one
  * GPU (different streams, or host threads without ordering) race; order them
  * on one stream.  A call whose plan and rows need more than the array holds
- * (cpthd_attn_workspace_bytes(capacity_tokens, ..., num_docs) above the
- * limit) returns CPTHD_ERR_SCRATCH before launching anything.
+ * returns CPTHD_ERR_SCRATCH before launching anything.
  * Arguments, results and other errors as cpthd_attn_bwd.
  */
 #define CPTHD_STATIC_SCRATCH_BYTES 16777216u /* 16 MiB */

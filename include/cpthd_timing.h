@@ -11,9 +11,14 @@
  *   events          n_events caller-created hipEvent_t handles (host array), used in
  *                   (start, stop) pairs around the kernels the call launches, in
  *                   launch order, recorded by hipExtLaunchKernel on `stream`:
- *                   forward  pair 0 plan check, pair 1 attention;
+ *                   forward  pair 0 plan check, pair 1 attention, pair 2 merge of
+ *                            split query tiles;
  *                   backward pair 0 plan check, pair 1 query-tile pass (delta, dq),
- *                            pair 2 key-tile pass (dk, dv).
+ *                            pair 2 key-tile pass (dk, dv), pair 3 merge of split
+ *                            tiles (dq, dk, dv).
+ *                   The merge kernels are launched when tiles may be split (see
+ *                   cpthd_attn_plan, cpthd_attn_fwd and cpthd_attn_bwd); a pair
+ *                   whose kernel a call leaves out is recorded back to back.
  *                   A kernel whose pair lies beyond n_events is launched untimed.
  *                   The events stay the caller's; the call only records them.
  */

@@ -98,6 +98,18 @@ def test_workspace_bytes(lib):
     assert f(65536, 4, 32, 8, 128, 0) == 0
 
 
+def test_workspace_min_bytes(lib):
+    """The smallest accepted workspace (no partial slots) is below the default one wherever the default has slots,
+    equal to it where the capacity is too small for any, and 0 for the same rejected arguments."""
+    fmin, fdef = lib.cpthd_attn_workspace_min_bytes, lib.cpthd_attn_workspace_bytes
+    for args in ((65536, 4, 32, 8, 128, 200), (8192, 2, 16, 16, 128, 40), (4096, 2, 8, 2, 64, 9)):
+        assert 0 < fmin(*args) < fdef(*args)
+    assert fmin(64, 2, 4, 2, 16, 4) == fdef(64, 2, 4, 2, 16, 4)   # under 128 tokens: no slots
+    assert fmin(65536, 4, 32, 7, 128, 200) == 0
+    assert fmin(65535, 4, 32, 8, 128, 200) == 0
+    assert fmin(65536, 4, 32, 8, 128, 0) == 0
+
+
 def test_attention_host_errors(lib):
     d = _defines()
     ws_bytes = lib.cpthd_attn_workspace_bytes(64, 2, 4, 2, 16, 4)
@@ -119,7 +131,7 @@ def test_attention_host_errors(lib):
     assert call_plan(hkv=3) == d["CPTHD_ERR_HEADS"]
     assert call_plan(D=48) == d["CPTHD_ERR_HEADS"]
     assert call_plan(ws=None) == d["CPTHD_ERR_WORKSPACE"]
-    assert call_plan(wsb=ws_bytes - 1) == d["CPTHD_ERR_WORKSPACE"]
+    assert call_plan(wsb=lib.cpthd_attn_workspace_min_bytes(64, 2, 4, 2, 16, 4) - 1) == d["CPTHD_ERR_WORKSPACE"]
     assert call_plan(ws=P + 16) == d["CPTHD_ERR_WORKSPACE"]
 
     def call_fwd(**kw):
@@ -231,6 +243,8 @@ def test_noalloc_backward_host_checks(lib):
         == d["CPTHD_ERR_NULL"]
     assert f(P, P, P, P, P, P, P, P, 4, 64, 64, 2, 0, 0, 4, 2, 16, 0.25, 0, -1, 0, P, P, P, None, None) \
         == d["CPTHD_ERR_MASK"]
+    import context_causal_thd_amd as cpthd
+    assert cpthd.STATIC_SCRATCH_BYTES == d["CPTHD_STATIC_SCRATCH_BYTES"]
     T = 1 << 20   # -delta and LSE rows alone: 2 * 2^20 * 64 * 4 bytes, beyond the array
     assert lib.cpthd_attn_workspace_bytes(T, 1, 64, 8, 128, 1) > d["CPTHD_STATIC_SCRATCH_BYTES"]
     assert f(P, P, P, P, P, P, P, P, 1, T, T, 1, 0, 1, 64, 8, 128, 0.1, 1, -1, 0, P, P, P, None, None) \

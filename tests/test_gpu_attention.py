@@ -25,7 +25,7 @@ class Share:
     """One rank's share on the GPU: plan, forward and (optionally) backward."""
 
     def __init__(self, wl, strategy, rank, capacity=None, backward=True, poison=False, allgathered=False,
-                 kv=None, qdo=None, dev_in=None):
+                 kv=None, qdo=None, dev_in=None, workspace_bytes=None):
         self.wl, self.s, self.r = wl, strategy, rank
         T, cp = wl.T, wl.cp
         S = T // cp
@@ -65,7 +65,8 @@ class Share:
         self.k = buf((wl.Hkv, wl.D), k)
         self.v = buf((wl.Hkv, wl.D), v)
         self.cu_a, self.cu_p = i32_dev(wl.cu_actual), i32_dev(wl.cu_padded)
-        self.plan = cpthd.AttnPlan(cap, cp, wl.Hq, wl.Hkv, wl.D, max_docs=max(wl.num_docs, 1))
+        self.plan = cpthd.AttnPlan(cap, cp, wl.Hq, wl.Hkv, wl.D, max_docs=max(wl.num_docs, 1),
+                                   workspace_bytes=workspace_bytes)
         self.st = status_dev()
         self.plan.build(self.cu_a, self.cu_p, T, rank, strategy, self.st)
         canary = 7.0
@@ -206,6 +207,48 @@ def _late_keys(wl, idx, doc_id, n=64):
     p_last = int(mine.max())
     lo = max(int(wl.cu_padded[doc_id]), p_last - n + 1)
     return np.arange(lo, p_last + 1)
+
+
+def plan_header(plan):
+    """The int32 words of the plan header at the start of the workspace, as the plan kernel records them: word 19
+    is the workspace's partial-slot count, words 21 and 22 the part sizes of split query and key tiles (0: none
+    split)."""
+    return plan.workspace[:256].view(torch.int32).cpu().numpy()
+
+
+def _long_docs():
+    """T = 4096, cp = 2: two long documents (with pads) on a grid far smaller than the chip, so the plan splits
+    both tile lists."""
+    return W.Workload("long2x4096", [2000, 7], 4096, 4, 2, 128, W._cu([2560, 1536]), W._cu([2555, 1500]), 2,
+                      (0, 1), (0, 1), True, qkv_scale=0.5, do_scale=1.0, bf16=True)
+
+
+@pytest.mark.parametrize("s", [0, 1])
+def test_split_tiles_match_whole_tiles(s):
+    """Split tiles (the default workspace) and whole tiles (the smallest workspace, no partial slots) both match
+    the oracle, in physical and all-gathered K/V order; a second run of the split plan gives the same bits (the
+    parts merge in part order, whichever work-group finishes last)."""
+    wl = _long_docs()
+    every = np.arange(wl.T)
+    kv, qdo = (wl.k(), wl.v()), (wl.q(every), wl.do(every))
+    wmin = cpthd.cpthd_attn_workspace_min_bytes(wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D, wl.num_docs)
+    for r in range(wl.cp):
+        log(f"split tiles {wl.name} s={s} r={r}")
+        whole = Share(wl, s, r, kv=kv, qdo=qdo, workspace_bytes=wmin)
+        hw = plan_header(whole.plan)
+        assert hw[19] == 0 and hw[21] == 0 and hw[22] == 0, hw[19:23]
+        whole.compare()
+        for ag in (False, True):
+            split = Share(wl, s, r, kv=kv, qdo=qdo, allgathered=ag)
+            hs = plan_header(split.plan)
+            assert hs[19] > 0 and hs[21] > 0 and hs[22] > 0, hs[19:23]
+            split.compare()
+            if ag:
+                continue
+            again = Share(wl, s, r, kv=kv, qdo=qdo)
+            for name, dt in (("o", torch.int16), ("lse", torch.int32), ("dq", torch.int32), ("dk", torch.int32),
+                             ("dv", torch.int32)):
+                assert torch.equal(getattr(again, name).view(dt), getattr(split, name).view(dt)), name
 
 
 FULL_DOC_WORK = 4_000_000   # (rank rows in a document) x (document length) up to which a document is compared in full

@@ -23,7 +23,9 @@ def _bwd_both(wl, s, r):
     q, k, v, do = _inputs(wl, s, r)
     T, S = wl.T, wl.T // wl.cp
     cu_a, cu_p = i32_dev(wl.cu_actual), i32_dev(wl.cu_padded)
-    plan = cpthd.AttnPlan(T, wl.cp, wl.Hq, wl.Hkv, wl.D, max_docs=wl.num_docs)
+    # a workspace of the static array's size: the same partial slots, so the same plan (and split tiles)
+    plan = cpthd.AttnPlan(T, wl.cp, wl.Hq, wl.Hkv, wl.D, max_docs=wl.num_docs,
+                          workspace_bytes=cpthd.STATIC_SCRATCH_BYTES)
     st = status_dev()
     plan.build(cu_a, cu_p, T, r, s, st)
     o, lse = cpthd.attn_fwd(q, k, v, plan, wl.softmax_scale, dev_status=st)
