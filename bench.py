@@ -51,7 +51,7 @@ PEAK_BF16_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk 
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 STRAT_NAME = {0: "dcs", 1: "contiguous", 2: "packed"}
 KERNELS = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_dkdv", "attn_fwd_merge",
-           "attn_bwd_merge"]
+           "attn_bwd_merge", "attn_fwd_vt"]
 
 KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
 # the physical-order kernels a step launches at head_dim 128 (rocprofv3 kernel names)
@@ -292,7 +292,7 @@ class ShareSet:
     def make_events(self):
         t = self.torch
         return [([[t.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(3)],
-                 [self.cpthd.HipEvents(6), self.cpthd.HipEvents(8)]) for _ in self.shares]
+                 [self.cpthd.HipEvents(8), self.cpthd.HipEvents(8)]) for _ in self.shares]
 
     def step(self, evs=None, allgathered=False):
         """partition -> restoration -> plan -> forward -> backward for every share; `evs` from make_events()
@@ -337,6 +337,7 @@ class ShareSet:
                 # the merge kernels of split tiles (launched when the workspace has partial slots)
                 acc[i, 6] += he[0].elapsed_ms(4, 5)
                 acc[i, 7] += he[1].elapsed_ms(6, 7)
+                acc[i, 8] += he[0].elapsed_ms(6, 7)   # the forward's V^T pass
         return acc / max(len(events), 1)
 
     def timed(self, steps, warmup, allgathered=False, clock=False):
@@ -370,7 +371,7 @@ class ShareSet:
         for i, sh in enumerate(self.shares):
             per_share.append({
                 "strategy": STRAT_NAME[sh["s"]], "rank": sh["r"], "causal_pairs_per_head": int(sh["pairs"]),
-                "fwd_tflops": float(self.flops_fwd[i] / ((pk[i, 3] + pk[i, 6]) * 1e-3) / 1e12),
+                "fwd_tflops": float(self.flops_fwd[i] / ((pk[i, 3] + pk[i, 6] + pk[i, 8]) * 1e-3) / 1e12),
                 "bwd_tflops": float(self.flops_bwd[i] / ((pk[i, 4] + pk[i, 5] + pk[i, 7]) * 1e-3) / 1e12),
                 "fwd_bwd_tflops": float((self.flops_fwd[i] + self.flops_bwd[i]) / (pk[i, 3:].sum() * 1e-3) / 1e12),
                 "ms": {n: float(pk[i, j]) for j, n in enumerate(KERNELS)}})

@@ -8,7 +8,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcpthd.so")
+# the in-tree build; CPTHD_LIB names another build of the same library (a variant built with
+# `python -m context_causal_thd_amd.build --out <path> -D...`)
+LIB_PATH = os.environ.get("CPTHD_LIB") or os.path.join(_HERE, "libcpthd.so")
 
 c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 

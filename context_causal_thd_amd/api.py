@@ -375,8 +375,8 @@ def attn_fwd(q_local, k, v, plan: AttnPlan, softmax_scale=None, o_local=None, ls
              events=None, kv_allgathered=False, layout=None):
     """O and LSE of the rank's query rows for ``layout`` (default: the plan's current one).  ``kv_allgathered``:
     k and v are in rank-major all-gathered order (as an all-gather of the ranks' local K/V leaves them) instead
-    of physical order.  ``events`` (HipEvents of 6) times the call's kernels: plan check, attention, and the merge
-    of split tiles (when the workspace has partial slots)."""
+    of physical order.  ``events`` (HipEvents of 8) times the call's kernels: plan check, attention, the merge of
+    split tiles and the V^T pass (pairs the call leaves out are recorded back to back)."""
     lay = layout or plan.layout
     args = plan._args(lay)
     T = lay.total_tokens

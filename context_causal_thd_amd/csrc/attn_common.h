@@ -314,7 +314,7 @@ __device__ inline bf16x8 acc_to_bf16(const f32x16& a, int r0) {
 // offset the cursor gives; a step over two chunks picks one of two scalar row
 // bases per lane; only a step over more chunks (chunks under 64 keys) maps
 // every lane's row through the map.
-template <bool AG, int DP, int NW>
+template <bool AG, int DP, int NW, bool WITH_V = true>
 __device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buffer_rsrc_t krs,
                                      __amdgpu_buffer_rsrc_t vrs, const AgMap& agm, AgCursor& cur, int kb, int ds,
                                      int kend, uint32_t row_bytes, int kvh, int D, int wave, int lane, uint16_t* Kn,
@@ -338,27 +338,78 @@ __device__ inline void issue_kv_step(TileLoader<DP, true, NW>& ld, __amdgpu_buff
       const int row0 = chunk_row(cur.j) + (kb - cur.start);
       ld.set_rows_linear(row_bytes, col, nvalid);
       ld.issue(krs, Kn, (uint32_t)row0 * row_bytes, wave);
-      ld.issue(vrs, Vn, (uint32_t)row0 * row_bytes, wave);
+      if constexpr (WITH_V) ld.issue(vrs, Vn, (uint32_t)row0 * row_bytes, wave);
     } else if (kb >= cur.start && kb + nvalid <= cur.start + 2 * agm.c && cur.j + 1 < 2 * agm.cp) {
       // two chunks: two runs of consecutive gathered rows
       const int split = cur.start + agm.c - kb;
       ld.set_rows_two(row_bytes, col, nvalid, split, chunk_row(cur.j) + (kb - cur.start), chunk_row(cur.j + 1));
       ld.issue(krs, Kn, 0, wave);
-      ld.issue(vrs, Vn, 0, wave);
+      if constexpr (WITH_V) ld.issue(vrs, Vn, 0, wave);
     } else {
       const int last = kend - 1;
       ld.set_rows([&](int r) __attribute__((always_inline)) { return (uint32_t)agm.row(min(kb + r, last)) * row_bytes + col; },
                   [&](int r) __attribute__((always_inline)) { return kb + r < kend; });
       ld.issue(krs, Kn, 0, wave);
-      ld.issue(vrs, Vn, 0, wave);
+      if constexpr (WITH_V) ld.issue(vrs, Vn, 0, wave);
     }
   } else {
     const uint32_t soff = (uint32_t)(kb - ds) * row_bytes;
     ld.issue(krs, Kn, soff, wave);
-    ld.issue(vrs, Vn, soff, wave);
+    if constexpr (WITH_V) ld.issue(vrs, Vn, soff, wave);
   }
 #endif
 }
+
+// ---------------------------------------------------------------------------
+// V^T tiles of the forward: DP rows (head-dim columns) x 64 keys
+// ---------------------------------------------------------------------------
+// The workspace's V^T rows hold each 16-key group of a row in the order
+// 0-3, 8-11, 4-7, 12-15, which is the order of the contraction index in the
+// forward's P^T operand (the scores' accumulator layout): half-wave h then
+// reads its 8 keys of a 16-key slice as one 16-byte row read at column 8h.
+// Rows are 64 + 8 elements apart, so 8 consecutive rows of a 16-byte read fall
+// on distinct banks.
+template <int DP>
+struct LdsTileVT {
+  static constexpr int SPR = 9;                    // 16-byte slots per row: 8 of keys, 1 of padding
+  static constexpr int STRIDE = 72;                // elements per row
+  static constexpr int ELEMS = DP * STRIDE;
+  static constexpr int NLOAD = DP * SPR / 64;      // 1 KiB wave loads per tile
+  static_assert(DP * SPR % 64 == 0, "whole wave loads");
+};
+
+// Position of key k (0..15) of a 16-key group in a V^T row.
+__host__ __device__ inline int vt_pos16(int k) { return (k & 3) | ((k & 4) << 1) | ((k & 8) >> 1); }
+
+// Direct loads of one step's V^T tile: lane offsets fixed per lane (row d,
+// 16-byte chunk), the step's first column in the scalar offset; rows >= D and
+// padding slots read as zero.
+template <int DP, int NW>
+struct VTLoader {
+  using L = LdsTileVT<DP>;
+  static constexpr int NLW = (L::NLOAD + NW - 1) / NW;
+  uint32_t voff[NLW];
+  __device__ inline void init(int wave, int lane, int D, uint32_t row_bytes) {
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int u = wave + NW * i;
+      const int slot = 64 * u + lane;
+      const int R = slot / L::SPR, ch = slot - R * L::SPR;
+      voff[i] = (u < L::NLOAD && ch < 8 && R < D) ? (uint32_t)R * row_bytes + 16u * ch : 0x80000000u;
+    }
+  }
+  __device__ inline void issue(__amdgpu_buffer_rsrc_t rsrc, uint16_t* tile, uint32_t soff, int wave) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+#pragma unroll
+    for (int i = 0; i < NLW; ++i) {
+      const int u = wave + NW * i;
+      if (u < L::NLOAD)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(tile + 512 * u), 16,
+                                                 voff[i], soff, 0, 0);
+    }
+#endif
+  }
+};
 
 // Host helpers shared by the plan, forward and backward entry points.
 int check_attn_args(int64_t T, int64_t capacity, int32_t cp, int32_t rank, int32_t strategy, int32_t num_docs,

@@ -39,23 +39,23 @@ constexpr int kFwdRowBlocks = CPTHD_FWD_ROW_BLOCKS;
 #define CPTHD_FWD_PREFETCH 1     // K operands of a 32-key block read ahead of its products
 #endif
 
-template <int DP, int QB, bool AG>
+template <int DP, int QB, bool AG, bool VTR>
 __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_EU(kQWaves / QB * kQMinBlocks / 4) void attn_fwd_kernel(const uint16_t* __restrict__ q,
                                                           const uint16_t* __restrict__ k,
                                                           const uint16_t* __restrict__ v, uint16_t* __restrict__ o,
                                                           float* __restrict__ lse, const char* __restrict__ ws,
                                                           PlanLayout lay, AttnParams prm, int32_t* status) {
   constexpr int NW = kQWaves / QB;  // waves, QB 32-row blocks each
-  // K: read by rows (S^T operand); V: read through the transpose read (V^T
-  // operand).  Both use the transpose-friendly row order, so one loader with
-  // the same lane offsets fills both.
+  // K: read by rows (S^T operand).  V^T operand: with VTR, rows of the
+  // workspace's V^T tile, read at the row rate; else the natural V tile
+  // through the transpose read, in K's row order (one loader fills both).
   using KT = LdsTile<DP, true>;
-  using VT = LdsTile<DP, true>;
+  constexpr int V_ELEMS = VTR ? LdsTileVT<VTR ? DP : 64>::ELEMS : LdsTile<DP, true>::ELEMS;
   // two separate buffers per tensor (not one 2-D array): with the step loop
   // unrolled by two, every LDS access names its buffer statically, so the
   // in-flight direct loads into the other buffer need no wait before it
   __shared__ __align__(16) uint16_t K0[KT::ELEMS], K1[KT::ELEMS];
-  __shared__ __align__(16) uint16_t V0[VT::ELEMS], V1[VT::ELEMS];
+  __shared__ __align__(16) uint16_t V0[V_ELEMS], V1[V_ELEMS];
 
   const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
   const int tile = blockIdx.x / prm.Hkv, kvh = blockIdx.x - (blockIdx.x / prm.Hkv) * prm.Hkv;
@@ -87,8 +87,19 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     agm = ag_map(reinterpret_cast<const DocSeg*>(ws + lay.docs)[t.doc], prm);
     agm.chunk_of(t.ds + s0 * kKvStep, cur.j, cur.start);
   }
+  // V^T rows of kv head kvh: the tile's keys from column t.vt on (the
+  // document's columns, zero past its actual tokens)
+  VTLoader<VTR ? DP : 64, NW> vtld;   // (unused without VTR; 64 keeps the type valid for head dim 32)
+  __amdgpu_buffer_rsrc_t vtrs;
+  if constexpr (VTR) {
+    const uint32_t vt_row_bytes = (uint32_t)lay.vt_cols * 2;
+    vtrs = make_rsrc(reinterpret_cast<const uint16_t*>(ws + lay.vt) + (int64_t)kvh * D * lay.vt_cols,
+                     (uint32_t)D * vt_row_bytes);
+    vtld.init(wave, lane, D, vt_row_bytes);
+  }
   auto issue_kv = [&](int kb, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
-    issue_kv_step<AG>(kvld, krs, vrs, agm, cur, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
+    issue_kv_step<AG, DP, NW, !VTR>(kvld, krs, vrs, agm, cur, kb, t.ds, kend, row_bytes, kvh, D, wave, lane, Kn, Vn);
+    if constexpr (VTR) vtld.issue(vtrs, Vn, (uint32_t)(t.vt + (kb - t.ds)) * 2u, wave);
   };
   if constexpr (AG) {
     kvld.init_slots(wave, lane, D);
@@ -239,7 +250,11 @@ __global__ __launch_bounds__(64 * (kQWaves / QB), kQMinBlocks) CPTHD_WAVES_PER_E
     for (int db = 0; db < DP / 32; ++db)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = lds_tr8<DP, true>(Vt, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
+        bf16x8 a;
+        if constexpr (VTR)   // keys 16ks + 4h + 0..3 and 16ks + 8 + 4h + 0..3, stored together at column 16ks + 8h
+          a = *reinterpret_cast<const bf16x8*>(Vt + (32 * db + l32) * LdsTileVT<64>::STRIDE + 16 * ks + 8 * h);
+        else
+          a = lds_tr8<DP, true>(Vt, 16 * ks + 4 * h, 16 * ks + 8 + 4 * h, 32 * db);
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) acc[qb][db] = mfma32(a, pb[qb][ks], acc[qb][db]);
       }
@@ -372,13 +387,83 @@ __global__ __launch_bounds__(64) void attn_fwd_merge_kernel(uint16_t* __restrict
   if (h == 0) lse[qrow] = (valid && l_tot > 0.f) ? (mx + log2_fast(l_tot)) * 0.69314718055994531f : -INFINITY;
 }
 
+// ---------------------------------------------------------------------------
+// V^T of the forward, written once per call
+// ---------------------------------------------------------------------------
+// One work-group per (key tile of the plan's list before splitting, kv head):
+// the tile's 128 keys of V go through LDS and out as 128-column pieces of the
+// D rows of V^T, each 16-key group in the order the forward's operand wants
+// (vt_pos16).  Keys past the tile's end or at or past the document's actual
+// end are written as zeros, so every column a forward step loads is finite.
+template <bool AG>
+__global__ __launch_bounds__(256) void attn_vt_kernel(const uint16_t* __restrict__ v, char* __restrict__ ws,
+                                                     PlanLayout lay, AttnParams prm, int32_t* status) {
+  __shared__ __align__(16) uint16_t sv[kKeysPerWG * (128 + 8)];   // [key][d], rows D + 8 apart
+  const PlanHeader* hdr = reinterpret_cast<const PlanHeader*>(ws);
+  const int Hkv = prm.Hkv, D = prm.D, tid = threadIdx.x;
+  const int t = blockIdx.x / Hkv, kvh = blockIdx.x - t * Hkv;
+  const KVTile kt = reinterpret_cast<const KVTile*>(ws + lay.kvtiles_tmp)[t];
+  const bool kt_ok = (kt.doc >= 0) & (kt.doc < prm.num_docs) & (kt.k0 >= 0) & (kt.nkeys >= 0) &
+                     (kt.nkeys <= kKeysPerWG) & (kt.k0 <= prm.T - kt.nkeys);
+  if (!tile_usable(plan_matches(hdr, prm, lay), t < hdr->n_kvwhole, kt_ok, status)) return;
+  const DocSeg d = reinterpret_cast<const DocSeg*>(ws + lay.docs)[kt.doc];
+  AgMap agm;
+  if constexpr (AG) {
+    const bool ds_ok = docseg_ok(d, prm) & ((prm.strategy != kDCS) |
+                                            ((kt.k0 >= d.ds) & (kt.k0 - d.ds <= 2 * prm.cp * d.na - kt.nkeys)));
+    if (!tile_usable(true, true, ds_ok, status)) return;
+    agm = ag_map(d, prm);
+  }
+  const int stride = D + 8, cpr = D / 8;   // LDS row stride; 16-byte chunks per key row
+  // keys [k0, k0 + 128) of kv head kvh into LDS, zeros past the tile or the document's actual tokens
+  for (int c = tid; c < kKeysPerWG * cpr; c += 256) {
+    const int key = c / cpr, ch = c - key * cpr, p = kt.k0 + key;
+    u32x4 val = {0u, 0u, 0u, 0u};
+    if (key < kt.nkeys && p < d.ve) {
+      const int64_t row = (AG ? (int64_t)agm.row(p) : (int64_t)p) * Hkv + kvh;
+      val = *reinterpret_cast<const u32x4*>(v + row * D + 8 * ch);
+    }
+    *reinterpret_cast<u32x4*>(sv + key * stride + 8 * ch) = val;
+  }
+  __syncthreads();
+  // row dd of V^T, columns 128 t .. +127: 16 chunks of 8 positions
+  uint16_t* out = reinterpret_cast<uint16_t*>(ws + lay.vt) + (int64_t)kvh * D * lay.vt_cols + (int64_t)t * kKeysPerWG;
+  for (int c = tid; c < D * 16; c += 256) {
+    const int dd = c >> 4, cc = c & 15;
+    uint16_t e[8];
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const int pos = 8 * cc + s;
+      e[s] = sv[((pos & ~15) | vt_pos16(pos & 15)) * stride + dd];
+    }
+    u32x4 w;
+    w.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
+    w.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
+    w.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
+    w.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
+    *reinterpret_cast<u32x4*>(out + (int64_t)dd * lay.vt_cols + 8 * cc) = w;
+  }
+}
+
 template <int DP, bool AG>
 static int launch_fwd(const void* q, const void* k, const void* v, void* o, float* lse, const char* ws,
                       const PlanLayout& lay, const AttnParams& prm, int32_t* status, unsigned grid,
                       hipStream_t stream, hipEvent_t* ev, int nev) {
   constexpr int QB = kFwdRowBlocks;
-  int e = launch(attn_fwd_kernel<DP, QB, AG>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 1,
-                 (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+  int e;
+  if (DP >= 64 && lay.has_vt) {   // (call_layout gives V^T rows only where vt_wanted)
+    // V^T rows first (event pair 3), then the forward reading them at the row rate
+    const int64_t gvt = ((int64_t)(prm.T + kKeysPerWG - 1) / kKeysPerWG + prm.num_docs) * prm.Hkv;
+    e = launch(attn_vt_kernel<AG>, dim3((unsigned)gvt), dim3(256), 0, stream, ev, nev, 3, (const uint16_t*)v,
+               const_cast<char*>(ws), lay, prm, status);
+    if (e) return e;
+    e = launch(attn_fwd_kernel<DP, QB, AG, (DP >= 64)>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 1,
+               (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+  } else {
+    if ((e = skip_launch(ev, nev, 3, stream))) return e;
+    e = launch(attn_fwd_kernel<DP, QB, AG, false>, dim3(grid), dim3(64 * (kQWaves / QB)), 0, stream, ev, nev, 1,
+               (const uint16_t*)q, (const uint16_t*)k, (const uint16_t*)v, (uint16_t*)o, lse, ws, lay, prm, status);
+  }
   if (e) return e;
   if (lay.max_parts < 2 || !prm.qsplit) return skip_launch(ev, nev, 2, stream);   // no split query tile possible
   return launch(attn_fwd_merge_kernel<DP>, dim3((unsigned)(split_grid(prm, lay) * (kRowsPerWG / 32))), dim3(64), 0,

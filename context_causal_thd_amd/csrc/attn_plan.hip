@@ -363,6 +363,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       hdr->n_kvtiles = 0;
       hdr->n_qsplit = 0;
       hdr->n_kvsplit = 0;
+      hdr->n_kvwhole = 0;
     }
     return;
   }
@@ -425,6 +426,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
       e.slot = -1;
       e.part = 0;
       e.nparts = 1;
+      e.vt = (carry_kv + s_kvoff[lo]) * kKeysPerWG;   // the document's first key tile, in V^T columns
       qtmp[carry_q + t] = e;
       if (carry_q + t < kLdsCosts) s_split[0].cost[carry_q + t] = e.cost;
       atomicAdd(&s_hist_q[min(e.cost, kCostBins - 1)], 1);
@@ -524,6 +526,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int32_t* __res
     hdr->kv_part_chunks = n_kvsplit ? s_split[1].P : 0;
     hdr->n_qsplit = n_qsplit;
     hdr->n_kvsplit = n_kvsplit;
+    hdr->n_kvwhole = carry_kv;
     hdr->valid = 1;
   }
 }
@@ -537,8 +540,12 @@ extern "C" size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp
   if (cp_size < 1 || max_docs < 1) return 0;
   if (check_tokens(capacity_tokens, capacity_tokens, cp_size, max_docs)) return 0;
   if (check_heads(num_q_heads, num_kv_heads, head_dim)) return 0;
+  // with the V^T rows of the forward where it reads them
+  const PlanLayout v = plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs,
+                                   default_split_parts(num_kv_heads, capacity_tokens), true);
+  if (vt_wanted(head_dim, v.vt_cols)) return v.total;
   return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs,
-                     default_split_parts(num_kv_heads, capacity_tokens))
+                     default_split_parts(num_kv_heads, capacity_tokens), false)
       .total;
 }
 
@@ -547,7 +554,7 @@ extern "C" size_t cpthd_attn_workspace_min_bytes(int64_t capacity_tokens, int32_
   if (cp_size < 1 || max_docs < 1) return 0;
   if (check_tokens(capacity_tokens, capacity_tokens, cp_size, max_docs)) return 0;
   if (check_heads(num_q_heads, num_kv_heads, head_dim)) return 0;
-  return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, 0).total;
+  return plan_layout(capacity_tokens, cp_size, num_q_heads, num_kv_heads, head_dim, max_docs, 0, false).total;
 }
 
 namespace cpthd {

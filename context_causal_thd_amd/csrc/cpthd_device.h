@@ -70,7 +70,8 @@ struct QTile {
   int32_t s0, s1;  // the key steps this entry visits
   int32_t slot;    // first partial slot of the split tile, -1 when the tile is whole
   int32_t part, nparts;
-  int32_t pad_[3];
+  int32_t vt;      // column of key ds in the workspace's V^T rows
+  int32_t pad_[2];
 };
 static_assert(sizeof(QTile) == 64, "query tile is 64 bytes");
 
@@ -114,13 +115,17 @@ struct PlanHeader {
   int32_t num_cu;               // compute units the split rule balanced the work over
   int32_t q_part_steps, kv_part_chunks;   // part sizes of split tiles (0: nothing split)
   int32_t n_qsplit, n_kvsplit;            // split tiles (entries of the merge lists)
-  int32_t pad_[39];
+  int32_t n_kvwhole;                      // key tiles before splitting (they tile the V^T columns)
+  int32_t pad_[38];
 };
 static_assert(sizeof(PlanHeader) == 256, "plan header is 256 bytes");
 
 // Workspace layout (byte offsets), identical on host and device.
 struct PlanLayout {
   size_t qtiles, qtiles_tmp, kvtiles, kvtiles_tmp, docs, cu_copy, qsplit, kvsplit, qpart, kvpart, delta, lse2, total;
+  size_t vt;          // V^T rows (when has_vt): [Hkv][D][vt_cols] bf16
+  bool has_vt;
+  int64_t vt_cols;    // 128 columns per key tile of the list before splitting
   int64_t max_qtiles, max_kvtiles, max_docs;
   int64_t max_parts;                     // partial slots of each tile list (its entries hold up to that many more)
   int64_t qpart_stride, kvpart_stride;   // floats per (partial slot, kv head)
@@ -143,7 +148,7 @@ __host__ __device__ inline int default_split_parts(int Hkv, int64_t capacity) {
 }
 
 __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int Hq, int Hkv, int D, int max_docs,
-                                                  int max_parts) {
+                                                  int max_parts, bool with_vt) {
   PlanLayout L;
   const int G = Hq / Hkv;
   const int64_t S = capacity / cp;
@@ -170,22 +175,44 @@ __host__ __device__ inline PlanLayout plan_layout(int64_t capacity, int cp, int 
   L.kvpart = off;       off = align_up(off + (size_t)max_parts * Hkv * L.kvpart_stride * sizeof(float), 256);
   L.delta = off;        off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
   L.lse2 = off;         off = align_up(off + (size_t)S * Hq * sizeof(float), 256);
+  // V^T of the forward: one row per (kv head, head-dim column), the keys of
+  // document i from column 128 * (its first key tile) on, each document's
+  // columns padded to a multiple of 128 with zeros
+  L.vt_cols = nkv * kKeysPerWG;
+  L.has_vt = with_vt;
+  L.vt = off;
+  if (with_vt) off = align_up(off + (size_t)Hkv * D * L.vt_cols * 2, 256);
   L.total = off;
   return L;
 }
 
-// The layout of a call with a workspace of ws_bytes: the most partial slots,
-// up to the default, that it holds (none when it holds only the plan itself).
+// Whether the forward reads V^T rows written by a pass of its own instead of
+// reading V through the transpose LDS read: only in builds with CPTHD_FWD_VT=1
+// (measured slower: the V^T pass costs 2-6% of the forward and the forward
+// itself does not gain), for head dim 64 or 128 (the V^T tile needs whole wave
+// loads), with a kv head's rows inside one 32-bit buffer range.
+#ifndef CPTHD_FWD_VT
+#define CPTHD_FWD_VT 0
+#endif
+__host__ __device__ inline bool vt_wanted(int D, int64_t vt_cols) {
+  return CPTHD_FWD_VT && D >= 64 && (int64_t)D * vt_cols * 2 < ((int64_t)1 << 31);
+}
+
+// The layout of a call with a workspace of ws_bytes: the V^T rows when they
+// fit beside the plan, then the most partial slots, up to the default, that
+// the rest holds (none when it holds only the plan itself).
 inline PlanLayout call_layout(int64_t capacity, int cp, int Hq, int Hkv, int D, int max_docs, size_t ws_bytes) {
+  const PlanLayout v0 = plan_layout(capacity, cp, Hq, Hkv, D, max_docs, 0, true);
+  const bool vt = v0.total <= ws_bytes && vt_wanted(D, v0.vt_cols);
   int lo = 0, hi = default_split_parts(Hkv, capacity);
-  if (plan_layout(capacity, cp, Hq, Hkv, D, max_docs, hi).total > ws_bytes) {
+  if (plan_layout(capacity, cp, Hq, Hkv, D, max_docs, hi, vt).total > ws_bytes) {
     while (lo < hi) {   // the layout grows with the slot count
       const int mid = (lo + hi + 1) / 2;
-      if (plan_layout(capacity, cp, Hq, Hkv, D, max_docs, mid).total <= ws_bytes) lo = mid; else hi = mid - 1;
+      if (plan_layout(capacity, cp, Hq, Hkv, D, max_docs, mid, vt).total <= ws_bytes) lo = mid; else hi = mid - 1;
     }
     hi = lo;
   }
-  return plan_layout(capacity, cp, Hq, Hkv, D, max_docs, hi);
+  return plan_layout(capacity, cp, Hq, Hkv, D, max_docs, hi, vt);
 }
 
 // ---------------------------------------------------------------------------

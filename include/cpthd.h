@@ -163,11 +163,14 @@ int cpthd_gather_rows(const void* src, int64_t src_rows, int64_t row_bytes, cons
 /*
  * cpthd_attn_workspace_bytes -- workspace size for cpthd_attn_plan /
  * cpthd_attn_fwd / cpthd_attn_bwd at a token capacity and document count:
- * the plan, per-row backward scratch, and partial-result slots for split
- * tiles (see cpthd_attn_plan).  A smaller workspace is accepted down to the
- * size of the plan and row scratch alone (below it: CPTHD_ERR_WORKSPACE); it
- * holds fewer partial slots, so fewer tiles are split.  The plan, and so the
- * results, depend on the workspace size only through that slot count.
+ * the plan, per-row backward scratch, partial-result slots for split tiles
+ * (see cpthd_attn_plan) and, for the forward, V^T rows of the documents'
+ * keys (Hkv * D rows of 128 columns per key tile; left out where a kv head's
+ * rows would pass 2 GiB).  A smaller workspace is accepted down to the size of
+ * the plan and row scratch alone (below it: CPTHD_ERR_WORKSPACE): it holds the
+ * V^T rows only if they fit beside the plan, then as many partial slots as
+ * fit, so fewer tiles are split.  The plan, and so the results, depend on the
+ * workspace size only through that slot count.
  * Returns 0 for arguments no call would accept.
  */
 size_t cpthd_attn_workspace_bytes(int64_t capacity_tokens, int32_t cp_size, int32_t num_q_heads,
@@ -230,10 +233,14 @@ int cpthd_attn_plan(const int32_t* cu_seqlens, const int32_t* cu_seqlens_padded,
  *   workspace device, cpthd_attn_workspace_bytes(capacity_tokens, ..., num_docs) bytes (or fewer, see
  *             there), 256-byte aligned; holds the plan (built or checked by this call, see
  *             cpthd_attn_plan) and the partial results of split tiles
- * Launches two kernels: the plan check (a rebuild when the workspace holds
- * another plan) and the attention kernel, then, when query tiles may be split
- * (see cpthd_attn_plan) and the workspace has partial slots, a third that
- * merges the parts of split tiles.
+ * Launches the plan check (a rebuild when the workspace holds another plan);
+ * for head dim 64 and 128, when the workspace holds V^T rows (see
+ * cpthd_attn_workspace_bytes), a pass that writes V^T of the call's documents
+ * there, so the attention kernel reads its V^T operand as rows instead of
+ * through the transpose LDS read; the attention kernel; and, when query tiles
+ * may be split (see cpthd_attn_plan) and the workspace has partial slots, a
+ * kernel that merges the parts of split tiles.  With or without V^T the
+ * results are the same bits.
  * Errors: NULL, RANK, STRATEGY, TOKENS, HEADS, MASK, WORKSPACE, LAUNCH; device
  * bits as cpthd_attn_plan (then nothing is written) and PLAN.
  */

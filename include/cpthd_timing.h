@@ -12,7 +12,8 @@
  *                   (start, stop) pairs around the kernels the call launches, in
  *                   launch order, recorded by hipExtLaunchKernel on `stream`:
  *                   forward  pair 0 plan check, pair 1 attention, pair 2 merge of
- *                            split query tiles;
+ *                            split query tiles, pair 3 the V^T pass (launched
+ *                            before the attention kernel);
  *                   backward pair 0 plan check, pair 1 query-tile pass (delta, dq),
  *                            pair 2 key-tile pass (dk, dv), pair 3 merge of split
  *                            tiles (dq, dk, dv).

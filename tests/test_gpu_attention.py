@@ -251,6 +251,36 @@ def test_split_tiles_match_whole_tiles(s):
                 assert torch.equal(getattr(again, name).view(dt), getattr(split, name).view(dt)), name
 
 
+def _d64_full_grid():
+    """T = 16,384, cp = 2, 8 q / 8 kv heads of head dim 64: 8,192-token shares in 32 query tiles of 256 tokens per
+    kv head, enough work-groups to fill the device (no query tile is split)."""
+    return W.Workload("d64x16384", [2000, 9], 16384, 8, 8, 64, W._cu([3000, 5000, 4004, 4380]),
+                      W._cu([2990, 5000, 3999, 4380]), 2, (0, 1), (0, 1), False, qkv_scale=0.5, bf16=True)
+
+
+@pytest.mark.parametrize("name", ["t8192_mha16", "d64x16384"])
+def test_forward_bits_independent_of_workspace_size(name):
+    """With the full device occupied (no query tile split), the forward gives the same bits with the default
+    workspace and with the smallest one, in physical and all-gathered K/V order.  In a build with V^T rows
+    (CPTHD_FWD_VT=1) the default workspace holds them and the smallest does not, so this compares the forward
+    reading V^T rows with the forward reading V through the transpose LDS read."""
+    wl = W.t8192_mha16() if name == "t8192_mha16" else _d64_full_grid()
+    every = np.arange(wl.T)
+    kv, qdo = (wl.k(), wl.v()), (wl.q(every), None)
+    wmin = cpthd.cpthd_attn_workspace_min_bytes(wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D, wl.num_docs)
+    assert wmin < cpthd.cpthd_attn_workspace_bytes(wl.T, wl.cp, wl.Hq, wl.Hkv, wl.D, wl.num_docs)
+    for s in (0, 1):
+        for r in range(wl.cp):
+            for ag in (False, True):
+                log(f"vt rows {wl.name} s={s} r={r} ag={ag}")
+                rows = Share(wl, s, r, backward=False, kv=kv, qdo=qdo, allgathered=ag)
+                tr = Share(wl, s, r, backward=False, kv=kv, qdo=qdo, allgathered=ag, workspace_bytes=wmin)
+                assert torch.equal(rows.o.view(torch.int16), tr.o.view(torch.int16))
+                assert torch.equal(rows.lse.view(torch.int32), tr.lse.view(torch.int32))
+                if not ag and r == 0:
+                    rows.compare(docs=[0, wl.num_docs - 1], kv_heads=[0, wl.Hkv - 1], backward=False)
+
+
 FULL_DOC_WORK = 4_000_000   # (rank rows in a document) x (document length) up to which a document is compared in full
 
 
