@@ -55,7 +55,7 @@ KERNELS = ["partition", "reorder", "plan", "attn_fwd", "attn_bwd_dq", "attn_bwd_
 
 KERNEL_SOURCES = ("attn_bwd.hip", "attn_fwd.hip", "attn_common.h", "cpthd_device.h")
 # the physical-order kernels a step launches at head_dim 128 (rocprofv3 kernel names)
-KERNEL_SYMBOL = {"attn_fwd": "cpthd::attn_fwd_kernel<128, 1, false>",
+KERNEL_SYMBOL = {"attn_fwd": "cpthd::attn_fwd_kernel<128, 1, false, false>",
                  "attn_bwd_dq": "cpthd::attn_bwd_dq_kernel<128, 1, false>",
                  "attn_bwd_dkdv": "cpthd::attn_bwd_dkdv_kernel<128, 2, false>"}
 
