@@ -193,8 +193,9 @@ def test_small_full_parity(wl):
 # The measured workloads draw Q/K/V from 0.5 N(0,1).  The same layouts with unit-normal Q/K/V (logits four
 # times wider, so sharper softmax rows and larger gradients) under the same bounds, so that the bound is not
 # met only because of that scale.
-UNIT_NORMAL = [W.small_random(700 + i, cp, s, max_docs=4, max_len=ml, Hq=hq, Hkv=hkv, D=d, bf16=True,
-                              qkv_scale=1.0, do_scale=1.0)
+UNIT_NORMAL = [dataclasses.replace(W.small_random(700 + i, cp, s, max_docs=4, max_len=ml, Hq=hq, Hkv=hkv, D=d,
+                                                  bf16=True, qkv_scale=1.0, do_scale=1.0),
+                                   name=f"unit_normal.small{700 + i}")
                for i, (cp, s, hq, hkv, d, ml) in enumerate([(2, 0, 8, 2, 128, 1024), (3, 1, 16, 2, 128, 768),
                                                            (2, 2, 4, 4, 64, 700), (4, 0, 8, 1, 128, 1024),
                                                            (1, 0, 16, 2, 128, 1024)])]
@@ -211,7 +212,7 @@ def test_unit_normal_inputs(wl):
 @pytest.mark.parametrize("s,r", [(0, 0), (1, 3)])
 def test_t32768_gqa32x8_unit_normal_sampled(s, r):
     """The Llama-3-8B shape with unit-normal Q/K/V, sampled documents and kv heads."""
-    wl = dataclasses.replace(W.t32768_gqa32x8(), qkv_scale=1.0)
+    wl = dataclasses.replace(W.t32768_gqa32x8(), qkv_scale=1.0, name="t32768_gqa32x8.unit_normal")
     log(f"t32768_gqa32x8 unit-normal s={s} r={r}")
     compare_share(Share(wl, s, r), [0, 7])
 
