@@ -57,11 +57,13 @@ def to_np64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def assert_attn_close(name, got, ref, valid=None):
+def assert_attn_close(name, got, ref, valid=None, atol_rel_to_max=False):
     """Max-abs and relative-L2 on `valid` entries; everything else must match exactly.
 
     ``ref`` may hold NaN where the oracle did not compute (sampled checks): those
-    entries are skipped.
+    entries are skipped.  With ``atol_rel_to_max`` the max-abs bound is ATOL times
+    the larger of 1 and the reference's largest magnitude (for inputs far outside
+    the measured workloads' value range, where the gradients grow with them).
     """
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
@@ -82,9 +84,10 @@ def assert_attn_close(name, got, ref, valid=None):
         mx = float(err.max())
         nrm = float(np.linalg.norm(r))
         rel = float(np.linalg.norm(g - r) / nrm) if nrm > 0 else float(np.linalg.norm(g - r))
-        log(f"    {name}: max_abs={mx:.3e} rel_l2={rel:.3e} n={g.size}")
+        atol = ATOL * max(1.0, float(np.abs(r).max())) if atol_rel_to_max else ATOL
+        log(f"    {name}: max_abs={mx:.3e} rel_l2={rel:.3e} n={g.size} (max |ref| {float(np.abs(r).max()):.3g})")
         _record(name, mx, rel, g.size)
-        assert mx <= ATOL, f"{name}: max abs error {mx:.4e} > {ATOL}"
+        assert mx <= atol, f"{name}: max abs error {mx:.4e} > {atol}"
         assert rel <= REL_L2, f"{name}: relative L2 error {rel:.4e} > {REL_L2}"
 
 

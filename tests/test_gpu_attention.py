@@ -98,7 +98,7 @@ class Share:
         if hasattr(self, "dq"):
             assert (self.dq[S:] == 7.0).all() and (self.dk[T:] == 7.0).all() and (self.dv[T:] == 7.0).all()
 
-    def compare(self, docs=None, kv_heads=None, backward=True, rows=None, keys=None):
+    def compare(self, docs=None, kv_heads=None, backward=True, rows=None, keys=None, atol_rel_to_max=False):
         """GPU results against the oracle.  Everywhere (checked on the GPU): finite values, O = 0 and LSE = -inf on
         pad rows, dQ = 0 on pad rows and dK = dV = 0 on pad keys.  Within tolerance, with pads exact: the sampled
         documents (all by default) on the sampled kv heads (their q heads) and, optionally, only the given local
@@ -129,7 +129,7 @@ class Share:
         o_s, lse_s, dq_s, dk_s, dv_s = oracle_sampled(
             q_s, k_s, v_s, self.do_np[lsel][:, hsel] if backward else None, idx_s, wl.cu_padded, wl.cu_actual,
             wl.softmax_scale, G, docs=docs, rows=sub_rows, keys=keys)
-        assert_attn_close("O", rows_of(self.o), o_s, vq[lsel][:, None, None])
+        assert_attn_close("O", rows_of(self.o), o_s, vq[lsel][:, None, None], atol_rel_to_max=atol_rel_to_max)
         assert_attn_close("LSE", rows_of(self.lse), lse_s, vq[lsel][:, None])
         if not backward:
             return
@@ -148,9 +148,12 @@ class Share:
         def keys_of(t):
             return t.index_select(0, krows_d).index_select(1, gsel_d).double().cpu().numpy()
 
-        assert_attn_close("dQ", rows_of(self.dq), dq_s, vq[lsel][:, None, None])
-        assert_attn_close("dK", keys_of(dk_d), dk_s[krows], valid_tok[krows][:, None, None])
-        assert_attn_close("dV", keys_of(dv_d), dv_s[krows], valid_tok[krows][:, None, None])
+        assert_attn_close("dQ", rows_of(self.dq), dq_s, vq[lsel][:, None, None],
+                          atol_rel_to_max=atol_rel_to_max)
+        assert_attn_close("dK", keys_of(dk_d), dk_s[krows], valid_tok[krows][:, None, None],
+                          atol_rel_to_max=atol_rel_to_max)
+        assert_attn_close("dV", keys_of(dv_d), dv_s[krows], valid_tok[krows][:, None, None],
+                          atol_rel_to_max=atol_rel_to_max)
 
 
 def _small_cases():
@@ -207,6 +210,25 @@ def test_unit_normal_inputs(wl):
     for r in range(wl.cp):
         log(f"{wl.name} unit-normal T={wl.T} docs={wl.num_docs} s={s} r={r}")
         Share(wl, s, r).compare()
+
+
+# Far outside the measured value range: Q/K/V ~ 3 N(0,1) puts the logits' spread near 9, so most rows'
+# softmax is dominated by a few keys and the running maximum jumps by many times the rescale threshold.  O and
+# the gradients grow with the inputs (O up to ~13, where bf16's half-ulp alone is 3e-2), so their max-abs bound
+# is taken relative to the largest reference magnitude; LSE and every relative-L2 bound are unchanged.
+LARGE_LOGITS = [dataclasses.replace(W.small_random(720 + i, cp, s, max_docs=4, max_len=ml, Hq=hq, Hkv=hkv, D=d,
+                                                   bf16=True, qkv_scale=2.0, do_scale=1.0),
+                                    name=f"large_logits.small{720 + i}")
+                for i, (cp, s, hq, hkv, d, ml) in enumerate([(2, 0, 8, 2, 128, 1024), (3, 1, 8, 1, 64, 768),
+                                                            (2, 2, 4, 4, 128, 700)])]
+
+
+@pytest.mark.parametrize("wl", LARGE_LOGITS, ids=lambda w: f"{w.name}-D{w.D}-h{w.Hq}x{w.Hkv}-cp{w.cp}-s{w.strategies[0]}")
+def test_large_logits(wl):
+    s = wl.strategies[0]
+    for r in range(wl.cp):
+        log(f"{wl.name} large logits T={wl.T} docs={wl.num_docs} s={s} r={r}")
+        Share(wl, s, r).compare(atol_rel_to_max=True)
 
 
 @pytest.mark.parametrize("s,r", [(0, 0), (1, 3)])
