@@ -175,6 +175,22 @@ def _small_cases():
 SMALL = _small_cases()
 
 
+# Eight and sixteen ranks (the configured workloads stop at cp_size 8; 16 chunks per document under
+# DualChunkSwap at cp 8, 32 at cp 16): every rank of a small layout for each strategy.
+WIDE_CP = [W.small_random(740 + i, cp, s, max_docs=4, max_len=ml, Hq=4, Hkv=2, D=64, bf16=True, qkv_scale=0.5,
+                          do_scale=1.0)
+           for i, (cp, s, ml) in enumerate([(8, 0, 1024), (8, 1, 700), (8, 2, 900), (16, 0, 1600), (16, 1, 600),
+                                            (16, 2, 1100)])]
+
+
+@pytest.mark.parametrize("wl", WIDE_CP, ids=lambda w: f"{w.name}-cp{w.cp}-s{w.strategies[0]}")
+def test_many_ranks(wl):
+    s = wl.strategies[0]
+    for r in range(wl.cp):
+        log(f"{wl.name} T={wl.T} docs={wl.num_docs} cp={wl.cp} s={s} r={r}")
+        Share(wl, s, r).compare()
+
+
 def test_tiny_t28_all_shares():
     wl = W.tiny_t28(bf16=True)
     for s in wl.strategies:

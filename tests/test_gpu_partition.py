@@ -16,7 +16,7 @@ def _layouts():
     out = [("tiny_t28", W.tiny_t28()), ("t8192_mha16", W.t8192_mha16()), ("t32768_gqa32x8", W.t32768_gqa32x8()), ("t131072_gqa64x8", W.t131072_gqa64x8())]
     out += [(f"dynamic_t.mb{m}", W.dynamic_t(m)) for m in range(W.DYNAMIC_T_MICROBATCHES)]
     for seed in range(12):
-        for cp in (1, 2, 3, 4, 8):
+        for cp in (1, 2, 3, 4, 8, 16):
             for s in (0, 1, 2):
                 out.append((f"small{seed}.cp{cp}.s{s}", W.small_random(seed, cp, s, max_docs=7, max_len=200)))
     return out
