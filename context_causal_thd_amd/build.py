@@ -5,7 +5,7 @@
 Kernel variants kept for measurement are compile-time switches (CPTHD_* macros in csrc/); build one into another
 file without touching the in-tree library with
 
-    python -m context_causal_thd_amd.build --out <path.so> -DCPTHD_BWD_FUSED=1
+    python -m context_causal_thd_amd.build --out <path.so> -DCPTHD_FWD_VT=1
 """
 from __future__ import annotations
 
