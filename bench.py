@@ -69,16 +69,20 @@ def traffic_file(workload):
 
 
 def kernel_source_hash(root=ROOT):
-    """sha256 of the attention kernels' code: the sources with comments removed and whitespace collapsed, so a
-    comment edit does not invalidate counters taken on the same code."""
+    """sha256 of the attention kernels' code and compile flags: the sources with comments removed and whitespace
+    collapsed (a comment edit does not invalidate counters taken on the same code), plus the build's common and
+    per-source flags."""
     import hashlib
     import re
+    from context_causal_thd_amd import build as B
     code = []
     for f in KERNEL_SOURCES:
         text = open(os.path.join(root, "context_causal_thd_amd", "csrc", f)).read()
         text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
         text = re.sub(r"//[^\n]*", " ", text)
         code.append(" ".join(text.split()))
+    flags = [a for a in B.CFLAGS if not a.startswith("/")] + [f"{k}:{' '.join(v)}" for k, v in sorted(B.SOURCE_FLAGS.items())]
+    code.append(" ".join(flags))
     return hashlib.sha256("\n".join(code).encode()).hexdigest()
 
 

@@ -30,6 +30,12 @@ CFLAGS = [
 ]
 
 
+# Per-source compiler flags.  The forward kernel is scheduled by LLVM's AMDGPU "max-ilp" machine-scheduler
+# strategy, which interleaves its score products, exponentials and P V products more tightly than the default
+# (forward 2-3.5% faster on MI355X); the backward passes measured level or slower with it and keep the default.
+SOURCE_FLAGS = {"attn_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _run(cmd):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
@@ -45,7 +51,7 @@ def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
 
     def compile_one(pair):
         src, obj = pair
-        return _run([HIPCC, *CFLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj])
+        return _run([HIPCC, *CFLAGS, *SOURCE_FLAGS.get(src, []), *defines, "-c", os.path.join(CSRC, src), "-o", obj])
 
     with ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         for log in ex.map(compile_one, zip(SOURCES, objs)):
