@@ -832,6 +832,50 @@ def test_concurrent_streams_match_sequential():
             assert torch.equal(r["dk"][:T], sh.dk[:T]) and torch.equal(r["dv"][:T], sh.dv[:T]), rep
 
 
+def test_host_threads_match_sequential():
+    """Two host threads, each calling plan, forward and backward for its own share on its own stream (the library
+    calls release the interpreter lock), eight rounds: every output bit-identical to the share run alone."""
+    import threading
+    wl_a = W.small_random(83, 2, 2, max_docs=4, max_len=600, Hq=8, Hkv=2, D=128, bf16=True, qkv_scale=0.5,
+                          do_scale=1.0)
+    wl_b = W.small_random(84, 4, 0, max_docs=5, max_len=500, Hq=4, Hkv=1, D=64, bf16=True, qkv_scale=0.5,
+                          do_scale=1.0)
+    shares = [Share(wl_a, 2, 0), Share(wl_b, 0, 3)]
+    errors = []
+
+    def worker(sh):
+        try:
+            wl = sh.wl
+            S, T = wl.T // wl.cp, wl.T
+            stream = torch.cuda.Stream()
+            stream.wait_stream(torch.cuda.default_stream())
+            plan = cpthd.AttnPlan(T, wl.cp, wl.Hq, wl.Hkv, wl.D, max_docs=wl.num_docs)
+            st = status_dev()
+            o, lse = torch.empty_like(sh.o), torch.empty_like(sh.lse)
+            dq, dk, dv = torch.empty_like(sh.dq), torch.empty_like(sh.dk), torch.empty_like(sh.dv)
+            for _ in range(8):
+                with torch.cuda.stream(stream):
+                    for t in (o, lse, dq, dk, dv):
+                        t.fill_(float("nan"))
+                    plan.build(sh.cu_a, sh.cu_p, T, sh.r, sh.s, st)
+                    cpthd.attn_fwd(sh.q, sh.k, sh.v, plan, wl.softmax_scale, o, lse, st)
+                    cpthd.attn_bwd(sh.q, sh.k, sh.v, o, sh.do, lse, plan, wl.softmax_scale, dq, dk, dv, st)
+                stream.synchronize()
+                assert int(st.item()) == 0
+                assert torch.equal(o[:S], sh.o[:S]) and torch.equal(lse[:S], sh.lse[:S])
+                assert torch.equal(dq[:S], sh.dq[:S]) and torch.equal(dk[:T], sh.dk[:T]) and torch.equal(dv[:T], sh.dv[:T])
+        except Exception as e:  # noqa: BLE001 -- reported by the main thread
+            errors.append(repr(e))
+
+    threads = [threading.Thread(target=worker, args=(sh,)) for sh in shares]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads), "a worker thread did not finish"
+    assert not errors, errors
+
+
 def test_graph_replays_match_eager():
     """The plan, forward and backward launches captured in a HIP graph (torch.cuda.CUDAGraph) replay to the
     eager results bit for bit, several times, with eager work between the replays."""
